@@ -1,0 +1,415 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each test checks the oracle against something independent of its own code:
+hand-derived golden streams (tests/golden), the Gaussian-mass argmax window
+found by brute force, exact rational arithmetic, closed-form sizes with an
+independent escape count, library routines (torch's BF16 conversions), and
+invariants (bit-exact round trip of every BF16 pattern under every window).
+
+Method: ZipCCL (SIGCOMM scribe notes), "Key idea and contribution", first
+technique; data model from the same page's "Introduction" (near-Gaussian
+tensors).
+"""
+import math
+import struct
+from fractions import Fraction
+
+import mpmath as mp
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import derive_window_constant
+from lossless_bf16_exponent_zc_amd import workloads as W
+
+from conftest import read_golden
+
+C = 65536
+
+
+def u32_at(b, off):
+    return int.from_bytes(b[off:off + 4], "little")
+
+
+def hexwords(s):
+    return np.array([int(t, 16) for t in s.split()], dtype=np.uint16)
+
+
+def hexbytes(s):
+    return bytes(int(t, 16) for t in s.split())
+
+
+# --------------------------------------------------------------------------
+# Golden streams derived by hand
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["pm_one.txt", "escapes.txt"])
+def test_golden_streams(name):
+    (g,) = read_golden(name)
+    x = hexwords(g["input"])
+    c = int(g["chunk"])
+    S1, S2, n, var, L = oracle.sigma(x)
+    assert S1 == float(g["S1"]) and S2 == float(g["S2"])
+    assert n == int(g["n"]) and var == float(g["var"]) and L == int(g["L"])
+    s = oracle.compress(x, C=c)
+    h = oracle.parse_header(s)
+    assert h["magic"] == oracle.MAGIC and h["version"] == 1 and h["flags"] == 0
+    assert h["L"] == int(g["L"]) and h["N"] == x.size and h["C"] == c
+    assert h["K"] == 1 and h["E"] == int(g["E"])
+    for key in ("total", "code_off", "sm_off", "esc_off"):
+        assert h[key] == int(g[key]), key
+    assert len(s) == int(g["total"])
+    tab = [u32_at(s, 64 + 4 * i) for i in range(2)]
+    assert tab == [int(t) for t in g["table"].split()]
+    for b in range(3):
+        assert u32_at(s, h["code_off"] + 256 * b) == int(g[f"plane{b}_l0"], 16)
+    # every other code word is zero
+    codes = np.frombuffer(s[h["code_off"]:h["sm_off"]], dtype="<u4").copy()
+    codes[[0, 64, 128]] = 0
+    assert not codes.any()
+    sm = hexbytes(g["sm"])
+    assert s[h["sm_off"]:h["sm_off"] + len(sm)] == sm
+    assert not any(s[h["sm_off"] + len(sm):h["esc_off"]])
+    assert s[h["esc_off"]:] == hexbytes(g["escapes"])
+    assert not any(s[64 + 8:h["code_off"]])  # table padding
+    assert np.array_equal(oracle.decompress(s, x.size, c), x)
+
+
+def test_golden_pairwise_order():
+    cases = read_golden("pairwise_order.txt")
+    for g in cases:
+        x = hexwords(g["input"])
+        S1, S2, n, var, L = oracle.sigma(x)
+        assert S1 == float(g["S1"])
+        assert n == int(g["n"])
+        if "S2" in g:
+            assert S2 == float(g["S2"])
+            assert var == float(g["var"])
+            assert L == int(g["L"])
+        vals = oracle.bf16_to_f64(x)
+        assert oracle.pairwise_sum(vals) == float(g["S1"])
+
+
+# Hand-placed single codes: (index, lane word l, bit p, group g) from
+# r = 512 k + 8 l + j and p = 16 (j & 1) + 4 (j >> 1) + k.
+PLACEMENTS = [
+    (0, 0, 0, 0), (1, 0, 16, 0), (2, 0, 4, 0), (3, 0, 20, 0), (6, 0, 12, 0),
+    (7, 0, 28, 0), (8, 1, 0, 0), (15, 1, 28, 0), (512, 0, 1, 0),
+    (1024 + 8 * 5 + 3, 5, 22, 0), (2047, 63, 31, 0), (2048, 0, 0, 1),
+    (2048 + 1536 + 8 * 17 + 4, 17, 11, 1),
+]
+
+
+@pytest.mark.parametrize("i,l,p,g", PLACEMENTS)
+def test_code_placement(i, l, p, g):
+    # All values 1.0 (exponent 127) under a forced window L = 127 -> code 0,
+    # except one value 8.0 (exponent 130) -> code 3 = 0b011 in planes 0, 1.
+    N = 4096
+    x = np.full(N, 0x3F80, dtype=np.uint16)
+    x[i] = 0x4100
+    s = oracle.compress(x, C=C, L=127)
+    h = oracle.parse_header(s)
+    words = np.frombuffer(s[h["code_off"]:h["sm_off"]], dtype="<u4")
+    words = words.reshape(-1, 3, 64)
+    expect = np.zeros_like(words)
+    expect[g, 0, l] = expect[g, 1, l] = 1 << p
+    assert np.array_equal(words, expect)
+    assert h["E"] == 0
+
+
+# --------------------------------------------------------------------------
+# BF16 values and rounding against torch (library routines)
+# --------------------------------------------------------------------------
+def test_bf16_values_match_torch():
+    allp = np.arange(65536, dtype=np.uint16)
+    mine = oracle.bf16_to_f64(allp)
+    ref = torch.from_numpy(allp.view(np.int16)).view(torch.bfloat16).double().numpy()
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.array_equal(mine[~np.isnan(ref)], ref[~np.isnan(ref)])
+    assert np.array_equal(np.signbit(mine[fin]), np.signbit(ref[fin]))
+
+
+def _round_torch(f32):
+    t = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16)
+    return t.numpy().view(np.uint16)
+
+
+def test_round_bf16_matches_torch():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 2**32, 200000, dtype=np.uint64).astype(np.uint32)
+    # ties, near-ties, the overflow edge, subnormals, zeros, infinities
+    extra = [0x3F808000, 0x3F818000, 0x3F807FFF, 0x3F808001, 0x7F7F8000,
+             0x7F7F7FFF, 0xFF7F8000, 0x00008000, 0x00018000, 0x0000FFFF,
+             0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x007FFFFF]
+    bits = np.concatenate([bits, np.array(extra, dtype=np.uint32)])
+    f32 = bits.view(np.float32)
+    fin = ~np.isnan(f32)
+    mine = np.array([oracle.round_bf16(float(v)) for v in f32[fin]], dtype=np.uint16)
+    assert np.array_equal(mine, _round_torch(f32[fin].copy()))
+    for v in f32[~fin][:50]:
+        assert oracle.round_bf16(float(v)) == 0x7FC0
+
+
+# --------------------------------------------------------------------------
+# Pairwise sums: exactness and the error bound against exact rationals
+# --------------------------------------------------------------------------
+def test_pairwise_exact_and_bounded():
+    rng = np.random.default_rng(2)
+    for n in [0, 1, 2, 3, 5, 8, 31, 1000, 4097]:
+        ints = rng.integers(-1000, 1000, n).astype(np.float64)
+        assert oracle.pairwise_sum(ints) == float(ints.sum())  # exact
+        a = rng.standard_normal(n) * np.exp(rng.standard_normal(n) * 3)
+        exact = sum(Fraction(v) for v in a)
+        got = Fraction(oracle.pairwise_sum(a)) if n else Fraction(0)
+        depth = max(1, math.ceil(math.log2(max(n, 1))))
+        bound = Fraction(depth) * Fraction(2) ** -53 * sum(abs(Fraction(v)) for v in a)
+        assert abs(got - exact) <= bound * Fraction(101, 100)
+    # n = 0 is the empty sum +0.0
+    assert oracle.pairwise_sum(np.zeros(0)) == 0.0
+
+
+def _exact_population_var(x):
+    vals = [Fraction(v) for v in oracle.bf16_to_f64(x) if math.isfinite(v)]
+    if not vals:
+        return Fraction(0), Fraction(0)
+    n = len(vals)
+    mean = sum(vals) / n
+    return sum((v - mean) ** 2 for v in vals) / n, sum(v * v for v in vals) / n
+
+
+def test_variance_against_exact_rationals():
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        n = int(rng.integers(1, 40))
+        scale = 2.0 ** rng.integers(-100, 100)
+        z = rng.standard_normal(n) * scale + (rng.standard_normal() * scale * 0.1)
+        x = W.to_bits(torch.from_numpy(z.astype(np.float32)))
+        _, _, nf, var, _ = oracle.sigma(x)
+        exact, ms = _exact_population_var(x)
+        assert nf == n
+        # pairwise error <= depth*u*sum|v| on each moment, then three rounded
+        # operations: |error| <= (3 depth + 4) u E[x^2]
+        depth = max(1, math.ceil(math.log2(n)))
+        u = Fraction(2) ** -53
+        assert abs(Fraction(var) - exact) <= (3 * depth + 4) * u * ms
+
+
+def test_sigma_skips_nonfinite_values():
+    x = np.array([0x3F80, 0x7F80, 0xBF80, 0x7FC1, 0xFF80, 0x3F80, 0xBF80], dtype=np.uint16)
+    S1, S2, n, var, L = oracle.sigma(x)
+    assert (S1, S2, n, var, L) == (0.0, 4.0, 4, 1.0, 122)
+
+
+# --------------------------------------------------------------------------
+# Window rule against the brute-force Gaussian-mass argmax
+# --------------------------------------------------------------------------
+def _window_mass(L, sigma):
+    lo = mp.mpf(2) ** (L - 127)
+    return mp.ncdf(lo * 128 / sigma) - mp.ncdf(lo / sigma)
+
+
+def _argmax_window(var):
+    sigma = mp.sqrt(mp.mpf(var))
+    best, bestL = None, None
+    for L in range(1, 249):
+        m = _window_mass(L, sigma)
+        if best is None or m > best:
+            best, bestL = m, L
+    return bestL
+
+
+def _near_threshold(var, rel=1e-9):
+    t = mp.log(mp.mpf(var) / mp.mpf(oracle.c0()), 4)
+    return abs(t - mp.nint(t)) < rel
+
+
+def test_window_constant_rederived():
+    u, C0 = derive_window_constant.derive()
+    assert oracle.c0() == float(C0)
+
+
+def test_window_rule_is_gaussian_argmax():
+    mp.mp.dps = 40
+    rng = np.random.default_rng(4)
+    logs = rng.uniform(-260, 250, 150)
+    checked = 0
+    for lg in logs:
+        var = float(2.0 ** lg)
+        if _near_threshold(var):
+            continue
+        assert oracle.window(var) == _argmax_window(var), var
+        checked += 1
+    assert checked > 140
+
+
+def test_window_thresholds_and_clamps():
+    C0 = oracle.c0()
+    for k in [-126, -60, -5, 0, 1, 30, 121]:
+        v = math.ldexp(C0, 2 * k)
+        assert oracle.window(v) == max(1, min(248, 127 + k))
+        below = math.nextafter(v, 0.0)
+        assert oracle.window(below) == max(1, min(248, 126 + k))
+    assert oracle.window(0.0) == 1
+    assert oracle.window(1e-300) == 1
+    assert oracle.window(1e300) == 248
+    assert oracle.window(math.ldexp(C0, 2 * 125)) == 248
+
+
+def test_window_on_tiny_tensors_brute_force():
+    mp.mp.dps = 40
+    rng = np.random.default_rng(5)
+    checked = 0
+    for trial in range(60):
+        n = int(rng.integers(2, 17))
+        z = rng.standard_normal(n) * 2.0 ** rng.integers(-30, 30)
+        x = W.to_bits(torch.from_numpy(z.astype(np.float32)))
+        exact, _ = _exact_population_var(x)
+        if exact == 0 or _near_threshold(float(exact)):
+            continue
+        L = oracle.sigma(x)[4]
+        assert L == _argmax_window(float(exact))
+        checked += 1
+    assert checked > 50
+
+
+# --------------------------------------------------------------------------
+# Round trip of every BF16 pattern, every window
+# --------------------------------------------------------------------------
+def test_round_trip_every_pattern_every_window():
+    allp = np.arange(65536, dtype=np.uint16)
+    shuf = np.random.default_rng(6).permutation(allp)
+    for x in (allp, shuf):
+        for L in [None] + list(range(1, 249)):
+            s = oracle.compress(x, C=8192, L=L)
+            assert np.array_equal(oracle.decompress(s, x.size, 8192), x), L
+
+
+# --------------------------------------------------------------------------
+# Closed-form size with an independent escape count
+# --------------------------------------------------------------------------
+def _a256(v):
+    return (v + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("N", [0, 1, 7, 8, 2047, 2048, 2049, C - 1, C, C + 1, 3 * C + 12345])
+def test_size_closed_form(N):
+    x = W.small(N, seed=N) if N else np.zeros(0, dtype=np.uint16)
+    s = oracle.compress(x, C=C)
+    h = oracle.parse_header(s)
+    e = (x.astype(np.int64) >> 7) & 0xFF
+    E = int(((e < h["L"]) | (e > h["L"] + 6)).sum())
+    K, G = -(-N // C), -(-N // 2048)
+    assert h["E"] == E and h["K"] == K
+    assert len(s) == _a256(64 + 4 * (K + 1)) + 768 * G + 2048 * G + E
+    assert np.array_equal(oracle.decompress(s, N, C), x)
+    # per-chunk table from an independent count
+    esc = (e < h["L"]) | (e > h["L"] + 6)
+    tab = [u32_at(s, 64 + 4 * k) for k in range(K + 1)]
+    assert tab == [int(esc[:k * C].sum()) for k in range(K)] + [E]
+
+
+def test_ratio_bound_and_ideal_bits():
+    # 11 bits per value when nothing escapes (page: 16 -> about 11 bits)
+    x = np.full(1 << 20, 0x3F80, dtype=np.uint16)  # all 1.0, forced window
+    s = oracle.compress(x, C=C, L=127)
+    bits_per_value = 8 * (len(s) - 256) / x.size
+    assert bits_per_value == 11.0
+    assert 2 * x.size / len(s) <= 16 / 11
+
+
+# --------------------------------------------------------------------------
+# Special cases
+# --------------------------------------------------------------------------
+def test_special_cases():
+    s = oracle.compress(np.zeros(0, dtype=np.uint16))
+    h = oracle.parse_header(s)
+    assert len(s) == 256 and h["L"] == 1 and h["E"] == 0 and h["K"] == 0
+    assert oracle.decompress(s, 0).size == 0
+    z = np.zeros(5000, dtype=np.uint16)
+    s = oracle.compress(z)
+    h = oracle.parse_header(s)
+    assert h["L"] == 1 and h["E"] == 5000
+    assert np.array_equal(oracle.decompress(s, 5000), z)
+    nan = np.full(100, 0x7FC0, dtype=np.uint16)
+    S1, S2, n, var, L = oracle.sigma(nan)
+    assert n == 0 and var == 0.0 and L == 1
+    s = oracle.compress(nan)
+    assert oracle.parse_header(s)["E"] == 100
+    assert np.array_equal(oracle.decompress(s, 100), nan)
+    # constant nonzero tensor: var = 0 -> L = 1, so exponent 127 escapes
+    one = np.full(10, 0x3F80, dtype=np.uint16)
+    assert oracle.sigma(one)[3:] == (0.0, 1)
+
+
+# --------------------------------------------------------------------------
+# Decompress-reduce against numpy fp32 adds + torch rounding
+# --------------------------------------------------------------------------
+def test_decompress_reduce_matches_numpy_and_torch():
+    sh = W.shards(n=10000, nshards=5)
+    sh[2][:20] = [0x0001, 0x8001, 0x7F80, 0, 0x8000, 0x7F7F, 0x7F7F, 0x0080,
+                  0x3F80, 0xFF80, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10]
+    sh[3][3] = 0x7F80  # +Inf + -Inf at index 3 of shards 2 and 3 -> NaN
+    sh[3][9] = 0x7F80
+    streams = [oracle.compress(s, C=8192) for s in sh]
+    got = oracle.decompress_reduce(streams, 10000, C=8192)
+    acc = sh[0].astype(np.uint32) << 16
+    acc = acc.view(np.float32).copy()
+    for s in sh[1:]:
+        acc = acc + (s.astype(np.uint32) << 16).view(np.float32)
+    nan = np.isnan(acc)
+    ref = _round_torch(acc)
+    ref[nan] = 0x7FC0
+    assert nan.any()
+    assert np.array_equal(got, ref)
+
+
+# --------------------------------------------------------------------------
+# The decoder rejects damaged streams
+# --------------------------------------------------------------------------
+def _mutations(s, N):
+    h = oracle.parse_header(s)
+    out = []
+    b = bytearray(s); b[0] ^= 1; out.append(("magic", bytes(b), oracle.FMT_MAGIC))
+    b = bytearray(s); b[4] = 2; out.append(("version", bytes(b), oracle.FMT_MAGIC))
+    b = bytearray(s); b[7] = 1; out.append(("flags", bytes(b), oracle.FMT_MAGIC))
+    b = bytearray(s); b[6] = 0; out.append(("L=0", bytes(b), oracle.FMT_WINDOW))
+    b = bytearray(s); b[6] = 249; out.append(("L=249", bytes(b), oracle.FMT_WINDOW))
+    b = bytearray(s); b[8] ^= 1; out.append(("N", bytes(b), oracle.FMT_SHAPE))
+    b = bytearray(s); b[40] ^= 1; out.append(("code_off", bytes(b), oracle.FMT_SHAPE))
+    out.append(("truncated", s[:-1], oracle.FMT_SIZE))
+    b = bytearray(s); b[24] ^= 1; out.append(("E", bytes(b), oracle.FMT_SIZE))
+    b = bytearray(s); b[64 + 4] += 1; out.append(("table", bytes(b), oracle.FMT_COUNT))
+    b = bytearray(s); b[64] = 1; out.append(("table0", bytes(b), oracle.FMT_TABLE))
+    # flip one code bit of plane 0 in a chunk: changes that chunk's escapes
+    b = bytearray(s); b[h["code_off"] + 4 * 3] ^= 0x01
+    out.append(("plane bit", bytes(b), None))
+    # nonzero sm byte past N
+    b = bytearray(s); b[h["sm_off"] + N] = 1; out.append(("pad", bytes(b), oracle.FMT_PAD))
+    return out
+
+
+def test_rejection_set():
+    N = 3 * 2048 + 100
+    x = W.small(N, seed=7)
+    s = oracle.compress(x, C=2048)
+    assert oracle.decompress_status(s, N, 2048)[0] == 0
+    for name, m, bit in _mutations(s, N):
+        bad, _ = oracle.decompress_status(m, N, 2048)
+        if bit is None:
+            # a flipped code bit either changes the escape count (rejected)
+            # or turns one in-window code into another (accepted, lossy)
+            continue
+        assert bad & bit, name
+
+
+# --------------------------------------------------------------------------
+# Sanity bands on near-Gaussian data (the page's data model)
+# --------------------------------------------------------------------------
+def test_gaussian_escape_band():
+    x = W.small()
+    h = oracle.parse_header(oracle.compress(x))
+    rate = h["E"] / x.size
+    assert 0.0212 <= rate <= 0.0303 + 0.001  # Gaussian model: 2.13%..3.03%
+    assert h["L"] == 116
+    assert 1.42 < 2 * x.size / h["total"] < 16 / 11
