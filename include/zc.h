@@ -1,0 +1,166 @@
+/*
+ * zc.h -- lossless BF16 exponent coding on AMD MI355X (gfx950): C ABI.
+ *
+ * The codec (ZipCCL, SIGCOMM scribe notes, "Key idea and contribution",
+ * technique 1): a BF16 tensor's frequent-exponent window is derived from its
+ * standard deviation; each value whose 8-bit exponent falls in the 7-binade
+ * window is stored as a 3-bit code plus its raw sign+mantissa byte, and every
+ * other value (zeros, subnormals, Inf/NaN included) takes the escape code and
+ * keeps its full exponent byte in a separate compacted stream, so decoding
+ * is bit-exact at about 11 bits per value.  Technique 2 of the same section
+ * asks for GPU kernels with a communication-aware, aligned layout; the
+ * stream format (version 1) is:
+ *
+ *   [0,64) header | chunk table (K+1 u32) | code planes (768 B per 2048
+ *   values) | sign+mantissa bytes (2048 B per 2048 values) | escape bytes
+ *
+ * with every region after the table 256-byte aligned.  Field by field:
+ *   u32 magic "ZCB1" @0, u16 version=1 @4, u8 L @6, u8 flags=0 @7,
+ *   u64 N @8, u32 C @16, u32 K @20, u64 E @24, u64 total @32,
+ *   u64 code_off @40, u64 sm_off @48, u64 esc_off @56.
+ *
+ * Conventions for every call below:
+ *  - "d_" pointers are device memory owned by the caller; the library never
+ *    frees, keeps or reallocates them.  Host pointers are read during the
+ *    call only.
+ *  - BF16 data are 16-bit patterns.  A plan lays several independent
+ *    segments (each its own stream) side by side: segment s occupies BF16
+ *    elements [zc_plan_input_offset(s), +segment_elems[s]) of the
+ *    uncompressed buffer and bytes [zc_plan_stream_offset(s),
+ *    +zc_plan_max_stream_bytes(s)) of the compressed buffer.
+ *  - The compress / decompress calls only enqueue work on `stream`: they do
+ *    not allocate, synchronise or read device memory on the host.  Results
+ *    and data-dependent errors appear in device memory when the stream
+ *    reaches them.  Calls that share a workspace must not overlap.
+ *  - Argument errors are returned synchronously and enqueue nothing.
+ *  - Alignment: uncompressed buffers 16 B, compressed buffers and the
+ *    workspace 256 B.
+ */
+#ifndef ZC_H
+#define ZC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum zc_status {
+    ZC_OK = 0,
+    ZC_ERR_INVALID_ARG = 1, /* null pointer, bad size or misalignment      */
+    ZC_ERR_CAPACITY = 2,    /* a buffer is smaller than the plan needs      */
+    ZC_ERR_UNSUPPORTED = 3, /* chunk size or segment size out of range      */
+    ZC_ERR_FORMAT = 4,      /* zc_read_status found a rejected stream        */
+    ZC_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed    */
+} zc_status;
+
+/* Bits reported by zc_read_status for a rejected stream. */
+#define ZC_FMT_MAGIC  0x01u /* magic, version or flags wrong             */
+#define ZC_FMT_WINDOW 0x02u /* L outside 1..248                           */
+#define ZC_FMT_SHAPE  0x04u /* N, C, K or a region offset disagree        */
+#define ZC_FMT_SIZE   0x08u /* E > N, or total bytes past the buffer      */
+#define ZC_FMT_TABLE  0x10u /* chunk table not 0..E and non-decreasing    */
+#define ZC_FMT_COUNT  0x20u /* a chunk's escape count differs from codes  */
+#define ZC_FMT_PAD    0x40u /* nonzero code bits or sm bytes past N       */
+
+typedef struct zc_plan zc_plan; /* opaque, host-owned, immutable */
+
+/* Library version (stream format version is 1). */
+int zc_version(void);
+const char *zc_status_string(zc_status s);
+
+/*
+ * Plan for `num_segments` segments of `segment_elems[s]` BF16 values each
+ * (each < 2^32; zero allowed), chunk size `chunk_elems` (a power of two in
+ * 2048..65536; 0 selects 65536).  The chunk is the unit of the escape
+ * index (the chunk table).  Allocates a small device descriptor table on
+ * the current device.  On success *out_plan must later be passed to
+ * zc_plan_destroy.
+ */
+zc_status zc_plan_create(uint32_t num_segments, const uint64_t *segment_elems,
+                         uint32_t chunk_elems, zc_plan **out_plan);
+void zc_plan_destroy(zc_plan *plan);
+
+uint32_t zc_plan_num_segments(const zc_plan *plan);
+uint32_t zc_plan_chunk_elems(const zc_plan *plan);
+/* BF16 element offset of segment s (a multiple of 8) and total elements. */
+uint64_t zc_plan_input_offset(const zc_plan *plan, uint32_t s);
+uint64_t zc_plan_input_elems(const zc_plan *plan);
+/* Byte offset (multiple of 256) and worst-case size of segment s's stream. */
+uint64_t zc_plan_stream_offset(const zc_plan *plan, uint32_t s);
+uint64_t zc_plan_max_stream_bytes(const zc_plan *plan, uint32_t s);
+/* Bytes the compressed buffer must hold for every segment's worst case. */
+uint64_t zc_plan_out_bytes(const zc_plan *plan);
+/* Workspace bytes needed by any call with this plan. */
+uint64_t zc_plan_workspace_bytes(const zc_plan *plan);
+
+/*
+ * Compress every segment of d_in (BF16, zc_plan_input_elems elements) into
+ * d_out (out_capacity >= zc_plan_out_bytes bytes).  Segment s's stream is
+ * written at d_out + zc_plan_stream_offset(s) and its exact size in bytes to
+ * d_stream_bytes[s] (device, one u64 per segment).  Bytes between a stream's
+ * end and the next segment's offset are left untouched.
+ * The window of each segment comes from its standard deviation (fp64
+ * moments by a pairwise tree, population variance of the finite values,
+ * the 7-binade window of largest Gaussian mass).
+ */
+zc_status zc_compress(const zc_plan *plan, const void *d_in, void *d_out,
+                      uint64_t out_capacity, uint64_t *d_stream_bytes,
+                      void *d_ws, uint64_t ws_bytes, hipStream_t stream);
+
+/* As zc_compress, but every segment uses the window L (1..248) given here
+ * instead of one derived from its standard deviation (skips that pass). */
+zc_status zc_compress_window(const zc_plan *plan, const void *d_in, void *d_out,
+                             uint64_t out_capacity, uint64_t *d_stream_bytes,
+                             uint32_t window_L, void *d_ws, uint64_t ws_bytes,
+                             hipStream_t stream);
+
+/*
+ * Decode every segment's stream (at d_in + zc_plan_stream_offset(s); the
+ * buffer holds in_capacity readable bytes) into d_out (BF16, laid out as
+ * d_in of zc_compress).  Streams are validated on the device; a rejected
+ * chunk writes no output and is reported by zc_read_status.  Reads never
+ * leave [d_in, d_in + in_capacity).
+ */
+zc_status zc_decompress(const zc_plan *plan, const void *d_in,
+                        uint64_t in_capacity, void *d_out, void *d_ws,
+                        uint64_t ws_bytes, hipStream_t stream);
+
+/*
+ * Receive side of a reduce-scatter: the plan has one segment of N values;
+ * d_streams is a HOST array of `nstreams` (1..16) device pointers, each to a
+ * stream of N values with stream_capacity readable bytes.  Writes
+ * d_out[i] = bf16_rne(((x0[i] + x1[i]) + x2[i]) + ...) with the sum in fp32
+ * in the given stream order; any NaN sum gives 0x7FC0.  A rejected stream
+ * makes the affected chunks write no output (see zc_read_status).
+ */
+zc_status zc_decompress_reduce(const zc_plan *plan, const void *const *d_streams,
+                               uint32_t nstreams, uint64_t stream_capacity,
+                               void *d_out, void *d_ws, uint64_t ws_bytes,
+                               hipStream_t stream);
+
+/*
+ * Synchronises `stream`, then ORs the ZC_FMT_* bits of the most recent
+ * zc_decompress / zc_decompress_reduce that used this workspace into
+ * *host_bits.  Returns ZC_ERR_FORMAT if any bit is set.
+ */
+zc_status zc_read_status(const zc_plan *plan, const void *d_ws,
+                         hipStream_t stream, uint32_t *host_bits);
+
+/*
+ * Synchronises `stream`, then copies the window statistics of segment s from
+ * the most recent zc_compress on this workspace: S1 = sum of values,
+ * S2 = sum of squares (fp64 pairwise), n = finite values, var and L.
+ * Any output pointer may be NULL.
+ */
+zc_status zc_read_sigma(const zc_plan *plan, const void *d_ws, uint32_t s,
+                        hipStream_t stream, double *S1, double *S2,
+                        uint64_t *n, double *var, uint32_t *L);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZC_H */

@@ -1,0 +1,218 @@
+"""ctypes binding of libzc.so (the C ABI in include/zc.h).
+
+Argument marshalling only: every step of the codec runs in the HIP kernels of
+libzc.so.  torch is used for device memory and the current HIP stream.  There
+is no fallback: if the library is missing or cannot load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzc.so")
+
+ZC_OK, ZC_ERR_INVALID_ARG, ZC_ERR_CAPACITY = 0, 1, 2
+ZC_ERR_UNSUPPORTED, ZC_ERR_FORMAT, ZC_ERR_HIP = 3, 4, 5
+FMT_BITS = {0x01: "magic", 0x02: "window", 0x04: "shape", 0x08: "size",
+            0x10: "table", 0x20: "count", 0x40: "pad"}
+
+# Every symbol include/zc.h declares.
+EXPORTS = (
+    "zc_version", "zc_status_string", "zc_plan_create", "zc_plan_destroy",
+    "zc_plan_num_segments", "zc_plan_chunk_elems", "zc_plan_input_offset",
+    "zc_plan_input_elems", "zc_plan_stream_offset", "zc_plan_max_stream_bytes",
+    "zc_plan_out_bytes", "zc_plan_workspace_bytes", "zc_compress",
+    "zc_compress_window", "zc_decompress", "zc_decompress_reduce",
+    "zc_read_status", "zc_read_sigma",
+)
+
+
+class ZcError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {status_string(code)} ({code})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libzc.so, raising if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, u32, u64 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64
+    P = ctypes.POINTER
+    L.zc_version.restype = ctypes.c_int
+    L.zc_status_string.argtypes = [ctypes.c_int]
+    L.zc_status_string.restype = ctypes.c_char_p
+    L.zc_plan_create.argtypes = [u32, P(u64), u32, P(vp)]
+    L.zc_plan_destroy.argtypes = [vp]
+    L.zc_plan_destroy.restype = None
+    for name, rt in (("zc_plan_num_segments", u32), ("zc_plan_chunk_elems", u32),
+                     ("zc_plan_input_elems", u64), ("zc_plan_out_bytes", u64),
+                     ("zc_plan_workspace_bytes", u64)):
+        f = getattr(L, name)
+        f.argtypes = [vp]
+        f.restype = rt
+    for name in ("zc_plan_input_offset", "zc_plan_stream_offset",
+                 "zc_plan_max_stream_bytes"):
+        f = getattr(L, name)
+        f.argtypes = [vp, u32]
+        f.restype = u64
+    L.zc_compress.argtypes = [vp, vp, vp, u64, vp, vp, u64, vp]
+    L.zc_compress_window.argtypes = [vp, vp, vp, u64, vp, u32, vp, u64, vp]
+    L.zc_decompress.argtypes = [vp, vp, u64, vp, vp, u64, vp]
+    L.zc_decompress_reduce.argtypes = [vp, P(vp), u32, u64, vp, vp, u64, vp]
+    L.zc_read_status.argtypes = [vp, vp, vp, P(u32)]
+    L.zc_read_sigma.argtypes = [vp, vp, u32, vp, P(ctypes.c_double),
+                                P(ctypes.c_double), P(u64), P(ctypes.c_double),
+                                P(u32)]
+    for name in ("zc_plan_create", "zc_compress", "zc_compress_window",
+                 "zc_decompress", "zc_decompress_reduce", "zc_read_status",
+                 "zc_read_sigma"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(code: int) -> str:
+    return lib().zc_status_string(code).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != ZC_OK:
+        raise ZcError(rc, what)
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+class Plan:
+    """A codec plan: segment sizes and chunk size, plus its device tables."""
+
+    def __init__(self, segment_elems, chunk_elems: int = 65536):
+        sizes = [int(n) for n in segment_elems]
+        arr = (ctypes.c_uint64 * len(sizes))(*sizes)
+        h = ctypes.c_void_p()
+        _check(lib().zc_plan_create(len(sizes), arr, chunk_elems, ctypes.byref(h)),
+               "zc_plan_create")
+        self._h = h
+        self.segment_elems = sizes
+        self.chunk_elems = lib().zc_plan_chunk_elems(h)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().zc_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # geometry -----------------------------------------------------------
+    @property
+    def num_segments(self) -> int:
+        return lib().zc_plan_num_segments(self._h)
+
+    @property
+    def input_elems(self) -> int:
+        return lib().zc_plan_input_elems(self._h)
+
+    @property
+    def out_bytes(self) -> int:
+        return lib().zc_plan_out_bytes(self._h)
+
+    @property
+    def workspace_bytes(self) -> int:
+        return lib().zc_plan_workspace_bytes(self._h)
+
+    def input_offset(self, s: int) -> int:
+        return lib().zc_plan_input_offset(self._h, s)
+
+    def stream_offset(self, s: int) -> int:
+        return lib().zc_plan_stream_offset(self._h, s)
+
+    def max_stream_bytes(self, s: int) -> int:
+        return lib().zc_plan_max_stream_bytes(self._h, s)
+
+    # buffers (torch allocation only) -------------------------------------
+    def empty_input(self, device="cuda"):
+        import torch
+        return torch.zeros(max(self.input_elems, 1), dtype=torch.int16, device=device)
+
+    def empty_output(self, device="cuda"):
+        import torch
+        return torch.empty(self.out_bytes, dtype=torch.uint8, device=device)
+
+    def empty_workspace(self, device="cuda"):
+        import torch
+        return torch.empty(self.workspace_bytes, dtype=torch.uint8, device=device)
+
+    def empty_sizes(self, device="cuda"):
+        import torch
+        return torch.zeros(self.num_segments, dtype=torch.int64, device=device)
+
+    # codec calls ----------------------------------------------------------
+    def compress(self, x, out, stream_bytes, ws, window: int | None = None, stream=None):
+        """Enqueue compression of x (BF16 bits, 16-bit dtype) into out."""
+        if window is None:
+            rc = lib().zc_compress(self._h, _ptr(x), _ptr(out), _nbytes(out),
+                                   _ptr(stream_bytes), _ptr(ws), _nbytes(ws),
+                                   _stream(stream))
+            _check(rc, "zc_compress")
+        else:
+            rc = lib().zc_compress_window(self._h, _ptr(x), _ptr(out), _nbytes(out),
+                                          _ptr(stream_bytes), int(window), _ptr(ws),
+                                          _nbytes(ws), _stream(stream))
+            _check(rc, "zc_compress_window")
+
+    def decompress(self, comp, out, ws, capacity: int | None = None, stream=None):
+        """Enqueue decoding of the packed streams in comp into out."""
+        cap = _nbytes(comp) if capacity is None else int(capacity)
+        rc = lib().zc_decompress(self._h, _ptr(comp), cap, _ptr(out), _ptr(ws),
+                                 _nbytes(ws), _stream(stream))
+        _check(rc, "zc_decompress")
+
+    def decompress_reduce(self, streams, out, ws, capacity: int, stream=None):
+        """Enqueue decode + fixed-order fp32 sum of single-segment streams."""
+        arr = (ctypes.c_void_p * len(streams))(*[s.data_ptr() for s in streams])
+        rc = lib().zc_decompress_reduce(self._h, arr, len(streams), int(capacity),
+                                        _ptr(out), _ptr(ws), _nbytes(ws),
+                                        _stream(stream))
+        _check(rc, "zc_decompress_reduce")
+
+    def read_status(self, ws, stream=None) -> int:
+        """Synchronise and return the rejection bits of the last decode."""
+        bits = ctypes.c_uint32()
+        rc = lib().zc_read_status(self._h, _ptr(ws), _stream(stream), ctypes.byref(bits))
+        if rc not in (ZC_OK, ZC_ERR_FORMAT):
+            _check(rc, "zc_read_status")
+        return bits.value
+
+    def read_sigma(self, ws, s: int = 0, stream=None):
+        """Synchronise and return (S1, S2, n, var, L) of segment s."""
+        S1, S2, var = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+        n, L = ctypes.c_uint64(), ctypes.c_uint32()
+        _check(lib().zc_read_sigma(self._h, _ptr(ws), s, _stream(stream),
+                                   ctypes.byref(S1), ctypes.byref(S2), ctypes.byref(n),
+                                   ctypes.byref(var), ctypes.byref(L)), "zc_read_sigma")
+        return S1.value, S2.value, n.value, var.value, L.value

@@ -1,0 +1,305 @@
+// zc_api.hip -- the C ABI: plans, argument checks and launch sequences.
+//
+// Compress (ZipCCL scribe notes, "Key idea and contribution", technique 1):
+//   zc_sigma_partials  per-chunk fp64 moments
+//   zc_sigma_finalize  per-segment variance -> window, header, state reset
+//   zc_encode          codes, sign+mantissa bytes, escapes, chunk table, sizes
+// Decompress: zc_decode.  Decompress-reduce: zc_decode<REDUCE>.
+// Every call enqueues on the caller's stream and returns; nothing here reads
+// device memory except the two zc_read_* helpers, which synchronise.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/zc.h"
+#include "zc_kernels.h"
+
+using namespace zc;
+
+struct zc_plan {
+    uint32_t nseg = 0, chunk = 0;
+    std::vector<SegDesc> segs;
+    std::vector<ChunkDesc> chunks;
+    uint64_t input_elems = 0, out_bytes = 0;
+    WsLayout ws{};
+    SegDesc* d_segs = nullptr;
+    ChunkDesc* d_chunks = nullptr;
+};
+
+namespace {
+
+uint64_t a256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+uint64_t cdiv(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+uint32_t nchunks(const zc_plan* p) { return (uint32_t)p->chunks.size(); }
+
+zc_status launch_status() {
+    return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
+}
+
+zc_status check_ws(const zc_plan* p, const void* d_ws, uint64_t ws_bytes) {
+    if (!d_ws || !aligned(d_ws, 256)) return ZC_ERR_INVALID_ARG;
+    if (ws_bytes < p->ws.total) return ZC_ERR_CAPACITY;
+    return ZC_OK;
+}
+
+template <typename T>
+T* ws_ptr(const zc_plan* p, void* d_ws, uint64_t off) {
+    return reinterpret_cast<T*>(static_cast<uint8_t*>(d_ws) + off);
+}
+
+// sigma: NWV waves x BPW blocks of 2048 values = one chunk
+void launch_sigma(const zc_plan* p, const SigmaArgs& a, hipStream_t s) {
+    const uint32_t gpc = p->chunk / kGroup;
+    const dim3 grid(nchunks(p)), block(64 * (gpc < 16 ? gpc : 16));
+    switch (gpc) {
+        case 1: hipLaunchKernelGGL((zc_sigma_partials<1, 1>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((zc_sigma_partials<2, 1>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((zc_sigma_partials<4, 1>), grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((zc_sigma_partials<8, 1>), grid, block, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((zc_sigma_partials<16, 1>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((zc_sigma_partials<16, 2>), grid, block, 0, s, a); break;
+    }
+}
+
+// encode / decode: one wave per group up to 16 waves, then 2 groups per wave
+uint32_t codec_threads(const zc_plan* p) {
+    const uint32_t gpc = p->chunk / kGroup;
+    return 64u * (gpc < 16 ? gpc : 16u);
+}
+
+zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
+                        uint64_t* d_stream_bytes, uint32_t forced_L, void* d_ws, uint64_t ws_bytes,
+                        hipStream_t stream) {
+    if (!p) return ZC_ERR_INVALID_ARG;
+    if (p->input_elems && (!d_in || !aligned(d_in, 16))) return ZC_ERR_INVALID_ARG;
+    if (!d_out || !aligned(d_out, 256) || !d_stream_bytes || !aligned(d_stream_bytes, 8))
+        return ZC_ERR_INVALID_ARG;
+    if (out_capacity < p->out_bytes) return ZC_ERR_CAPACITY;
+    if (zc_status e = check_ws(p, d_ws, ws_bytes)) return e;
+
+    Partial* partials = ws_ptr<Partial>(p, d_ws, p->ws.partials);
+    SegStat* stats = ws_ptr<SegStat>(p, d_ws, p->ws.stats);
+    uint64_t* flags = ws_ptr<uint64_t>(p, d_ws, p->ws.flags);
+    uint32_t* ticket = ws_ptr<uint32_t>(p, d_ws, p->ws.ticket);
+    const uint16_t* in = static_cast<const uint16_t*>(d_in);
+    uint8_t* out = static_cast<uint8_t*>(d_out);
+
+    if (!forced_L && nchunks(p)) {
+        SigmaArgs sa{p->d_segs, p->d_chunks, in, partials, p->chunk};
+        launch_sigma(p, sa, stream);
+    }
+    FinalizeArgs fa{p->d_segs, partials, stats, flags, ticket, out, d_stream_bytes, p->chunk, forced_L};
+    hipLaunchKernelGGL(zc_sigma_finalize, dim3(p->nseg), dim3(256), 0, stream, fa);
+    if (nchunks(p)) {
+        EncodeArgs ea{p->d_segs, p->d_chunks, in, out, d_stream_bytes, stats, flags, ticket, p->chunk};
+        const dim3 grid(nchunks(p)), block(codec_threads(p));
+        if (p->chunk / kGroup > 16)
+            hipLaunchKernelGGL((zc_encode<2>), grid, block, 0, stream, ea);
+        else
+            hipLaunchKernelGGL((zc_encode<1>), grid, block, 0, stream, ea);
+    }
+    return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int zc_version(void) { return 1; }
+
+const char* zc_status_string(zc_status s) {
+    switch (s) {
+        case ZC_OK: return "ok";
+        case ZC_ERR_INVALID_ARG: return "invalid argument";
+        case ZC_ERR_CAPACITY: return "buffer too small";
+        case ZC_ERR_UNSUPPORTED: return "unsupported size";
+        case ZC_ERR_FORMAT: return "stream rejected";
+        case ZC_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, uint32_t chunk_elems,
+                         zc_plan** out_plan) {
+    if (!out_plan || num_segments == 0 || !segment_elems) return ZC_ERR_INVALID_ARG;
+    *out_plan = nullptr;
+    const uint32_t C = chunk_elems ? chunk_elems : 65536u;
+    if (C < kGroup || C > 65536u || (C & (C - 1))) return ZC_ERR_UNSUPPORTED;
+
+    zc_plan* p = new (std::nothrow) zc_plan;
+    if (!p) return ZC_ERR_HIP;
+    p->nseg = num_segments;
+    p->chunk = C;
+    uint64_t in_off = 0, out_off = 0;
+    for (uint32_t s = 0; s < num_segments; ++s) {
+        const uint64_t n = segment_elems[s];
+        if (n >= (1ull << 32)) {
+            delete p;
+            return ZC_ERR_UNSUPPORTED;
+        }
+        SegDesc d{};
+        d.n = n;
+        d.k = (uint32_t)cdiv(n, C);
+        d.g = (uint32_t)cdiv(n, kGroup);
+        d.code_off = a256(kHeaderBytes + 4ull * (d.k + 1));
+        d.sm_off = d.code_off + 768ull * d.g;
+        d.esc_off = d.sm_off + 2048ull * d.g;
+        d.max_bytes = d.esc_off + n;
+        d.in_off = in_off;
+        d.out_off = out_off;
+        d.chunk_base = (uint32_t)p->chunks.size();
+        in_off += (n + 7) & ~uint64_t(7);
+        out_off += a256(d.max_bytes);
+        for (uint32_t k = 0; k < d.k; ++k) p->chunks.push_back(ChunkDesc{s, k});
+        if (p->chunks.size() >= (1ull << 31)) {
+            delete p;
+            return ZC_ERR_UNSUPPORTED;
+        }
+        p->segs.push_back(d);
+    }
+    p->input_elems = in_off;
+    p->out_bytes = out_off;
+    const uint64_t K = p->chunks.size();
+    uint64_t o = 0;
+    p->ws.status = o;   o += a256(4 * K);
+    p->ws.partials = o; o += a256(sizeof(Partial) * K);
+    p->ws.flags = o;    o += a256(8 * K);
+    p->ws.stats = o;    o += a256(sizeof(SegStat) * num_segments);
+    p->ws.ticket = o;   o += 256;
+    p->ws.total = o;
+
+    if (hipMalloc(&p->d_segs, sizeof(SegDesc) * p->segs.size()) != hipSuccess ||
+        hipMalloc(&p->d_chunks, sizeof(ChunkDesc) * (K ? K : 1)) != hipSuccess ||
+        hipMemcpy(p->d_segs, p->segs.data(), sizeof(SegDesc) * p->segs.size(),
+                  hipMemcpyHostToDevice) != hipSuccess ||
+        (K && hipMemcpy(p->d_chunks, p->chunks.data(), sizeof(ChunkDesc) * K,
+                        hipMemcpyHostToDevice) != hipSuccess)) {
+        zc_plan_destroy(p);
+        return ZC_ERR_HIP;
+    }
+    *out_plan = p;
+    return ZC_OK;
+}
+
+void zc_plan_destroy(zc_plan* p) {
+    if (!p) return;
+    if (p->d_segs) (void)hipFree(p->d_segs);
+    if (p->d_chunks) (void)hipFree(p->d_chunks);
+    delete p;
+}
+
+uint32_t zc_plan_num_segments(const zc_plan* p) { return p ? p->nseg : 0; }
+uint32_t zc_plan_chunk_elems(const zc_plan* p) { return p ? p->chunk : 0; }
+uint64_t zc_plan_input_offset(const zc_plan* p, uint32_t s) {
+    return p && s < p->nseg ? p->segs[s].in_off : 0;
+}
+uint64_t zc_plan_input_elems(const zc_plan* p) { return p ? p->input_elems : 0; }
+uint64_t zc_plan_stream_offset(const zc_plan* p, uint32_t s) {
+    return p && s < p->nseg ? p->segs[s].out_off : 0;
+}
+uint64_t zc_plan_max_stream_bytes(const zc_plan* p, uint32_t s) {
+    return p && s < p->nseg ? p->segs[s].max_bytes : 0;
+}
+uint64_t zc_plan_out_bytes(const zc_plan* p) { return p ? p->out_bytes : 0; }
+uint64_t zc_plan_workspace_bytes(const zc_plan* p) { return p ? p->ws.total : 0; }
+
+zc_status zc_compress(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
+                      uint64_t* d_stream_bytes, void* d_ws, uint64_t ws_bytes, hipStream_t stream) {
+    return compress_impl(p, d_in, d_out, out_capacity, d_stream_bytes, 0, d_ws, ws_bytes, stream);
+}
+
+zc_status zc_compress_window(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
+                             uint64_t* d_stream_bytes, uint32_t window_L, void* d_ws,
+                             uint64_t ws_bytes, hipStream_t stream) {
+    if (window_L < 1 || window_L > 248) return ZC_ERR_INVALID_ARG;
+    return compress_impl(p, d_in, d_out, out_capacity, d_stream_bytes, window_L, d_ws, ws_bytes,
+                         stream);
+}
+
+zc_status zc_decompress(const zc_plan* p, const void* d_in, uint64_t in_capacity, void* d_out,
+                        void* d_ws, uint64_t ws_bytes, hipStream_t stream) {
+    if (!p || !d_in || !aligned(d_in, 256)) return ZC_ERR_INVALID_ARG;
+    if (p->input_elems && (!d_out || !aligned(d_out, 16))) return ZC_ERR_INVALID_ARG;
+    if (zc_status e = check_ws(p, d_ws, ws_bytes)) return e;
+    if (!nchunks(p)) return ZC_OK;
+    DecodeArgs a{};
+    a.segs = p->d_segs;
+    a.chunks = p->d_chunks;
+    a.in[0] = static_cast<const uint8_t*>(d_in);
+    a.capacity = in_capacity;
+    a.nstreams = 1;
+    a.chunk_elems = p->chunk;
+    a.out = static_cast<uint16_t*>(d_out);
+    a.status = ws_ptr<uint32_t>(p, d_ws, p->ws.status);
+    const dim3 grid(nchunks(p)), block(codec_threads(p));
+    if (p->chunk / kGroup > 16)
+        hipLaunchKernelGGL((zc_decode<2, false>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((zc_decode<1, false>), grid, block, 0, stream, a);
+    return launch_status();
+}
+
+zc_status zc_decompress_reduce(const zc_plan* p, const void* const* d_streams, uint32_t nstreams,
+                               uint64_t stream_capacity, void* d_out, void* d_ws, uint64_t ws_bytes,
+                               hipStream_t stream) {
+    if (!p || p->nseg != 1 || !d_streams || nstreams < 1 || nstreams > kMaxStreams)
+        return ZC_ERR_INVALID_ARG;
+    for (uint32_t s = 0; s < nstreams; ++s)
+        if (!d_streams[s] || !aligned(d_streams[s], 256)) return ZC_ERR_INVALID_ARG;
+    if (p->input_elems && (!d_out || !aligned(d_out, 16))) return ZC_ERR_INVALID_ARG;
+    if (zc_status e = check_ws(p, d_ws, ws_bytes)) return e;
+    if (!nchunks(p)) return ZC_OK;
+    DecodeArgs a{};
+    a.segs = p->d_segs;
+    a.chunks = p->d_chunks;
+    for (uint32_t s = 0; s < nstreams; ++s) a.in[s] = static_cast<const uint8_t*>(d_streams[s]);
+    a.capacity = stream_capacity;
+    a.nstreams = nstreams;
+    a.chunk_elems = p->chunk;
+    a.out = static_cast<uint16_t*>(d_out);
+    a.status = ws_ptr<uint32_t>(p, d_ws, p->ws.status);
+    const dim3 grid(nchunks(p)), block(codec_threads(p));
+    if (p->chunk / kGroup > 16)
+        hipLaunchKernelGGL((zc_decode<2, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((zc_decode<1, true>), grid, block, 0, stream, a);
+    return launch_status();
+}
+
+zc_status zc_read_status(const zc_plan* p, const void* d_ws, hipStream_t stream, uint32_t* host_bits) {
+    if (!p || !d_ws || !host_bits) return ZC_ERR_INVALID_ARG;
+    *host_bits = 0;
+    if (hipStreamSynchronize(stream) != hipSuccess) return ZC_ERR_HIP;
+    const uint32_t K = nchunks(p);
+    if (!K) return ZC_OK;
+    std::vector<uint32_t> st(K);
+    if (hipMemcpy(st.data(), static_cast<const uint8_t*>(d_ws) + p->ws.status, 4ull * K,
+                  hipMemcpyDeviceToHost) != hipSuccess)
+        return ZC_ERR_HIP;
+    uint32_t bits = 0;
+    for (uint32_t v : st) bits |= v;
+    *host_bits = bits;
+    return bits ? ZC_ERR_FORMAT : ZC_OK;
+}
+
+zc_status zc_read_sigma(const zc_plan* p, const void* d_ws, uint32_t s, hipStream_t stream,
+                        double* S1, double* S2, uint64_t* n, double* var, uint32_t* L) {
+    if (!p || !d_ws || s >= p->nseg) return ZC_ERR_INVALID_ARG;
+    if (hipStreamSynchronize(stream) != hipSuccess) return ZC_ERR_HIP;
+    SegStat st;
+    if (hipMemcpy(&st, static_cast<const uint8_t*>(d_ws) + p->ws.stats + sizeof(SegStat) * s,
+                  sizeof st, hipMemcpyDeviceToHost) != hipSuccess)
+        return ZC_ERR_HIP;
+    if (S1) *S1 = st.s1;
+    if (S2) *S2 = st.s2;
+    if (n) *n = st.n;
+    if (var) *var = st.var;
+    if (L) *L = st.L;
+    return ZC_OK;
+}
+
+}  // extern "C"

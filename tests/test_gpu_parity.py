@@ -1,0 +1,173 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Bar: compressed streams byte-identical to the oracle's, window statistics
+bit-identical, decompression and decompress-reduce bit-exact.  Inputs are the
+seeded generators of lossless_bf16_exponent_zc_amd.workloads at sizes the
+oracle finishes in seconds, spanning several chunks and a ragged tail.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from lossless_bf16_exponent_zc_amd import workloads as W
+
+from gpu_util import (gpu_compress, gpu_decompress, gpu_reduce, say,
+                      streams_to_packed)
+
+pytestmark = pytest.mark.gpu
+
+
+def check_segments(segs, chunk=65536, window=None):
+    say(f"  compress {len(segs)} segment(s), sizes {[s.size for s in segs][:6]}..., chunk {chunk}, L {window}")
+    streams, plan, out, ws = gpu_compress(segs, chunk, window)
+    for s, (seg, st) in enumerate(zip(segs, streams)):
+        ref = oracle.compress(seg, C=chunk, L=window)
+        if st != ref:
+            a = np.frombuffer(st, np.uint8)
+            b = np.frombuffer(ref, np.uint8)
+            m = min(a.size, b.size)
+            diff = np.nonzero(a[:m] != b[:m])[0]
+            raise AssertionError(
+                f"segment {s}: stream differs: len {a.size} vs {b.size}, first diffs at "
+                f"{diff[:10].tolist()} header {oracle.parse_header(st)} vs {oracle.parse_header(ref)}")
+        if window is None:
+            S1, S2, n, var, L = plan.read_sigma(ws, s)
+            o = oracle.sigma(seg)
+            assert (S1, S2, n, var, L) == o, (s, (S1, S2, n, var, L), o)
+    bits, dec = gpu_decompress(plan, out, ws)
+    assert bits == 0, hex(bits)
+    for seg, d in zip(segs, dec):
+        assert np.array_equal(seg, d)
+    return streams, plan
+
+
+def test_small_config_round_trip():
+    check_segments([W.small()])
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 511, 2047, 2048, 2049, 4095, 65535, 65536,
+                               65537, 3 * 65536 + 12345])
+def test_ragged_sizes(n):
+    check_segments([W.small(n, seed=n)])
+
+
+@pytest.mark.parametrize("chunk", [2048, 4096, 8192, 16384, 32768])
+def test_chunk_sizes(chunk):
+    check_segments([W.gradient(5 * chunk + 777, seed=3)], chunk=chunk)
+
+
+def test_every_pattern_every_window():
+    allp = np.arange(65536, dtype=np.uint16)
+    shuf = np.random.default_rng(6).permutation(allp)
+    for x in (allp, shuf):
+        check_segments([x], chunk=8192)
+        for L in list(range(1, 249, 7)) + [248]:
+            check_segments([x], chunk=8192, window=L)
+
+
+def test_special_tensors():
+    n = 70000
+    cases = {
+        "zeros": np.zeros(n, np.uint16),
+        "neg_zeros": np.full(n, 0x8000, np.uint16),
+        "nan": np.full(n, 0x7FC0, np.uint16),
+        "inf_mix": np.where(np.arange(n) % 3 == 0, 0x7F80, 0x3F80).astype(np.uint16),
+        "subnormal": (np.arange(n) % 127 + 1).astype(np.uint16),
+        "const": np.full(n, 0x4049, np.uint16),
+        "huge": np.full(n, 0x7F7F, np.uint16),
+    }
+    for name, x in cases.items():
+        say(f"  special tensor {name}")
+        check_segments([x])
+
+
+def test_moe_segments_scaled():
+    bits, sizes = W.moe(tokens=4096, hidden=512, experts=64)
+    segs, off = [], 0
+    for c in sizes:
+        segs.append(bits[off:off + c])
+        off += c
+    segs.insert(3, np.zeros(0, np.uint16))  # an empty segment in the middle
+    check_segments(segs)
+
+
+def test_llama_segments_scaled():
+    segs = W.llama_mlp(shapes=((256, 896), (896, 256), (256, 896)))
+    check_segments(segs, chunk=16384)
+
+
+def test_cross_decode_oracle_streams():
+    x = W.gradient(300000, seed=11)
+    ref = oracle.compress(x)
+    from lossless_bf16_exponent_zc_amd import Plan
+    plan = Plan([x.size])
+    bits, dec = gpu_decompress(plan, streams_to_packed(plan, [ref]))
+    assert bits == 0 and np.array_equal(dec[0], x)
+
+
+def test_determinism():
+    x = W.gradient(1 << 20, seed=5)
+    first, _ = check_segments([x])
+    for _ in range(5):
+        again, _, _, _ = gpu_compress([x])
+        assert again == first
+
+
+def test_decompress_reduce_scaled():
+    n = 200000 + 333
+    sh = W.shards(n=n, nshards=8)
+    sh[2][:10] = [0x0001, 0x8001, 0x7F80, 0, 0x8000, 0x7F7F, 0x7F7F, 0x0080, 0x3F80, 0xFF80]
+    sh[5][:10] = [0x0001, 0x0001, 0x3F80, 0, 0x8000, 0x7F7F, 0x7F7F, 0x8080, 0xFF80, 0x7F80]
+    streams = [oracle.compress(s) for s in sh]
+    ref = oracle.decompress_reduce(streams, n)
+    for S in (1, 2, 8):
+        say(f"  reduce over {S} shard(s)")
+        bits, got = gpu_reduce(streams[:S], n)
+        assert bits == 0
+        assert np.array_equal(got, oracle.decompress_reduce(streams[:S], n))
+    assert np.array_equal(gpu_reduce(streams, n)[1], ref)
+
+
+def _mutants(s, N):
+    h = oracle.parse_header(s)
+    out = []
+    def flip(off, val=None, xor=None):
+        b = bytearray(s)
+        if xor is not None:
+            b[off] ^= xor
+        else:
+            b[off] = val
+        return bytes(b)
+    out.append(flip(0, xor=1))
+    out.append(flip(4, val=2))
+    out.append(flip(7, val=1))
+    out.append(flip(6, val=0))
+    out.append(flip(6, val=249))
+    out.append(flip(8, xor=1))
+    out.append(flip(40, xor=1))
+    out.append(s[:-1])
+    out.append(flip(24, xor=1))
+    out.append(flip(64 + 4, xor=1))
+    out.append(flip(64, val=1))
+    out.append(flip(h["code_off"] + 12, xor=1))
+    out.append(flip(h["code_off"] + 256 + 12, xor=4))
+    out.append(flip(h["sm_off"] + N, val=1))
+    out.append(flip(h["sm_off"] - 1, xor=0x80))  # plane bit of a value past N
+    return out
+
+
+def test_rejection_set_matches_oracle():
+    N = 3 * 2048 + 100
+    x = W.small(N, seed=7)
+    s = oracle.compress(x, C=2048)
+    from lossless_bf16_exponent_zc_amd import Plan
+    plan = Plan([N], 2048)
+    for i, m in enumerate(_mutants(s, N)):
+        obits, _ = oracle.decompress_status(m, N, 2048)
+        packed = streams_to_packed(plan, [m])
+        gbits, dec = gpu_decompress(plan, packed, capacity=len(m))
+        say(f"  mutant {i}: oracle 0x{obits:02x} gpu 0x{gbits:02x}")
+        assert (obits == 0) == (gbits == 0), i
+        if obits == 0:
+            assert np.array_equal(dec[0], oracle.decompress(m, N, 2048))
