@@ -70,6 +70,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reduce", action="store_true")
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="also time a plain 128 MiB device-to-device copy (bandwidth "
+                         "reference and counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -143,6 +146,14 @@ def main():
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(dec_bytes / t_d / HBM_PEAK, 4), "traffic": None},
     }
+
+    if args.copy_ref:
+        src = torch.empty(64 << 20, dtype=torch.int16, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        tcp = float(np.median(timed(lambda: dst.copy_(src), args.steps, args.warmup, stream)))
+        res["copy_128MiB_ms"] = round(tcp * 1e3, 4)
+        res["copy_GBps"] = round(2 * src.numel() * 2 / tcp / 1e9, 1)  # read + write
+        del src, dst
 
     if not args.no_reduce:
         log("decompress-reduce workload")

@@ -1,9 +1,9 @@
 // zc_api.hip -- the C ABI: plans, argument checks and launch sequences.
 //
 // Compress (ZipCCL scribe notes, "Key idea and contribution", technique 1):
-//   zc_sigma_partials  per-chunk fp64 moments
-//   zc_sigma_finalize  per-segment variance -> window, header, state reset
-//   zc_encode          codes, sign+mantissa bytes, escapes, chunk table, sizes
+//   zc_sigma_partials  fp64 moments per 16,384-value block (clears look-back words)
+//   zc_sigma_finalize  per-segment variance -> window, header, work counter reset
+//   zc_encode          codes, sign+mantissa bytes, escapes, tables, sizes
 // Decompress: zc_decode.  Decompress-reduce: zc_decode<REDUCE>.
 // Every call enqueues on the caller's stream and returns; nothing here reads
 // device memory except the two zc_read_* helpers, which synchronise.
@@ -19,13 +19,15 @@
 using namespace zc;
 
 struct zc_plan {
-    uint32_t nseg = 0, chunk = 0;
+    uint32_t nseg = 0, chunk = 0, block = 0;
     std::vector<SegDesc> segs;
-    std::vector<ChunkDesc> chunks;
+    std::vector<ItemDesc> blocks, chunks, groups;
     uint64_t input_elems = 0, out_bytes = 0;
     WsLayout ws{};
     SegDesc* d_segs = nullptr;
-    ChunkDesc* d_chunks = nullptr;
+    ItemDesc* d_blocks = nullptr;
+    ItemDesc* d_chunks = nullptr;
+    ItemDesc* d_groups = nullptr;
 };
 
 namespace {
@@ -34,7 +36,10 @@ uint64_t a256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
 uint64_t cdiv(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+uint32_t nblocks(const zc_plan* p) { return (uint32_t)p->blocks.size(); }
 uint32_t nchunks(const zc_plan* p) { return (uint32_t)p->chunks.size(); }
+uint32_t ngroups(const zc_plan* p) { return (uint32_t)p->groups.size(); }
+uint32_t group_grid(const zc_plan* p) { return (ngroups(p) + 3) / 4; }
 
 zc_status launch_status() {
     return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
@@ -51,24 +56,15 @@ T* ws_ptr(const zc_plan* p, void* d_ws, uint64_t off) {
     return reinterpret_cast<T*>(static_cast<uint8_t*>(d_ws) + off);
 }
 
-// sigma: NWV waves x BPW blocks of 2048 values = one chunk
+// moment block = NWV waves x BPW blocks of 2048 values
 void launch_sigma(const zc_plan* p, const SigmaArgs& a, hipStream_t s) {
-    const uint32_t gpc = p->chunk / kGroup;
-    const dim3 grid(nchunks(p)), block(64 * (gpc < 16 ? gpc : 16));
-    switch (gpc) {
-        case 1: hipLaunchKernelGGL((zc_sigma_partials<1, 1>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((zc_sigma_partials<2, 1>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((zc_sigma_partials<4, 1>), grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((zc_sigma_partials<8, 1>), grid, block, 0, s, a); break;
-        case 16: hipLaunchKernelGGL((zc_sigma_partials<16, 1>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((zc_sigma_partials<16, 2>), grid, block, 0, s, a); break;
+    const dim3 grid(nblocks(p));
+    switch (p->block / kGroup) {
+        case 1: hipLaunchKernelGGL((zc_sigma_partials<1, 1>), grid, dim3(64), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((zc_sigma_partials<2, 1>), grid, dim3(128), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((zc_sigma_partials<4, 1>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((zc_sigma_partials<4, 2>), grid, dim3(256), 0, s, a); break;
     }
-}
-
-// encode / decode: one wave per group up to 16 waves, then 2 groups per wave
-uint32_t codec_threads(const zc_plan* p) {
-    const uint32_t gpc = p->chunk / kGroup;
-    return 64u * (gpc < 16 ? gpc : 16u);
 }
 
 zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
@@ -88,16 +84,22 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     const uint16_t* in = static_cast<const uint16_t*>(d_in);
     uint8_t* out = static_cast<uint8_t*>(d_out);
 
-    if (!forced_L && nchunks(p)) {
-        SigmaArgs sa{p->d_segs, p->d_chunks, in, partials, p->chunk};
+    if (!forced_L && nblocks(p)) {
+        SigmaArgs sa{p->d_segs, p->d_blocks, in, partials, flags, p->block, p->chunk};
         launch_sigma(p, sa, stream);
+    } else if (nchunks(p)) {
+        ResetArgs ra{flags, nchunks(p)};
+        const uint32_t grid = (nchunks(p) + 255) / 256;
+        hipLaunchKernelGGL(zc_reset_flags, dim3(grid < 1024 ? grid : 1024), dim3(256), 0, stream, ra);
     }
-    FinalizeArgs fa{p->d_segs, partials, stats, flags, ticket, out, d_stream_bytes, p->chunk, forced_L};
-    hipLaunchKernelGGL(zc_sigma_finalize, dim3(p->nseg), dim3(256), 0, stream, fa);
+    FinalizeArgs fa{p->d_segs, partials, stats, ticket, out, d_stream_bytes, p->chunk, forced_L};
+    hipLaunchKernelGGL(zc_sigma_finalize, dim3(p->nseg), dim3(1024), 0, stream, fa);
     if (nchunks(p)) {
         EncodeArgs ea{p->d_segs, p->d_chunks, in, out, d_stream_bytes, stats, flags, ticket, p->chunk};
-        const dim3 grid(nchunks(p)), block(codec_threads(p));
-        if (p->chunk / kGroup > 16)
+        // one wave per group up to 16 waves, then two groups per wave
+        const uint32_t gpc = p->chunk / kGroup;
+        const dim3 grid(nchunks(p)), block(64 * (gpc < 16 ? gpc : 16));
+        if (gpc > 16)
             hipLaunchKernelGGL((zc_encode<2>), grid, block, 0, stream, ea);
         else
             hipLaunchKernelGGL((zc_encode<1>), grid, block, 0, stream, ea);
@@ -134,6 +136,7 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
     if (!p) return ZC_ERR_HIP;
     p->nseg = num_segments;
     p->chunk = C;
+    p->block = C < kSigmaBlock ? C : kSigmaBlock;
     uint64_t in_off = 0, out_off = 0;
     for (uint32_t s = 0; s < num_segments; ++s) {
         const uint64_t n = segment_elems[s];
@@ -145,17 +148,23 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
         d.n = n;
         d.k = (uint32_t)cdiv(n, C);
         d.g = (uint32_t)cdiv(n, kGroup);
-        d.code_off = a256(kHeaderBytes + 4ull * (d.k + 1));
+        d.nsb = (uint32_t)cdiv(n, p->block);
+        d.gtab_off = kHeaderBytes + 4ull * (d.k + 1);
+        d.code_off = a256(d.gtab_off + 2ull * d.g);
         d.sm_off = d.code_off + 768ull * d.g;
         d.esc_off = d.sm_off + 2048ull * d.g;
         d.max_bytes = d.esc_off + n;
         d.in_off = in_off;
         d.out_off = out_off;
+        d.sb_base = (uint32_t)p->blocks.size();
+        d.group_base = (uint32_t)p->groups.size();
         d.chunk_base = (uint32_t)p->chunks.size();
         in_off += (n + 7) & ~uint64_t(7);
         out_off += a256(d.max_bytes);
-        for (uint32_t k = 0; k < d.k; ++k) p->chunks.push_back(ChunkDesc{s, k});
-        if (p->chunks.size() >= (1ull << 31)) {
+        for (uint32_t b = 0; b < d.nsb; ++b) p->blocks.push_back(ItemDesc{s, b});
+        for (uint32_t k = 0; k < d.k; ++k) p->chunks.push_back(ItemDesc{s, k});
+        for (uint32_t g = 0; g < d.g; ++g) p->groups.push_back(ItemDesc{s, g});
+        if (p->groups.size() >= (1ull << 31)) {
             delete p;
             return ZC_ERR_UNSUPPORTED;
         }
@@ -163,20 +172,26 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
     }
     p->input_elems = in_off;
     p->out_bytes = out_off;
-    const uint64_t K = p->chunks.size();
+    const uint64_t G = p->groups.size(), B = p->blocks.size(), K = p->chunks.size();
     uint64_t o = 0;
-    p->ws.status = o;   o += a256(4 * K);
-    p->ws.partials = o; o += a256(sizeof(Partial) * K);
+    p->ws.status = o;   o += a256(4 * G);
+    p->ws.partials = o; o += a256(sizeof(Partial) * B);
     p->ws.flags = o;    o += a256(8 * K);
     p->ws.stats = o;    o += a256(sizeof(SegStat) * num_segments);
     p->ws.ticket = o;   o += 256;
     p->ws.total = o;
 
     if (hipMalloc(&p->d_segs, sizeof(SegDesc) * p->segs.size()) != hipSuccess ||
-        hipMalloc(&p->d_chunks, sizeof(ChunkDesc) * (K ? K : 1)) != hipSuccess ||
+        hipMalloc(&p->d_blocks, sizeof(ItemDesc) * (B ? B : 1)) != hipSuccess ||
+        hipMalloc(&p->d_chunks, sizeof(ItemDesc) * (K ? K : 1)) != hipSuccess ||
+        hipMalloc(&p->d_groups, sizeof(ItemDesc) * (G ? G : 1)) != hipSuccess ||
         hipMemcpy(p->d_segs, p->segs.data(), sizeof(SegDesc) * p->segs.size(),
                   hipMemcpyHostToDevice) != hipSuccess ||
-        (K && hipMemcpy(p->d_chunks, p->chunks.data(), sizeof(ChunkDesc) * K,
+        (B && hipMemcpy(p->d_blocks, p->blocks.data(), sizeof(ItemDesc) * B,
+                        hipMemcpyHostToDevice) != hipSuccess) ||
+        (K && hipMemcpy(p->d_chunks, p->chunks.data(), sizeof(ItemDesc) * K,
+                        hipMemcpyHostToDevice) != hipSuccess) ||
+        (G && hipMemcpy(p->d_groups, p->groups.data(), sizeof(ItemDesc) * G,
                         hipMemcpyHostToDevice) != hipSuccess)) {
         zc_plan_destroy(p);
         return ZC_ERR_HIP;
@@ -188,7 +203,9 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
 void zc_plan_destroy(zc_plan* p) {
     if (!p) return;
     if (p->d_segs) (void)hipFree(p->d_segs);
+    if (p->d_blocks) (void)hipFree(p->d_blocks);
     if (p->d_chunks) (void)hipFree(p->d_chunks);
+    if (p->d_groups) (void)hipFree(p->d_groups);
     delete p;
 }
 
@@ -225,21 +242,18 @@ zc_status zc_decompress(const zc_plan* p, const void* d_in, uint64_t in_capacity
     if (!p || !d_in || !aligned(d_in, 256)) return ZC_ERR_INVALID_ARG;
     if (p->input_elems && (!d_out || !aligned(d_out, 16))) return ZC_ERR_INVALID_ARG;
     if (zc_status e = check_ws(p, d_ws, ws_bytes)) return e;
-    if (!nchunks(p)) return ZC_OK;
+    if (!ngroups(p)) return ZC_OK;
     DecodeArgs a{};
     a.segs = p->d_segs;
-    a.chunks = p->d_chunks;
+    a.groups = p->d_groups;
     a.in[0] = static_cast<const uint8_t*>(d_in);
     a.capacity = in_capacity;
     a.nstreams = 1;
     a.chunk_elems = p->chunk;
+    a.ngroups = ngroups(p);
     a.out = static_cast<uint16_t*>(d_out);
     a.status = ws_ptr<uint32_t>(p, d_ws, p->ws.status);
-    const dim3 grid(nchunks(p)), block(codec_threads(p));
-    if (p->chunk / kGroup > 16)
-        hipLaunchKernelGGL((zc_decode<2, false>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((zc_decode<1, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((zc_decode<false>), dim3(group_grid(p)), dim3(256), 0, stream, a);
     return launch_status();
 }
 
@@ -252,21 +266,18 @@ zc_status zc_decompress_reduce(const zc_plan* p, const void* const* d_streams, u
         if (!d_streams[s] || !aligned(d_streams[s], 256)) return ZC_ERR_INVALID_ARG;
     if (p->input_elems && (!d_out || !aligned(d_out, 16))) return ZC_ERR_INVALID_ARG;
     if (zc_status e = check_ws(p, d_ws, ws_bytes)) return e;
-    if (!nchunks(p)) return ZC_OK;
+    if (!ngroups(p)) return ZC_OK;
     DecodeArgs a{};
     a.segs = p->d_segs;
-    a.chunks = p->d_chunks;
+    a.groups = p->d_groups;
     for (uint32_t s = 0; s < nstreams; ++s) a.in[s] = static_cast<const uint8_t*>(d_streams[s]);
     a.capacity = stream_capacity;
     a.nstreams = nstreams;
     a.chunk_elems = p->chunk;
+    a.ngroups = ngroups(p);
     a.out = static_cast<uint16_t*>(d_out);
     a.status = ws_ptr<uint32_t>(p, d_ws, p->ws.status);
-    const dim3 grid(nchunks(p)), block(codec_threads(p));
-    if (p->chunk / kGroup > 16)
-        hipLaunchKernelGGL((zc_decode<2, true>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((zc_decode<1, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((zc_decode<true>), dim3(group_grid(p)), dim3(256), 0, stream, a);
     return launch_status();
 }
 
@@ -274,7 +285,7 @@ zc_status zc_read_status(const zc_plan* p, const void* d_ws, hipStream_t stream,
     if (!p || !d_ws || !host_bits) return ZC_ERR_INVALID_ARG;
     *host_bits = 0;
     if (hipStreamSynchronize(stream) != hipSuccess) return ZC_ERR_HIP;
-    const uint32_t K = nchunks(p);
+    const uint32_t K = ngroups(p);
     if (!K) return ZC_OK;
     std::vector<uint32_t> st(K);
     if (hipMemcpy(st.data(), static_cast<const uint8_t*>(d_ws) + p->ws.status, 4ull * K,

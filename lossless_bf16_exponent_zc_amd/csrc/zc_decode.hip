@@ -5,15 +5,16 @@
 // escape byte for code 7, sign and mantissa from the raw byte.  The fused
 // variant is the receive side of a compressed reduce-scatter (technique 3
 // names the reduce-scatter path; the UCCL-Zip page's abstract argues for
-// fusing the codec into the collective to drop extra memory traffic): every
-// shard is decoded tile by tile into registers and added in shard order in
-// fp32, so the only global write is the final BF16 sum.
+// fusing the codec into the collective to drop extra memory traffic): each
+// shard's group is decoded into registers and added in shard order in fp32,
+// so the only global write is the final BF16 sum.
 //
-// One workgroup per chunk; each wave owns GPW consecutive groups.  Planes are
-// read first so every lane knows where its escapes start (wave scan + LDS
-// scan over the chunk, plus the chunk table); the group is then rebuilt with
-// packed ops, staged in LDS, and each lane patches its escaped values.
-// Every stream is validated first; a chunk that fails writes nothing.
+// One wave per 2048-value group.  The chunk table and the group table give
+// the group's first escape directly, so groups decode independently: planes
+// and sign+mantissa bytes are loaded, the group's escape bytes are copied to
+// LDS, values are rebuilt with packed ops and staged in LDS, and each lane
+// patches its escaped values.  Every stream's header, tables, counts and
+// padding are checked; a group that fails writes nothing.
 #include "zc_kernels.h"
 
 namespace zc {
@@ -79,24 +80,41 @@ __device__ __forceinline__ uint64_t sm_pad_mask(uint32_t lane, uint32_t valid, i
     return ~0ull << (8 * left);
 }
 
+__device__ __forceinline__ void store_values(uint16_t* __restrict__ out, uint64_t n, uint64_t g,
+                                             uint32_t lane, const u32x4 (&o)[4]) {
+    const uint64_t base = (uint64_t)kGroup * g + 8u * lane;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint64_t b = base + 512u * k;
+        if (b + 8 <= n) {
+            *reinterpret_cast<u32x4*>(out + b) = o[k];
+        } else {
+            for (uint32_t j = 0; j < 8; ++j)
+                if (b + j < n) out[b + j] = (uint16_t)(o[k][j >> 1] >> (16 * (j & 1)));
+        }
+    }
+}
+
 }  // namespace
 
-template <int GPW, bool REDUCE>
-__global__ __launch_bounds__(1024) void zc_decode(DecodeArgs a) {
-    __shared__ uint32_t s_gbase[32];
-    __shared__ uint32_t s_total;
-    __shared__ u32x4 s_stage[16][256];
+template <bool REDUCE>
+__global__ __launch_bounds__(256) void zc_decode(DecodeArgs a) {
+    __shared__ u32x4 s_stage[4][256];   // decoded group per wave
+    __shared__ uint8_t s_esc[4][2048];  // the group's escape bytes per wave
 
-    const uint32_t chunk = blockIdx.x;
-    const ChunkDesc cd = a.chunks[chunk];
-    const SegDesc sd = a.segs[cd.seg];
-    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-    const uint64_t g0 = (uint64_t)cd.local * (a.chunk_elems / kGroup) + (uint64_t)wave * GPW;
-    const uint64_t tail_valid = sd.n - (uint64_t)kGroup * (sd.g ? sd.g - 1 : 0);
-    uint16_t* __restrict__ out = a.out + sd.in_off;
+    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+    const uint32_t gg = blockIdx.x * 4 + wave;
+    if (gg >= a.ngroups) return;
+    const ItemDesc gd = a.groups[gg];
+    const SegDesc sd = a.segs[gd.seg];
+    const uint32_t g = gd.local;
+    const uint32_t gpc = a.chunk_elems / kGroup;
+    const uint32_t k = g / gpc;
+    const bool tail = (uint64_t)kGroup * (g + 1) > sd.n;
+    const uint32_t valid = (uint32_t)(sd.n - (uint64_t)kGroup * g);  // meaningful when tail
     uint16_t* stage = reinterpret_cast<uint16_t*>(s_stage[wave]);
 
-    float acc[REDUCE ? GPW : 1][REDUCE ? 32 : 1];
+    float acc[REDUCE ? 32 : 1];
     uint32_t bad_all = 0;
 
     for (uint32_t s = 0; s < a.nstreams; ++s) {
@@ -111,153 +129,108 @@ __global__ __launch_bounds__(1024) void zc_decode(DecodeArgs a) {
             if (cap > sd.max_bytes) cap = sd.max_bytes;
         }
         uint32_t bad = check_header(st, cap, sd, a.chunk_elems);
-        uint32_t t0 = 0, t1 = 0, L = 0;
+        uint32_t t0 = 0, rel = 0, span = 0, L = 0;
         if (!bad) {
             const uint32_t* table = reinterpret_cast<const uint32_t*>(st + kHeaderBytes);
+            const uint16_t* gtab = reinterpret_cast<const uint16_t*>(st + sd.gtab_off);
             const uint64_t E = ld<uint64_t>(st + 24);
             L = st[6];
-            t0 = table[cd.local];
-            t1 = table[cd.local + 1];
-            if (t0 > t1 || t1 > E || (cd.local == 0 && t0 != 0) ||
-                (cd.local + 1 == sd.k && t1 != E))
+            t0 = table[k];
+            const uint32_t t1 = table[k + 1];
+            rel = gtab[g];
+            const bool last_in_chunk = (g + 1) % gpc == 0 || g + 1 == sd.g;
+            const uint32_t next = last_in_chunk ? t1 - t0 : gtab[g + 1];
+            if (t0 > t1 || t1 > E || (k == 0 && t0 != 0) || (k + 1 == sd.k && t1 != E) ||
+                (g % gpc == 0 && rel != 0))
                 bad |= kBadTable;
+            else if (rel > next || next > t1 - t0)
+                bad |= kBadCount;
+            span = next - rel;
         }
         if (bad) {
             bad_all |= bad;
             continue;
         }
 
-        // planes, escape masks, per-lane escape offsets inside the chunk
-        uint32_t P[GPW][3], M[GPW], base[GPW];
-        uint32_t padbad = 0;
+        uint32_t P[3];
+        const uint8_t* cw = st + sd.code_off + 768ull * g + 4u * lane;
 #pragma unroll
-        for (int q = 0; q < GPW; ++q) {
-            const uint64_t g = g0 + q;
-            if (g < sd.g) {
-                const uint8_t* cw = st + sd.code_off + 768ull * g + 4u * lane;
+        for (int b = 0; b < 3; ++b) P[b] = ld<uint32_t>(cw + 256 * b);
+        u32x2 sm[4];
+        const uint8_t* sw = st + sd.sm_off + 2048ull * g + 8u * lane;
 #pragma unroll
-                for (int b = 0; b < 3; ++b) P[q][b] = ld<uint32_t>(cw + 256 * b);
-                if (g + 1 == sd.g && tail_valid < kGroup) {
-                    const uint32_t V = valid_bits(lane, (uint32_t)tail_valid);
-                    if ((P[q][0] | P[q][1] | P[q][2]) & ~V) padbad = 1;
-                    const uint8_t* sw = st + sd.sm_off + 2048ull * g + 8u * lane;
+        for (int kk = 0; kk < 4; ++kk) sm[kk] = ld<u32x2>(sw + 512 * kk);
+        bool padbad = false;
+        if (tail) {
+            const uint32_t V = valid_bits(lane, valid);
+            padbad = ((P[0] | P[1] | P[2]) & ~V) != 0;
 #pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        if (ld<uint64_t>(sw + 512 * k) & sm_pad_mask(lane, (uint32_t)tail_valid, k))
-                            padbad = 1;
-                }
-            } else {
-                P[q][0] = P[q][1] = P[q][2] = 0;
-            }
-            M[q] = P[q][0] & P[q][1] & P[q][2];
-            const uint32_t cnt = __builtin_popcount(M[q]);
-            const uint32_t incl = wave_inclusive_scan(cnt);
-            base[q] = incl - cnt;
-            if (lane == 63) s_gbase[wave * GPW + q] = incl;
+            for (int kk = 0; kk < 4; ++kk)
+                padbad |= (__builtin_bit_cast(uint64_t, sm[kk]) & sm_pad_mask(lane, valid, kk)) != 0;
         }
-        const uint32_t anypad = __syncthreads_or(padbad) ? kBadPad : 0u;
-        if (threadIdx.x < 64) {
-            const uint32_t ng = nwaves * GPW;
-            const uint32_t v = threadIdx.x < ng ? s_gbase[threadIdx.x] : 0u;
-            const uint32_t incl = wave_inclusive_scan(v);
-            if (threadIdx.x < ng) s_gbase[threadIdx.x] = incl - v;
-            if (threadIdx.x == 63) s_total = incl;
-        }
-        __syncthreads();
-        bad = anypad | (s_total != t1 - t0 ? kBadCount : 0u);
+        const uint32_t M = P[0] & P[1] & P[2];
+        const uint32_t cnt = __builtin_popcount(M);
+        const uint32_t incl = wave_inclusive_scan(cnt);
+        const uint32_t total = __shfl(incl, 63, 64);
+        if (__ballot(padbad)) bad |= kBadPad;
+        if (total != span) bad |= kBadCount;
         if (bad) {
             bad_all |= bad;
-            __syncthreads();  // s_gbase / s_total are rewritten by the next stream
             continue;
         }
 
+        // the group's escape bytes -> LDS
+        const uint8_t* esc = st + sd.esc_off + t0 + rel;
+        for (uint32_t i = lane; i < total; i += 64) s_esc[wave][i] = esc[i];
         const uint32_t L7 = (L << 7) | (L << 23);
+        u32x4 o[4];
+        decode_group(P, sm, L7, o);
 #pragma unroll
-        for (int q = 0; q < GPW; ++q) {
-            const uint64_t g = g0 + q;
-            if (g >= sd.g) continue;
-            u32x2 sm[4];
-            const uint8_t* sw = st + sd.sm_off + 2048ull * g + 8u * lane;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) sm[k] = ld<u32x2>(sw + 512 * k);
-            u32x4 o[4];
-            decode_group(P[q], sm, L7, o);
-            // stage, patch escaped exponents, read back
-#pragma unroll
-            for (int k = 0; k < 4; ++k) s_stage[wave][64 * k + lane] = o[k];
-            __builtin_amdgcn_wave_barrier();
-            const uint8_t* esc = st + sd.esc_off + t0 + s_gbase[wave * GPW + q] + base[q];
-            uint32_t m = M[q], i = 0;
-            while (m) {
-                const uint32_t p = __builtin_ctz(m);
-                m &= m - 1;
-                const uint32_t r = group_index(lane, p);
-                const uint32_t e = esc[i++];
-                stage[r] = (uint16_t)((stage[r] & 0x807Fu) | (e << 7));
-            }
-            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int k = 0; k < 4; ++k) o[k] = s_stage[wave][64 * k + lane];
-            __builtin_amdgcn_wave_barrier();
-
-            if (REDUCE) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-#pragma unroll
-                    for (int mm = 0; mm < 4; ++mm) {
-                        const float lo = __uint_as_float(o[k][mm] << 16);
-                        const float hi = __uint_as_float(o[k][mm] & 0xFFFF0000u);
-                        float& a0 = acc[REDUCE ? q : 0][REDUCE ? 8 * k + 2 * mm : 0];
-                        float& a1 = acc[REDUCE ? q : 0][REDUCE ? 8 * k + 2 * mm + 1 : 0];
-                        a0 = s == 0 ? lo : a0 + lo;
-                        a1 = s == 0 ? hi : a1 + hi;
-                    }
-            } else {
-                const uint64_t base_i = (uint64_t)kGroup * g + 8u * lane;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint64_t b = base_i + 512u * k;
-                    if (b + 8 <= sd.n) {
-                        *reinterpret_cast<u32x4*>(out + b) = o[k];
-                    } else {
-                        for (uint32_t j = 0; j < 8; ++j)
-                            if (b + j < sd.n) out[b + j] = (uint16_t)(o[k][j >> 1] >> (16 * (j & 1)));
-                    }
-                }
-            }
+        for (int kk = 0; kk < 4; ++kk) s_stage[wave][64 * kk + lane] = o[kk];
+        __builtin_amdgcn_wave_barrier();
+        uint32_t m = M, i = incl - cnt;
+        while (m) {
+            const uint32_t p = __builtin_ctz(m);
+            m &= m - 1;
+            const uint32_t r = group_index(lane, p);
+            stage[r] = (uint16_t)((stage[r] & 0x807Fu) | ((uint32_t)s_esc[wave][i++] << 7));
         }
-        __syncthreads();  // s_gbase / s_total are rewritten by the next stream
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) o[kk] = s_stage[wave][64 * kk + lane];
+        __builtin_amdgcn_wave_barrier();
+
+        if (REDUCE) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    const float lo = __uint_as_float(o[kk][mm] << 16);
+                    const float hi = __uint_as_float(o[kk][mm] & 0xFFFF0000u);
+                    float& a0 = acc[REDUCE ? 8 * kk + 2 * mm : 0];
+                    float& a1 = acc[REDUCE ? 8 * kk + 2 * mm + 1 : 0];
+                    a0 = s == 0 ? lo : a0 + lo;
+                    a1 = s == 0 ? hi : a1 + hi;
+                }
+        } else {
+            store_values(a.out + sd.in_off, sd.n, g, lane, o);
+        }
     }
 
     if (REDUCE && bad_all == 0 && a.nstreams > 0) {
+        u32x4 o[4];
 #pragma unroll
-        for (int q = 0; q < GPW; ++q) {
-            const uint64_t g = g0 + q;
-            if (g >= sd.g) continue;
-            const uint64_t base_i = (uint64_t)kGroup * g + 8u * lane;
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                u32x4 o;
-#pragma unroll
-                for (int mm = 0; mm < 4; ++mm)
-                    o[mm] = to_bf16(acc[REDUCE ? q : 0][REDUCE ? 8 * k + 2 * mm : 0]) |
-                            (to_bf16(acc[REDUCE ? q : 0][REDUCE ? 8 * k + 2 * mm + 1 : 0]) << 16);
-                const uint64_t b = base_i + 512u * k;
-                if (b + 8 <= sd.n) {
-                    *reinterpret_cast<u32x4*>(out + b) = o;
-                } else {
-                    for (uint32_t j = 0; j < 8; ++j)
-                        if (b + j < sd.n) out[b + j] = (uint16_t)(o[j >> 1] >> (16 * (j & 1)));
-                }
-            }
-        }
+            for (int mm = 0; mm < 4; ++mm)
+                o[kk][mm] = to_bf16(acc[REDUCE ? 8 * kk + 2 * mm : 0]) |
+                            (to_bf16(acc[REDUCE ? 8 * kk + 2 * mm + 1 : 0]) << 16);
+        store_values(a.out + sd.in_off, sd.n, g, lane, o);
     }
-    if (threadIdx.x == 0) a.status[chunk] = bad_all;
+    if (lane == 0) a.status[gg] = bad_all;
 }
 
-template __global__ void zc_decode<1, false>(DecodeArgs);
-template __global__ void zc_decode<2, false>(DecodeArgs);
-template __global__ void zc_decode<1, true>(DecodeArgs);
-template __global__ void zc_decode<2, true>(DecodeArgs);
+template __global__ void zc_decode<false>(DecodeArgs);
+template __global__ void zc_decode<true>(DecodeArgs);
 
 }  // namespace zc

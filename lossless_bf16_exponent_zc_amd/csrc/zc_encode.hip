@@ -5,16 +5,18 @@
 // stay raw, other exponents are kept whole in a separate stream) and
 // technique 2 (GPU kernel with a communication-aware, aligned layout).
 //
-// One workgroup per chunk.  Each wave owns GPW consecutive 2048-value groups
-// of the chunk and reads them with one 16-byte load per lane per tile.
-//  1. codes: packed 16-bit ops give (e - L) clamped to 7 for two values at a
-//     time; nibble-packing and a 4-way bit interleave turn a lane's 32 codes
-//     into its three plane words without any per-value branch;
-//  2. the sign+mantissa bytes come from two byte permutes and a bit select;
-//  3. escape masks (code 7 = all three plane bits set) are counted per lane,
-//     scanned across the wave (shuffles) and across the chunk (LDS);
-//  4. the chunk's offset in the segment's escape stream is found by a
-//     decoupled look-back over earlier chunks (an atomic work counter orders
+// One workgroup per chunk; each wave owns GPW consecutive 2048-value groups.
+//  1. one 16-byte load per lane per tile; packed 16-bit ops give (e - L)
+//     clamped to 7 for two values at a time; nibble packing and a 4-way bit
+//     interleave turn the lane's 32 codes into its three plane words;
+//  2. sign+mantissa bytes from two byte permutes and a bit select; planes and
+//     sign+mantissa bytes go out at once (their offsets are static);
+//  3. the lane keeps only its 32 exponent bytes, in plane-bit order, and its
+//     escape mask (code 7 = all three plane bits set);
+//  4. escape counts are scanned across the wave (shuffles) and across the
+//     chunk (LDS), which gives the group table; the chunk's offset in the
+//     segment's escape stream comes from a decoupled look-back in which one
+//     wave reads 64 earlier chunks per round (an atomic work counter orders
 //     the workgroups, so every chunk waited on is already running);
 //  5. each lane writes its escape exponents, contiguous in code order.
 #include "zc_kernels.h"
@@ -45,32 +47,68 @@ __device__ __forceinline__ void encode_group(const u32x4 (&w)[4], uint32_t L7, u
                (((Z[2] >> b) & 0x11111111u) << 2) | (((Z[3] >> b) & 0x11111111u) << 3);
 }
 
-// Decoupled look-back: publish this chunk's escape count, add up earlier
-// chunks of the segment until one with a published inclusive prefix, then
-// publish our own inclusive prefix.  Returns the exclusive prefix.
-__device__ uint32_t look_back(uint64_t* flags, uint32_t chunk, uint32_t local, uint32_t total) {
+// Exponent bytes of the lane's 32 values in plane-bit order: byte p of the
+// 32-byte array belongs to bit p (p = 4n + k: tile k, nibble n).
+__device__ __forceinline__ void exponent_bytes(const u32x4 (&w)[4], uint32_t (&Q)[8]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        // after << 1 the exponent of the low value is byte 1, of the high one byte 3
+        const uint32_t A = w[0][m] << 1, B = w[1][m] << 1, C = w[2][m] << 1, D = w[3][m] << 1;
+        const uint32_t X = perm(B, A, 0x07030501u);  // A.b1 B.b1 A.b3 B.b3
+        const uint32_t Y = perm(D, C, 0x07030501u);  // C.b1 D.b1 C.b3 D.b3
+        Q[m] = perm(Y, X, 0x05040100u);              // low values of tiles 0..3
+        Q[m + 4] = perm(Y, X, 0x07060302u);          // high values of tiles 0..3
+    }
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) v += __shfl_xor(v, d, 64);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t load_flag(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_flag(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Run by one whole wave.  Publishes the chunk's count, then finds the
+// exclusive escape prefix of chunk `ci` (local index `local` in its segment):
+// lane i of a round looks at the chunk base + i + 1 places back; a round is
+// usable once every chunk before the nearest published prefix has at least
+// published its count.
+__device__ uint32_t look_back(uint64_t* flags, uint32_t ci, uint32_t local, uint32_t total) {
+    const uint32_t lane = lane_id();
     if (local == 0) {
-        __hip_atomic_store(&flags[chunk], kFlagPrefix | total, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) store_flag(flags + ci, kFlagPrefix | total);
         return 0;
     }
-    __hip_atomic_store(&flags[chunk], kFlagAggregate | total, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    uint64_t prefix = 0;
-    uint32_t j = chunk - 1;
-    for (;;) {
-        uint64_t f = __hip_atomic_load(&flags[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        while ((f >> 62) == 0) {
+    if (lane == 0) store_flag(flags + ci, kFlagAggregate | total);
+    uint32_t acc = 0;
+    for (uint32_t base = 0;; base += 64) {
+        const uint32_t d = base + lane + 1;
+        const bool valid = d <= local;
+        uint64_t f;
+        uint32_t fp;
+        for (;;) {
+            f = valid ? load_flag(flags + ci - d) : 0;
+            const uint32_t st = (uint32_t)(f >> 62);
+            const uint64_t valid_m = __ballot(valid);
+            const uint64_t pre_m = __ballot(valid && st == 2);
+            const uint64_t rdy_m = __ballot(valid && st != 0);
+            fp = pre_m ? (uint32_t)__builtin_ctzll(pre_m) : 64u;
+            const uint64_t need = fp == 64 ? valid_m : ((1ull << fp) - 1);
+            if ((rdy_m & need) == need && (fp < 64 || valid_m == ~0ull)) break;
             __builtin_amdgcn_s_sleep(1);
-            f = __hip_atomic_load(&flags[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        prefix += f & kFlagValueMask;
-        if ((f >> 62) == 2) break;
-        --j;
+        acc += wave_sum(valid && lane <= fp ? (uint32_t)f : 0u);
+        if (fp < 64) break;
     }
-    __hip_atomic_store(&flags[chunk], kFlagPrefix | (prefix + total), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    return (uint32_t)prefix;
+    if (lane == 0) store_flag(flags + ci, kFlagPrefix | (acc + total));
+    return acc;
 }
 
 }  // namespace
@@ -79,22 +117,23 @@ template <int GPW>
 __global__ __launch_bounds__(1024) void zc_encode(EncodeArgs a) {
     __shared__ uint32_t s_ticket, s_prefix;
     __shared__ uint32_t s_gbase[32];
-    __shared__ u32x4 s_stage[16][256];  // one 2048-value group per wave
+    __shared__ __attribute__((aligned(16))) uint32_t s_q[16][64 * 10];  // per wave: 32 exponent
+    // bytes per lane at a 40-byte stride (10 dwords: reads by byte index spread over banks)
 
     const uint32_t lane = lane_id(), wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
     if (threadIdx.x == 0) s_ticket = atomicAdd(a.ticket, 1u);
     __syncthreads();
-    const uint32_t chunk = s_ticket;
-    const ChunkDesc cd = a.chunks[chunk];
+    const uint32_t ci = s_ticket;
+    const ItemDesc cd = a.chunks[ci];
     const SegDesc sd = a.segs[cd.seg];
     const uint32_t L = a.stats[cd.seg].L;
     const uint32_t L7 = (L << 7) | (L << 23);
     const uint16_t* __restrict__ x = a.in + sd.in_off;
     uint8_t* __restrict__ st = a.out + sd.out_off;
-    const uint64_t g0 = (uint64_t)cd.local * (a.chunk_elems / kGroup) + (uint64_t)wave * GPW;
+    const uint32_t gpc = a.chunk_elems / kGroup;
+    const uint64_t g0 = (uint64_t)cd.local * gpc + (uint64_t)wave * GPW;
 
     u32x4 w[GPW][4];
-    uint32_t M[GPW], base[GPW];
 #pragma unroll
     for (int q = 0; q < GPW; ++q) {
         if (g0 + q < sd.g) {
@@ -104,6 +143,7 @@ __global__ __launch_bounds__(1024) void zc_encode(EncodeArgs a) {
             for (int k = 0; k < 4; ++k) w[q][k] = u32x4{0, 0, 0, 0};
         }
     }
+    uint32_t Q[GPW][8], M[GPW], excl[GPW];
 #pragma unroll
     for (int q = 0; q < GPW; ++q) {
         const uint64_t g = g0 + q;
@@ -125,25 +165,31 @@ __global__ __launch_bounds__(1024) void zc_encode(EncodeArgs a) {
             for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x2*>(sw + 512 * k) = sm[k];
             M[q] = P[0] & P[1] & P[2];
         }
+        exponent_bytes(w[q], Q[q]);
         const uint32_t cnt = __builtin_popcount(M[q]);
         const uint32_t incl = wave_inclusive_scan(cnt);
-        base[q] = incl - cnt;
+        excl[q] = incl - cnt;
         if (lane == 63) s_gbase[wave * GPW + q] = incl;
     }
     __syncthreads();
 
-    if (threadIdx.x < 64) {
+    if (wave == 0) {
         const uint32_t ng = nwaves * GPW;
-        const uint32_t v = threadIdx.x < ng ? s_gbase[threadIdx.x] : 0u;
+        const uint32_t v = lane < ng ? s_gbase[lane] : 0u;
         const uint32_t incl = wave_inclusive_scan(v);
         const uint32_t total = __shfl(incl, 63, 64);
-        if (threadIdx.x < ng) s_gbase[threadIdx.x] = incl - v;
-        if (threadIdx.x == 0) {
-            const uint32_t prefix = look_back(a.flags, chunk, cd.local, total);
+        const uint64_t g = (uint64_t)cd.local * gpc + lane;
+        if (lane < ng) {
+            s_gbase[lane] = incl - v;
+            if (g < sd.g) reinterpret_cast<uint16_t*>(st + sd.gtab_off)[g] = (uint16_t)(incl - v);
+        }
+        const uint32_t prefix = look_back(a.flags, ci, cd.local, total);
+        if (lane == 0) {
             s_prefix = prefix;
-            reinterpret_cast<uint32_t*>(st + kHeaderBytes)[cd.local + 1] = prefix + total;
+            reinterpret_cast<uint32_t*>(st + kHeaderBytes)[cd.local] = prefix;
             if (cd.local + 1 == sd.k) {
                 const uint64_t E = (uint64_t)prefix + total;
+                reinterpret_cast<uint32_t*>(st + kHeaderBytes)[sd.k] = (uint32_t)E;
                 *reinterpret_cast<uint64_t*>(st + 24) = E;
                 *reinterpret_cast<uint64_t*>(st + 32) = sd.esc_off + E;
                 a.stream_bytes[cd.seg] = sd.esc_off + E;
@@ -152,19 +198,22 @@ __global__ __launch_bounds__(1024) void zc_encode(EncodeArgs a) {
     }
     __syncthreads();
 
+    // escape exponents: each lane's are contiguous, in plane-bit order
     const uint32_t prefix = s_prefix;
-    const uint16_t* stage = reinterpret_cast<const uint16_t*>(s_stage[wave]);
+    uint32_t* qs = s_q[wave] + 10 * lane;
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(qs);
 #pragma unroll
     for (int q = 0; q < GPW; ++q) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) s_stage[wave][64 * k + lane] = w[q][k];
+        for (int t = 0; t < 4; ++t)
+            *reinterpret_cast<u32x2*>(qs + 2 * t) = u32x2{Q[q][2 * t], Q[q][2 * t + 1]};
         __builtin_amdgcn_wave_barrier();
-        uint8_t* esc = st + sd.esc_off + prefix + s_gbase[wave * GPW + q] + base[q];
+        uint8_t* esc = st + sd.esc_off + prefix + s_gbase[wave * GPW + q] + excl[q];
         uint32_t m = M[q], i = 0;
         while (m) {
             const uint32_t p = __builtin_ctz(m);
             m &= m - 1;
-            esc[i++] = (uint8_t)(stage[group_index(lane, p)] >> 7);
+            esc[i++] = qb[p];
         }
         __builtin_amdgcn_wave_barrier();
     }

@@ -1,9 +1,11 @@
 // zc_internal.h -- shared definitions of the gfx950 codec kernels.
 //
 // Stream format version 1 (ZipCCL scribe notes, "Key idea and contribution",
-// techniques 1 and 2): per 2048-value group, three planes of 64 u32 words
-// (bit b of each 3-bit code in plane b), then one sign+mantissa byte per
-// value, then the escape exponents in code order.
+// techniques 1 and 2): header, chunk table (u32 escape offset of each chunk),
+// group table (u16 escape offset of each 2048-value group inside its chunk),
+// then per group three planes of 64 u32 words (bit b of each 3-bit code in
+// plane b), then one sign+mantissa byte per value, then the escape exponents
+// in code order.  The two-level index lets any group be decoded on its own.
 //
 // Lane view used by every kernel: a group is 4 tiles of 512 values; lane l of
 // a wave owns values 512k + 8l + j (k = 0..3 tile, j = 0..7 slot), read with
@@ -24,25 +26,29 @@ constexpr uint32_t kHeaderBytes = 64;
 constexpr uint32_t kMagic = 0x3142435Au;  // "ZCB1"
 constexpr uint32_t kVersion = 1;
 constexpr uint32_t kMaxStreams = 16;
+constexpr uint32_t kSigmaBlock = 16384;  // values per moment partial (or the chunk, if smaller)
 
 // Per-segment geometry, built on the host at plan time.
 struct SegDesc {
     uint64_t n;          // values
     uint64_t in_off;     // element offset in the BF16 buffers
     uint64_t out_off;    // byte offset of the stream in the compressed buffer
-    uint64_t code_off;   // region offsets relative to the stream start
+    uint64_t gtab_off;   // region offsets relative to the stream start
+    uint64_t code_off;
     uint64_t sm_off;
     uint64_t esc_off;
     uint64_t max_bytes;  // worst-case stream size
     uint32_t k;          // chunks
     uint32_t g;          // groups
-    uint32_t chunk_base; // first chunk of this segment in the plan's chunk list
-    uint32_t pad;
+    uint32_t nsb;        // moment blocks
+    uint32_t sb_base;    // first moment block of this segment in the plan's list
+    uint32_t group_base; // first group of this segment in the plan's list
+    uint32_t chunk_base; // first chunk of this segment in the plan's list
 };
 
-struct ChunkDesc {
+struct ItemDesc {  // a moment block, chunk or group: its segment and index inside it
     uint32_t seg;
-    uint32_t local;  // chunk index inside the segment
+    uint32_t local;
 };
 
 struct Partial {  // per-chunk moments
@@ -60,18 +66,19 @@ struct SegStat {  // per-segment window statistics
 
 // Workspace carve-up (all offsets 256-aligned), computed on the host.
 struct WsLayout {
-    uint64_t status;    // u32 per chunk: rejection bits of the last decode
-    uint64_t partials;  // Partial per chunk
+    uint64_t status;    // u32 per group: rejection bits of the last decode
+    uint64_t partials;  // Partial per moment block
     uint64_t flags;     // u64 per chunk: look-back state of the encoder
     uint64_t stats;     // SegStat per segment
     uint64_t ticket;    // u32: encoder work counter
     uint64_t total;
 };
 
-// Look-back flag word: state in the top two bits, value below.
+// Look-back flag word of a chunk: state in bits 62-63, count in bits 0-31.
+//   aggregate: the chunk's escape count
+//   prefix:    escapes of the segment up to and including the chunk
 constexpr uint64_t kFlagAggregate = 1ull << 62;
 constexpr uint64_t kFlagPrefix = 2ull << 62;
-constexpr uint64_t kFlagValueMask = (1ull << 62) - 1;
 
 // ---------------------------------------------------------------- helpers
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));

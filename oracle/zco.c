@@ -189,7 +189,9 @@ static unsigned code_of(unsigned e, unsigned L)
 /*   [0, 64)        header                                              */
 /*   [64, ...)      chunk table: K+1 u32, entry k = escapes before      */
 /*                  chunk k (entry K = E)                               */
-/*   code_off       = A256(64 + 4(K+1)); 768 bytes per group of 2048   */
+/*   then           group table: G u16, entry g = escapes before group  */
+/*                  g counted from the start of g's chunk               */
+/*   code_off       = A256(64 + 4(K+1) + 2G); 768 bytes per group       */
 /*   sm_off         = code_off + 768 G; 2048 bytes per group            */
 /*   esc_off        = sm_off + 2048 G; E escape bytes                   */
 /*   total          = esc_off + E                                       */
@@ -207,10 +209,13 @@ static unsigned code_of(unsigned e, unsigned L)
 static uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 static uint64_t align256(uint64_t x) { return (x + 255u) & ~(uint64_t)255u; }
 
+static uint64_t group_table_off(uint64_t N, uint32_t C)
+{
+    return ZCO_HEADER_BYTES + 4u * (ceil_div(N, C) + 1u);
+}
 uint64_t zco_code_off(uint64_t N, uint32_t C)
 {
-    uint64_t K = ceil_div(N, C);
-    return align256(ZCO_HEADER_BYTES + 4u * (K + 1u));
+    return align256(group_table_off(N, C) + 2u * ceil_div(N, ZCO_GROUP));
 }
 uint64_t zco_sm_off(uint64_t N, uint32_t C)
 {
@@ -323,11 +328,15 @@ int zco_compress(const uint16_t *x, uint64_t N, uint32_t C, int forced_L,
         out[sm_off + i] = (uint8_t)((bf16_sign(x[i]) << 7) | bf16_mantissa(x[i]));
     }
 
-    /* 5. escape bytes in code order, chunk table */
-    uint64_t groups_per_chunk = C / ZCO_GROUP, pos = 0;
+    /* 5. escape bytes in code order, chunk table, group table */
+    uint64_t groups_per_chunk = C / ZCO_GROUP, pos = 0, chunk_start = 0;
+    uint8_t *gtab = out + group_table_off(N, C);
     for (uint64_t g = 0; g < G; ++g) {
-        if (g % groups_per_chunk == 0)
+        if (g % groups_per_chunk == 0) {
             put_u32(out + ZCO_HEADER_BYTES + 4u * (g / groups_per_chunk), (uint32_t)pos);
+            chunk_start = pos;
+        }
+        put_u16(gtab + 2u * g, (uint16_t)(pos - chunk_start));
         for (unsigned l = 0; l < 64; ++l)
             for (unsigned p = 0; p < 32; ++p) {
                 uint64_t i = index_of(g, l, p);
@@ -390,13 +399,19 @@ uint32_t zco_decompress(const uint8_t *s, uint64_t len, uint64_t N, uint32_t C,
         if (code_at(s, code_off, i) != 0 || s[sm_off + i] != 0)
             bad |= ZCO_FMT_PAD;
 
-    /* every chunk's escape count must match its codes */
+    /* every chunk's escape count must match its codes, and the group
+     * table must hold each group's escape offset inside its chunk */
     uint64_t groups_per_chunk = C / ZCO_GROUP;
+    const uint8_t *gtab = s + group_table_off(N, C);
     for (uint64_t k = 0; k < K; ++k) {
         uint64_t cnt = 0;
-        for (uint64_t i = k * C; i < N && i < (k + 1) * C; ++i)
-            if (code_at(s, code_off, i) == ZCO_ESC)
-                ++cnt;
+        for (uint64_t g = k * groups_per_chunk; g < G && g < (k + 1) * groups_per_chunk; ++g) {
+            if (get_u16(gtab + 2u * g) != cnt)
+                bad |= (g == k * groups_per_chunk) ? ZCO_FMT_TABLE : ZCO_FMT_COUNT;
+            for (uint64_t i = g * ZCO_GROUP; i < N && i < (g + 1) * ZCO_GROUP; ++i)
+                if (code_at(s, code_off, i) == ZCO_ESC)
+                    ++cnt;
+        }
         if (cnt != (uint64_t)get_u32(tab + 4u * (k + 1)) - get_u32(tab + 4u * k))
             bad |= ZCO_FMT_COUNT;
     }

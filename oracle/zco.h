@@ -39,8 +39,10 @@ extern "C" {
 #define ZCO_FMT_WINDOW   0x02u  /* L outside [1, 248]                       */
 #define ZCO_FMT_SHAPE    0x04u  /* N, C, K or a region offset disagree      */
 #define ZCO_FMT_SIZE     0x08u  /* total bytes exceed the buffer            */
-#define ZCO_FMT_TABLE    0x10u  /* chunk table not 0..E and monotone        */
-#define ZCO_FMT_COUNT    0x20u  /* a chunk's escapes differ from its codes  */
+#define ZCO_FMT_TABLE    0x10u  /* chunk table not 0..E and monotone, or a
+                                   chunk's first group-table entry not 0   */
+#define ZCO_FMT_COUNT    0x20u  /* a chunk's or group's escape offsets
+                                   differ from its codes                    */
 #define ZCO_FMT_PAD      0x40u  /* nonzero code bits or sm bytes past N     */
 
 /* The window constant C0: var >= C0 * 4^k  <=>  window k or higher. */

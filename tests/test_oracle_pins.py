@@ -301,20 +301,26 @@ def test_size_closed_form(N):
     E = int(((e < h["L"]) | (e > h["L"] + 6)).sum())
     K, G = -(-N // C), -(-N // 2048)
     assert h["E"] == E and h["K"] == K
-    assert len(s) == _a256(64 + 4 * (K + 1)) + 768 * G + 2048 * G + E
+    assert len(s) == _a256(64 + 4 * (K + 1) + 2 * G) + 768 * G + 2048 * G + E
     assert np.array_equal(oracle.decompress(s, N, C), x)
-    # per-chunk table from an independent count
+    # per-chunk and per-group tables from an independent count
     esc = (e < h["L"]) | (e > h["L"] + 6)
     tab = [u32_at(s, 64 + 4 * k) for k in range(K + 1)]
     assert tab == [int(esc[:k * C].sum()) for k in range(K)] + [E]
+    goff = 64 + 4 * (K + 1)
+    gtab = [int.from_bytes(s[goff + 2 * g:goff + 2 * g + 2], "little") for g in range(G)]
+    assert gtab == [int(esc[(g * 2048 // C) * C:g * 2048].sum()) for g in range(G)]
 
 
 def test_ratio_bound_and_ideal_bits():
     # 11 bits per value when nothing escapes (page: 16 -> about 11 bits)
     x = np.full(1 << 20, 0x3F80, dtype=np.uint16)  # all 1.0, forced window
     s = oracle.compress(x, C=C, L=127)
-    bits_per_value = 8 * (len(s) - 256) / x.size
+    h = oracle.parse_header(s)
+    bits_per_value = 8 * (len(s) - h["code_off"]) / x.size
     assert bits_per_value == 11.0
+    # the index (chunk + group tables) costs 16 bits per 2048 values and up
+    assert h["code_off"] - 64 <= 4 * (h["K"] + 1) + 2 * (x.size // 2048) + 255
     assert 2 * x.size / len(s) <= 16 / 11
 
 
@@ -381,12 +387,28 @@ def _mutations(s, N):
     b = bytearray(s); b[24] ^= 1; out.append(("E", bytes(b), oracle.FMT_SIZE))
     b = bytearray(s); b[64 + 4] += 1; out.append(("table", bytes(b), oracle.FMT_COUNT))
     b = bytearray(s); b[64] = 1; out.append(("table0", bytes(b), oracle.FMT_TABLE))
+    goff = 64 + 4 * (h["K"] + 1)
+    b = bytearray(s); b[goff + 2] += 1
+    out.append(("group table", bytes(b), oracle.FMT_TABLE | oracle.FMT_COUNT))
     # flip one code bit of plane 0 in a chunk: changes that chunk's escapes
     b = bytearray(s); b[h["code_off"] + 4 * 3] ^= 0x01
     out.append(("plane bit", bytes(b), None))
     # nonzero sm byte past N
     b = bytearray(s); b[h["sm_off"] + N] = 1; out.append(("pad", bytes(b), oracle.FMT_PAD))
     return out
+
+
+def test_group_table_rejections():
+    N = 5 * 2048 + 7
+    x = W.small(N, seed=8)
+    s = oracle.compress(x, C=8192)
+    goff = 64 + 4 * (2 + 1)
+    for g, bit in [(0, oracle.FMT_TABLE), (1, oracle.FMT_COUNT), (3, oracle.FMT_COUNT),
+                   (4, oracle.FMT_TABLE)]:
+        b = bytearray(s)
+        b[goff + 2 * g] ^= 1
+        bad, _ = oracle.decompress_status(bytes(b), N, 8192)
+        assert bad == bit, (g, bad)
 
 
 def test_rejection_set():
