@@ -10,11 +10,13 @@
 // so the only global write is the final BF16 sum.
 //
 // One wave per 2048-value group.  The chunk table and the group table give
-// the group's first escape directly, so groups decode independently: planes
-// and sign+mantissa bytes are loaded, the group's escape bytes are copied to
-// LDS, values are rebuilt with packed ops and staged in LDS, and each lane
-// patches its escaped values.  Every stream's header, tables, counts and
-// padding are checked; a group that fails writes nothing.
+// the group's first escape directly, so groups decode independently.  The
+// plane words and sign+mantissa bytes are requested before the header is
+// checked (their offsets follow from the plan alone), the escape bytes as
+// soon as the tables arrive, so a group costs two memory round trips.
+// Values are rebuilt with packed ops, staged in LDS, and each lane patches
+// its escaped values.  Every stream's header, tables, counts and padding are
+// checked; a group that fails writes nothing.
 #include "zc_kernels.h"
 
 namespace zc {
@@ -83,6 +85,11 @@ __device__ __forceinline__ uint64_t sm_pad_mask(uint32_t lane, uint32_t valid, i
 __device__ __forceinline__ void store_values(uint16_t* __restrict__ out, uint64_t n, uint64_t g,
                                              uint32_t lane, const u32x4 (&o)[4]) {
     const uint64_t base = (uint64_t)kGroup * g + 8u * lane;
+    if ((uint64_t)kGroup * (g + 1) <= n) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(out + base + 512u * k) = o[k];
+        return;
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const uint64_t b = base + 512u * k;
@@ -95,136 +102,189 @@ __device__ __forceinline__ void store_values(uint16_t* __restrict__ out, uint64_
     }
 }
 
+// Everything one wave reads of one stream for one group.
+struct GroupData {
+    uint32_t P[3];
+    u32x2 sm[4];
+    uint32_t bad, L, t0, rel, span;
+};
+
+// Issue the loads of group g of stream st (cap readable bytes).  Plane words
+// and sm bytes are only read when the buffer holds the fixed regions.
+__device__ __forceinline__ void fetch(const uint8_t* st, uint64_t cap, const SegDesc& sd,
+                                      uint32_t C, uint32_t g, uint32_t lane, GroupData& d) {
+    const bool fixed_ok = cap >= sd.esc_off;
+    const uint8_t* cw = st + sd.code_off + 768ull * g + 4u * lane;
+    const uint8_t* sw = st + sd.sm_off + 2048ull * g + 8u * lane;
+#pragma unroll
+    for (int b = 0; b < 3; ++b) d.P[b] = fixed_ok ? ld<uint32_t>(cw + 256 * b) : 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) d.sm[k] = fixed_ok ? ld<u32x2>(sw + 512 * k) : u32x2{0, 0};
+
+    d.bad = check_header(st, cap, sd, C);
+    d.L = d.t0 = d.rel = d.span = 0;
+    if (!d.bad) {
+        const uint32_t gpc = C / kGroup, k = g / gpc;
+        const uint32_t* table = reinterpret_cast<const uint32_t*>(st + kHeaderBytes);
+        const uint16_t* gtab = reinterpret_cast<const uint16_t*>(st + sd.gtab_off);
+        const uint64_t E = ld<uint64_t>(st + 24);
+        d.L = st[6];
+        d.t0 = table[k];
+        const uint32_t t1 = table[k + 1];
+        d.rel = gtab[g];
+        const bool last_in_chunk = (g + 1) % gpc == 0 || g + 1 == sd.g;
+        const uint32_t next = last_in_chunk ? t1 - d.t0 : gtab[g + 1];
+        if (d.t0 > t1 || t1 > E || (k == 0 && d.t0 != 0) || (k + 1 == sd.k && t1 != E) ||
+            (g % gpc == 0 && d.rel != 0))
+            d.bad |= kBadTable;
+        else if (d.rel > next || next > t1 - d.t0)
+            d.bad |= kBadCount;
+        else
+            d.span = next - d.rel;
+    }
+}
+
+// Copy the group's `span` escape bytes (starting at stream byte `at`) into
+// LDS as whole dwords; returns the offset of the first byte in `dst`.
+__device__ __forceinline__ uint32_t fetch_escapes(const uint8_t* st, uint64_t cap, uint64_t at,
+                                                  uint32_t span, uint32_t lane, uint32_t* dst) {
+    const uint64_t a0 = at & ~3ull;
+    const uint32_t ndw = (uint32_t)((at + span + 3 - a0) >> 2);
+    for (uint32_t i = lane; i < ndw; i += 64) {
+        const uint64_t o = a0 + 4ull * i;
+        uint32_t v;
+        if (o + 4 <= cap) {
+            v = ld<uint32_t>(st + o);
+        } else {
+            v = 0;
+            for (uint32_t b = 0; b < 4; ++b)
+                if (o + b < cap) v |= (uint32_t)st[o + b] << (8 * b);
+        }
+        dst[i] = v;
+    }
+    return (uint32_t)(at - a0);
+}
+
+// Rebuild the group's values into o, with escaped exponents patched.
+__device__ __forceinline__ void rebuild(const GroupData& d, uint32_t M, uint32_t first,
+                                        const uint8_t* esc, u32x4* stage4, uint32_t lane,
+                                        u32x4 (&o)[4]) {
+    decode_group(d.P, d.sm, (d.L << 7) | (d.L << 23), o);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) stage4[64 * k + lane] = o[k];
+    __builtin_amdgcn_wave_barrier();
+    uint16_t* stage = reinterpret_cast<uint16_t*>(stage4);
+    uint32_t m = M, i = first;
+    while (m) {
+        const uint32_t p = __builtin_ctz(m);
+        m &= m - 1;
+        const uint32_t r = group_index(lane, p);
+        stage[r] = (uint16_t)((stage[r] & 0x807Fu) | ((uint32_t)esc[i++] << 7));
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = stage4[64 * k + lane];
+    __builtin_amdgcn_wave_barrier();
+}
+
 }  // namespace
 
 template <bool REDUCE>
 __global__ __launch_bounds__(256) void zc_decode(DecodeArgs a) {
     __shared__ u32x4 s_stage[4][256];   // decoded group per wave
-    __shared__ uint8_t s_esc[4][2048];  // the group's escape bytes per wave
+    __shared__ uint32_t s_esc[4][520];  // the group's escape bytes per wave (whole dwords)
 
-    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+    const uint32_t lane = lane_id(), wave = wave_id();
     const uint32_t gg = blockIdx.x * 4 + wave;
     if (gg >= a.ngroups) return;
     const ItemDesc gd = a.groups[gg];
     const SegDesc sd = a.segs[gd.seg];
     const uint32_t g = gd.local;
-    const uint32_t gpc = a.chunk_elems / kGroup;
-    const uint32_t k = g / gpc;
     const bool tail = (uint64_t)kGroup * (g + 1) > sd.n;
     const uint32_t valid = (uint32_t)(sd.n - (uint64_t)kGroup * g);  // meaningful when tail
-    uint16_t* stage = reinterpret_cast<uint16_t*>(s_stage[wave]);
+    const uint8_t* escb = reinterpret_cast<const uint8_t*>(s_esc[wave]);
 
     float acc[REDUCE ? 32 : 1];
     uint32_t bad_all = 0;
 
-    for (uint32_t s = 0; s < a.nstreams; ++s) {
-        const uint8_t* st;
-        uint64_t cap;
+    auto stream_of = [&](uint32_t s, uint64_t& cap) -> const uint8_t* {
         if (REDUCE) {
-            st = a.in[s];
             cap = a.capacity;
-        } else {
-            st = a.in[0] + sd.out_off;
-            cap = a.capacity > sd.out_off ? a.capacity - sd.out_off : 0;
-            if (cap > sd.max_bytes) cap = sd.max_bytes;
+            return a.in[s];
         }
-        uint32_t bad = check_header(st, cap, sd, a.chunk_elems);
-        uint32_t t0 = 0, rel = 0, span = 0, L = 0;
+        cap = a.capacity > sd.out_off ? a.capacity - sd.out_off : 0;
+        if (cap > sd.max_bytes) cap = sd.max_bytes;
+        return a.in[0] + sd.out_off;
+    };
+
+    uint64_t cap;
+    const uint8_t* st = stream_of(0, cap);
+    GroupData cur;
+    fetch(st, cap, sd, a.chunk_elems, g, lane, cur);
+    for (uint32_t s = 0; s < a.nstreams; ++s) {
+        // escape bytes of this stream, then the next stream's loads
+        uint32_t first = 0;
+        if (!cur.bad)
+            first = fetch_escapes(st, cap, sd.esc_off + cur.t0 + cur.rel, cur.span, lane, s_esc[wave]);
+        GroupData nxt;
+        uint64_t ncap = 0;
+        const uint8_t* nst = nullptr;
+        if (REDUCE && s + 1 < a.nstreams) {
+            nst = stream_of(s + 1, ncap);
+            fetch(nst, ncap, sd, a.chunk_elems, g, lane, nxt);
+        }
+
+        uint32_t bad = cur.bad;
         if (!bad) {
-            const uint32_t* table = reinterpret_cast<const uint32_t*>(st + kHeaderBytes);
-            const uint16_t* gtab = reinterpret_cast<const uint16_t*>(st + sd.gtab_off);
-            const uint64_t E = ld<uint64_t>(st + 24);
-            L = st[6];
-            t0 = table[k];
-            const uint32_t t1 = table[k + 1];
-            rel = gtab[g];
-            const bool last_in_chunk = (g + 1) % gpc == 0 || g + 1 == sd.g;
-            const uint32_t next = last_in_chunk ? t1 - t0 : gtab[g + 1];
-            if (t0 > t1 || t1 > E || (k == 0 && t0 != 0) || (k + 1 == sd.k && t1 != E) ||
-                (g % gpc == 0 && rel != 0))
-                bad |= kBadTable;
-            else if (rel > next || next > t1 - t0)
-                bad |= kBadCount;
-            span = next - rel;
-        }
-        if (bad) {
-            bad_all |= bad;
-            continue;
-        }
-
-        uint32_t P[3];
-        const uint8_t* cw = st + sd.code_off + 768ull * g + 4u * lane;
+            bool padbad = false;
+            if (tail) {
+                const uint32_t V = valid_bits(lane, valid);
+                padbad = ((cur.P[0] | cur.P[1] | cur.P[2]) & ~V) != 0;
 #pragma unroll
-        for (int b = 0; b < 3; ++b) P[b] = ld<uint32_t>(cw + 256 * b);
-        u32x2 sm[4];
-        const uint8_t* sw = st + sd.sm_off + 2048ull * g + 8u * lane;
+                for (int k = 0; k < 4; ++k)
+                    padbad |= (__builtin_bit_cast(uint64_t, cur.sm[k]) & sm_pad_mask(lane, valid, k)) != 0;
+            }
+            const uint32_t M = cur.P[0] & cur.P[1] & cur.P[2];
+            const uint32_t cnt = __builtin_popcount(M);
+            const uint32_t incl = wave_inclusive_scan(cnt);
+            if (__ballot(padbad)) bad |= kBadPad;
+            if (__shfl(incl, 63, 64) != cur.span) bad |= kBadCount;
+            if (!bad) {
+                u32x4 o[4];
+                rebuild(cur, M, first + incl - cnt, escb, s_stage[wave], lane, o);
+                if (REDUCE) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) sm[kk] = ld<u32x2>(sw + 512 * kk);
-        bool padbad = false;
-        if (tail) {
-            const uint32_t V = valid_bits(lane, valid);
-            padbad = ((P[0] | P[1] | P[2]) & ~V) != 0;
+                    for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                padbad |= (__builtin_bit_cast(uint64_t, sm[kk]) & sm_pad_mask(lane, valid, kk)) != 0;
-        }
-        const uint32_t M = P[0] & P[1] & P[2];
-        const uint32_t cnt = __builtin_popcount(M);
-        const uint32_t incl = wave_inclusive_scan(cnt);
-        const uint32_t total = __shfl(incl, 63, 64);
-        if (__ballot(padbad)) bad |= kBadPad;
-        if (total != span) bad |= kBadCount;
-        if (bad) {
-            bad_all |= bad;
-            continue;
-        }
-
-        // the group's escape bytes -> LDS
-        const uint8_t* esc = st + sd.esc_off + t0 + rel;
-        for (uint32_t i = lane; i < total; i += 64) s_esc[wave][i] = esc[i];
-        const uint32_t L7 = (L << 7) | (L << 23);
-        u32x4 o[4];
-        decode_group(P, sm, L7, o);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) s_stage[wave][64 * kk + lane] = o[kk];
-        __builtin_amdgcn_wave_barrier();
-        uint32_t m = M, i = incl - cnt;
-        while (m) {
-            const uint32_t p = __builtin_ctz(m);
-            m &= m - 1;
-            const uint32_t r = group_index(lane, p);
-            stage[r] = (uint16_t)((stage[r] & 0x807Fu) | ((uint32_t)s_esc[wave][i++] << 7));
-        }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) o[kk] = s_stage[wave][64 * kk + lane];
-        __builtin_amdgcn_wave_barrier();
-
-        if (REDUCE) {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int mm = 0; mm < 4; ++mm) {
-                    const float lo = __uint_as_float(o[kk][mm] << 16);
-                    const float hi = __uint_as_float(o[kk][mm] & 0xFFFF0000u);
-                    float& a0 = acc[REDUCE ? 8 * kk + 2 * mm : 0];
-                    float& a1 = acc[REDUCE ? 8 * kk + 2 * mm + 1 : 0];
-                    a0 = s == 0 ? lo : a0 + lo;
-                    a1 = s == 0 ? hi : a1 + hi;
+                        for (int mm = 0; mm < 4; ++mm) {
+                            const float lo = __uint_as_float(o[k][mm] << 16);
+                            const float hi = __uint_as_float(o[k][mm] & 0xFFFF0000u);
+                            float& a0 = acc[REDUCE ? 8 * k + 2 * mm : 0];
+                            float& a1 = acc[REDUCE ? 8 * k + 2 * mm + 1 : 0];
+                            a0 = s == 0 ? lo : a0 + lo;
+                            a1 = s == 0 ? hi : a1 + hi;
+                        }
+                } else {
+                    store_values(a.out + sd.in_off, sd.n, g, lane, o);
                 }
-        } else {
-            store_values(a.out + sd.in_off, sd.n, g, lane, o);
+            }
+        }
+        bad_all |= bad;
+        if (REDUCE && s + 1 < a.nstreams) {
+            cur = nxt;
+            st = nst;
+            cap = ncap;
         }
     }
 
     if (REDUCE && bad_all == 0 && a.nstreams > 0) {
         u32x4 o[4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int k = 0; k < 4; ++k)
 #pragma unroll
             for (int mm = 0; mm < 4; ++mm)
-                o[kk][mm] = to_bf16(acc[REDUCE ? 8 * kk + 2 * mm : 0]) |
-                            (to_bf16(acc[REDUCE ? 8 * kk + 2 * mm + 1 : 0]) << 16);
+                o[k][mm] = to_bf16(acc[REDUCE ? 8 * k + 2 * mm : 0]) |
+                           (to_bf16(acc[REDUCE ? 8 * k + 2 * mm + 1 : 0]) << 16);
         store_values(a.out + sd.in_off, sd.n, g, lane, o);
     }
     if (lane == 0) a.status[gg] = bad_all;

@@ -120,10 +120,10 @@ __global__ __launch_bounds__(1024) void zc_encode(EncodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t s_q[16][64 * 10];  // per wave: 32 exponent
     // bytes per lane at a 40-byte stride (10 dwords: reads by byte index spread over banks)
 
-    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    const uint32_t lane = lane_id(), wave = wave_id(), nwaves = blockDim.x >> 6;
     if (threadIdx.x == 0) s_ticket = atomicAdd(a.ticket, 1u);
     __syncthreads();
-    const uint32_t ci = s_ticket;
+    const uint32_t ci = uniform(s_ticket);
     const ItemDesc cd = a.chunks[ci];
     const SegDesc sd = a.segs[cd.seg];
     const uint32_t L = a.stats[cd.seg].L;

@@ -106,6 +106,14 @@ __device__ __forceinline__ uint32_t bitsel(uint32_t mask, uint32_t a, uint32_t b
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
+// Index of the calling wave in its workgroup, as a wave-uniform value (so
+// that values derived from it live in scalar registers).
+__device__ __forceinline__ uint32_t wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
     const uint32_t lane = lane_id();

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void zc_sigma_partials(SigmaArgs a) {
     const ItemDesc bd = a.blocks[blk];
     const SegDesc sd = a.segs[bd.seg];
     const uint16_t* __restrict__ x = a.in + sd.in_off;
-    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+    const uint32_t lane = lane_id(), wave = wave_id();
     __shared__ double s_s1[NWV], s_s2[NWV];
     __shared__ uint32_t s_n[NWV];
 
@@ -204,7 +204,7 @@ constexpr int kMaxLevels = 10;  // up to 8 * 512 leaves per thread
 // window, writes the header fields known before encoding and resets the
 // encoder's work counter.  With forced_L != 0 the moments are skipped.
 __global__ __launch_bounds__(1024) void zc_sigma_finalize(FinalizeArgs a) {
-    const uint32_t seg = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const uint32_t seg = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const SegDesc sd = a.segs[seg];
     __shared__ double s_v1[16], s_v2[16];
     __shared__ unsigned long long s_n[16];
