@@ -18,11 +18,12 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libzc.so")
 SOURCES = ["zc_api.hip", "zc_sigma.hip", "zc_encode.hip", "zc_decode.hip"]
 
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-std=c++17", "-O3", "-fPIC", "--offload-arch=gfx950",
          "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wall", "-Wno-unused-result"]
+         "-Wall", "-Wno-unused-result", "-I" + INCLUDE]
 
 
 def _compile(src: str, extra) -> str:

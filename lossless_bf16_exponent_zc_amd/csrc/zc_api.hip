@@ -1,9 +1,9 @@
 // zc_api.hip -- the C ABI: plans, argument checks and launch sequences.
 //
 // Compress (ZipCCL scribe notes, "Key idea and contribution", technique 1):
-//   zc_sigma_partials  fp64 moments per 16,384-value block (clears look-back words)
-//   zc_sigma_finalize  per-segment variance -> window, header, work counter reset
-//   zc_encode          codes, sign+mantissa bytes, escapes, tables, sizes
+//   zc_sigma_partials  fp64 moments per 16,384-value block; clears encoder state
+//   zc_encode          per segment: variance -> window, header (first chunk);
+//                      codes, sign+mantissa bytes, escapes, tables, sizes
 // Decompress: zc_decode.  Decompress-reduce: zc_decode<REDUCE>.
 // Every call enqueues on the caller's stream and returns; nothing here reads
 // device memory except the two zc_read_* helpers, which synchronise.
@@ -13,13 +13,14 @@
 #include <new>
 #include <vector>
 
-#include "../../include/zc.h"
+#include "zc.h"
 #include "zc_kernels.h"
 
 using namespace zc;
 
 struct zc_plan {
     uint32_t nseg = 0, chunk = 0, block = 0;
+    bool has_empty = false;
     std::vector<SegDesc> segs;
     std::vector<ItemDesc> blocks, chunks, groups;
     uint64_t input_elems = 0, out_bytes = 0;
@@ -81,21 +82,26 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     SegStat* stats = ws_ptr<SegStat>(p, d_ws, p->ws.stats);
     uint64_t* flags = ws_ptr<uint64_t>(p, d_ws, p->ws.flags);
     uint32_t* ticket = ws_ptr<uint32_t>(p, d_ws, p->ws.ticket);
+    uint32_t* lflags = ws_ptr<uint32_t>(p, d_ws, p->ws.lflags);
     const uint16_t* in = static_cast<const uint16_t*>(d_in);
     uint8_t* out = static_cast<uint8_t*>(d_out);
 
     if (!forced_L && nblocks(p)) {
-        SigmaArgs sa{p->d_segs, p->d_blocks, in, partials, flags, p->block, p->chunk};
+        SigmaArgs sa{p->d_segs, p->d_blocks, in, partials, flags, lflags, ticket, p->block, p->chunk};
         launch_sigma(p, sa, stream);
     } else if (nchunks(p)) {
-        ResetArgs ra{flags, nchunks(p)};
-        const uint32_t grid = (nchunks(p) + 255) / 256;
+        ResetArgs ra{flags, lflags, ticket, nchunks(p), p->nseg};
+        const uint32_t n = nchunks(p) > p->nseg ? nchunks(p) : p->nseg;
+        const uint32_t grid = (n + 255) / 256;
         hipLaunchKernelGGL(zc_reset_flags, dim3(grid < 1024 ? grid : 1024), dim3(256), 0, stream, ra);
     }
-    FinalizeArgs fa{p->d_segs, partials, stats, ticket, out, d_stream_bytes, p->chunk, forced_L};
-    hipLaunchKernelGGL(zc_sigma_finalize, dim3(p->nseg), dim3(1024), 0, stream, fa);
+    if (p->has_empty) {
+        EmptyArgs ma{p->d_segs, out, d_stream_bytes, stats, p->chunk, forced_L};
+        hipLaunchKernelGGL(zc_empty_headers, dim3(p->nseg), dim3(64), 0, stream, ma);
+    }
     if (nchunks(p)) {
-        EncodeArgs ea{p->d_segs, p->d_chunks, in, out, d_stream_bytes, stats, flags, ticket, p->chunk};
+        EncodeArgs ea{p->d_segs, p->d_chunks, in, out, d_stream_bytes, partials, stats, lflags,
+                      flags, ticket, p->chunk, forced_L};
         // one wave per group up to 16 waves, then two groups per wave
         const uint32_t gpc = p->chunk / kGroup;
         const dim3 grid(nchunks(p)), block(64 * (gpc < 16 ? gpc : 16));
@@ -146,6 +152,7 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
         }
         SegDesc d{};
         d.n = n;
+        if (n == 0) p->has_empty = true;
         d.k = (uint32_t)cdiv(n, C);
         d.g = (uint32_t)cdiv(n, kGroup);
         d.nsb = (uint32_t)cdiv(n, p->block);
@@ -178,6 +185,7 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
     p->ws.partials = o; o += a256(sizeof(Partial) * B);
     p->ws.flags = o;    o += a256(8 * K);
     p->ws.stats = o;    o += a256(sizeof(SegStat) * num_segments);
+    p->ws.lflags = o;   o += a256(4ull * num_segments);
     p->ws.ticket = o;   o += 256;
     p->ws.total = o;
 

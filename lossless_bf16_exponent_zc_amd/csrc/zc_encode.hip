@@ -6,13 +6,17 @@
 // technique 2 (GPU kernel with a communication-aware, aligned layout).
 //
 // One workgroup per chunk; each wave owns GPW consecutive 2048-value groups.
+//  0. the workgroup of a segment's first chunk joins the segment's moment
+//     partials (fp64, pairwise) into the variance, picks the window and
+//     publishes it; the other workgroups issue their loads first and then
+//     wait for the window (that chunk always holds an earlier ticket);
 //  1. one 16-byte load per lane per tile; packed 16-bit ops give (e - L)
 //     clamped to 7 for two values at a time; nibble packing and a 4-way bit
 //     interleave turn the lane's 32 codes into its three plane words;
 //  2. sign+mantissa bytes from two byte permutes and a bit select; planes and
 //     sign+mantissa bytes go out at once (their offsets are static);
-//  3. the lane keeps only its 32 exponent bytes, in plane-bit order, and its
-//     escape mask (code 7 = all three plane bits set);
+//  3. the lane's 32 exponent bytes go to LDS in plane-bit order, so only its
+//     escape mask (code 7 = all three plane bits set) stays in registers;
 //  4. escape counts are scanned across the wave (shuffles) and across the
 //     chunk (LDS), which gives the group table; the chunk's offset in the
 //     segment's escape stream comes from a decoupled look-back in which one
@@ -20,6 +24,7 @@
 //     the workgroups, so every chunk waited on is already running);
 //  5. each lane writes its escape exponents, contiguous in code order.
 #include "zc_kernels.h"
+#include "zc_moments.h"
 
 namespace zc {
 
@@ -115,10 +120,12 @@ __device__ uint32_t look_back(uint64_t* flags, uint32_t ci, uint32_t local, uint
 
 template <int GPW>
 __global__ __launch_bounds__(1024) void zc_encode(EncodeArgs a) {
-    __shared__ uint32_t s_ticket, s_prefix;
+    __shared__ uint32_t s_ticket, s_prefix, s_L;
     __shared__ uint32_t s_gbase[32];
-    __shared__ __attribute__((aligned(16))) uint32_t s_q[16][64 * 10];  // per wave: 32 exponent
-    // bytes per lane at a 40-byte stride (10 dwords: reads by byte index spread over banks)
+    __shared__ MomentScratch s_mom;
+    // per wave and group: the 32 exponent bytes of each lane at a 36-byte
+    // stride (9 dwords, so byte reads at lane-dependent offsets spread banks)
+    __shared__ uint32_t s_q[16][GPW * 64 * 9];
 
     const uint32_t lane = lane_id(), wave = wave_id(), nwaves = blockDim.x >> 6;
     if (threadIdx.x == 0) s_ticket = atomicAdd(a.ticket, 1u);
@@ -126,28 +133,62 @@ __global__ __launch_bounds__(1024) void zc_encode(EncodeArgs a) {
     const uint32_t ci = uniform(s_ticket);
     const ItemDesc cd = a.chunks[ci];
     const SegDesc sd = a.segs[cd.seg];
-    const uint32_t L = a.stats[cd.seg].L;
-    const uint32_t L7 = (L << 7) | (L << 23);
     const uint16_t* __restrict__ x = a.in + sd.in_off;
     uint8_t* __restrict__ st = a.out + sd.out_off;
     const uint32_t gpc = a.chunk_elems / kGroup;
     const uint64_t g0 = (uint64_t)cd.local * gpc + (uint64_t)wave * GPW;
 
+    // The segment's window: its first chunk joins the moment partials (before
+    // issuing its own loads, to keep registers free); the others load first,
+    // then wait for the window word.
+    if (cd.local == 0) {
+        double s1 = 0.0, s2 = 0.0;
+        uint64_t n = 0;
+        if (!a.forced_L) reduce_partials(a.partials + sd.sb_base, sd.nsb, blockDim.x, s_mom, s1, s2, n);
+        if (threadIdx.x == 0) {
+            SegStat ss{};
+            ss.s1 = s1;
+            ss.s2 = s2;
+            ss.n = n;
+            ss.var = a.forced_L ? 0.0 : variance(s1, s2, n);
+            ss.L = a.forced_L ? a.forced_L : window_from_variance(ss.var);
+            a.stats[cd.seg] = ss;
+            s_L = ss.L;
+            __hip_atomic_store(a.lflags + cd.seg, 0x100u | ss.L, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            write_static_header(st, sd, a.chunk_elems, ss.L);
+        }
+        // zero the gap between the group table and the code region
+        for (uint64_t i = sd.gtab_off + 2ull * sd.g + threadIdx.x; i < sd.code_off; i += blockDim.x)
+            st[i] = 0;
+    }
+
+    // the first group's loads go out before the window is known; later groups
+    // are loaded one at a time (fewer registers, two workgroups per CU)
     u32x4 w[GPW][4];
 #pragma unroll
-    for (int q = 0; q < GPW; ++q) {
-        if (g0 + q < sd.g) {
-            load_group(x, sd.n, g0 + q, lane, w[q]);
-        } else {
+    for (int q = 0; q < GPW; ++q)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) w[q][k] = u32x4{0, 0, 0, 0};
-        }
+        for (int k = 0; k < 4; ++k) w[q][k] = u32x4{0, 0, 0, 0};
+    if (g0 < sd.g) load_group(x, sd.n, g0, lane, w[0]);
+
+    if (cd.local != 0 && threadIdx.x == 0) {
+        uint32_t f;
+        while ((f = __hip_atomic_load(a.lflags + cd.seg, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT)) == 0)
+            __builtin_amdgcn_s_sleep(2);
+        s_L = f & 0xFFu;
     }
-    uint32_t Q[GPW][8], M[GPW], excl[GPW];
+    __syncthreads();
+    const uint32_t L = uniform(s_L);
+    const uint32_t L7 = (L << 7) | (L << 23);
+
+    uint32_t M[GPW], excl[GPW];
 #pragma unroll
     for (int q = 0; q < GPW; ++q) {
         const uint64_t g = g0 + q;
         M[q] = 0;
+        if (q > 0 && g < sd.g) load_group(x, sd.n, g, lane, w[q]);
         if (g < sd.g) {
             uint32_t P[3];
             u32x2 sm[4];
@@ -164,8 +205,12 @@ __global__ __launch_bounds__(1024) void zc_encode(EncodeArgs a) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x2*>(sw + 512 * k) = sm[k];
             M[q] = P[0] & P[1] & P[2];
+            uint32_t Q[8];
+            exponent_bytes(w[q], Q);
+            uint32_t* qs = s_q[wave] + 9 * (64 * q + lane);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qs[i] = Q[i];
         }
-        exponent_bytes(w[q], Q[q]);
         const uint32_t cnt = __builtin_popcount(M[q]);
         const uint32_t incl = wave_inclusive_scan(cnt);
         excl[q] = incl - cnt;
@@ -200,14 +245,9 @@ __global__ __launch_bounds__(1024) void zc_encode(EncodeArgs a) {
 
     // escape exponents: each lane's are contiguous, in plane-bit order
     const uint32_t prefix = s_prefix;
-    uint32_t* qs = s_q[wave] + 10 * lane;
-    const uint8_t* qb = reinterpret_cast<const uint8_t*>(qs);
 #pragma unroll
     for (int q = 0; q < GPW; ++q) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            *reinterpret_cast<u32x2*>(qs + 2 * t) = u32x2{Q[q][2 * t], Q[q][2 * t + 1]};
-        __builtin_amdgcn_wave_barrier();
+        const uint8_t* qb = reinterpret_cast<const uint8_t*>(s_q[wave] + 9 * (64 * q + lane));
         uint8_t* esc = st + sd.esc_off + prefix + s_gbase[wave * GPW + q] + excl[q];
         uint32_t m = M[q], i = 0;
         while (m) {
@@ -215,7 +255,6 @@ __global__ __launch_bounds__(1024) void zc_encode(EncodeArgs a) {
             m &= m - 1;
             esc[i++] = qb[p];
         }
-        __builtin_amdgcn_wave_barrier();
     }
 }
 

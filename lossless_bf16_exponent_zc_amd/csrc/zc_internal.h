@@ -70,6 +70,7 @@ struct WsLayout {
     uint64_t partials;  // Partial per moment block
     uint64_t flags;     // u64 per chunk: look-back state of the encoder
     uint64_t stats;     // SegStat per segment
+    uint64_t lflags;    // u32 per segment: the encoder's window word
     uint64_t ticket;    // u32: encoder work counter
     uint64_t total;
 };

@@ -10,25 +10,28 @@ struct SigmaArgs {
     const ItemDesc* blocks;  // moment blocks
     const uint16_t* in;
     Partial* partials;
-    uint64_t* flags;         // encoder look-back words, cleared here
+    uint64_t* flags;         // encoder state, cleared here: look-back words,
+    uint32_t* lflags;        // window words,
+    uint32_t* ticket;        // work counter
     uint32_t block_elems;
     uint32_t chunk_elems;
 };
 
-struct FinalizeArgs {
-    const SegDesc* segs;
-    const Partial* partials;
-    SegStat* stats;
-    uint32_t* ticket;
-    uint8_t* out;
-    uint64_t* stream_bytes;
-    uint32_t chunk_elems;
-    uint32_t forced_L;  // 0: window from the moments
-};
-
 struct ResetArgs {
     uint64_t* flags;
-    uint32_t n;
+    uint32_t* lflags;
+    uint32_t* ticket;
+    uint32_t nchunks;
+    uint32_t nseg;
+};
+
+struct EmptyArgs {
+    const SegDesc* segs;
+    uint8_t* out;
+    uint64_t* stream_bytes;
+    SegStat* stats;
+    uint32_t chunk_elems;
+    uint32_t forced_L;
 };
 
 struct EncodeArgs {
@@ -37,10 +40,13 @@ struct EncodeArgs {
     const uint16_t* in;
     uint8_t* out;
     uint64_t* stream_bytes;
-    const SegStat* stats;
+    const Partial* partials;
+    SegStat* stats;
+    uint32_t* lflags;   // per segment: 0x100 | L once the window is known
     uint64_t* flags;
     uint32_t* ticket;
     uint32_t chunk_elems;
+    uint32_t forced_L;  // 0: window from the moments
 };
 
 struct DecodeArgs {
@@ -57,8 +63,8 @@ struct DecodeArgs {
 
 template <int NWV, int BPW>
 __global__ void zc_sigma_partials(SigmaArgs a);
-__global__ void zc_sigma_finalize(FinalizeArgs a);
 __global__ void zc_reset_flags(ResetArgs a);
+__global__ void zc_empty_headers(EmptyArgs a);
 template <int GPW>
 __global__ void zc_encode(EncodeArgs a);
 template <bool REDUCE>

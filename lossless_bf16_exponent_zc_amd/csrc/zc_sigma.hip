@@ -17,6 +17,7 @@
 // (the sigma-relative position where shifting the window by one binade
 // gains as much mass at the top as it loses at the bottom).
 #include "zc_kernels.h"
+#include "zc_moments.h"
 
 namespace zc {
 
@@ -28,15 +29,6 @@ __device__ __forceinline__ double bf16_hi(uint32_t w) {
 }
 __device__ __forceinline__ double bf16_lo(uint32_t w) {
     return (double)__uint_as_float(w << 16);
-}
-
-// Pairwise sum of 8 values in registers (index order).
-__device__ __forceinline__ double tree8(double (&v)[8]) {
-#pragma unroll
-    for (int s = 1; s < 8; s <<= 1)
-#pragma unroll
-        for (int i = 0; i < 8; i += 2 * s) v[i] = v[i] + v[i + s];
-    return v[0];
 }
 
 // Moments of 8 consecutive values (one 16-byte word).  Values at or past n
@@ -89,19 +81,13 @@ __device__ __forceinline__ void load32(const uint16_t* __restrict__ x, uint64_t 
     }
 }
 
-__device__ __forceinline__ double wave_tree(double v) {
-    // after distance d every lane holds the sum of its aligned 2d-lane block
-    // (fp64 addition is commutative, so both lanes compute the same value)
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) v = v + __shfl_xor(v, d, 64);
-    return v;
-}
-
 }  // namespace
 
 // One workgroup per moment block: NWV waves own BPW consecutive 2048-value
-// blocks each (lane l: values 32l .. 32l+31 of a block).  The block that
-// opens a chunk also clears that chunk's encoder look-back word.
+// blocks each (lane l: values 32l .. 32l+31 of a block).  It also clears the
+// encoder's state for this call: the block that opens a chunk clears that
+// chunk's look-back word, the first block of a segment its window word, and
+// block 0 the work counter.
 template <int NWV, int BPW>
 __global__ __launch_bounds__(256) void zc_sigma_partials(SigmaArgs a) {
     const uint32_t blk = blockIdx.x;
@@ -115,6 +101,8 @@ __global__ __launch_bounds__(256) void zc_sigma_partials(SigmaArgs a) {
     if (threadIdx.x == 0) {
         const uint64_t first = (uint64_t)bd.local * a.block_elems;
         if (first % a.chunk_elems == 0) a.flags[sd.chunk_base + first / a.chunk_elems] = 0;
+        if (bd.local == 0) a.lflags[bd.seg] = 0;
+        if (blk == 0) *a.ticket = 0;
     }
     if (wave < NWV) {
         double b1[BPW], b2[BPW];
@@ -178,159 +166,29 @@ __global__ __launch_bounds__(256) void zc_sigma_partials(SigmaArgs a) {
     }
 }
 
+// Clears the encoder's state when the moment pass is skipped (fixed window).
 __global__ __launch_bounds__(256) void zc_reset_flags(ResetArgs a) {
-    for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < a.n; i += gridDim.x * 256) a.flags[i] = 0;
+    const uint32_t i0 = blockIdx.x * 256 + threadIdx.x, step = gridDim.x * 256;
+    for (uint32_t i = i0; i < a.nchunks; i += step) a.flags[i] = 0;
+    for (uint32_t i = i0; i < a.nseg; i += step) a.lflags[i] = 0;
+    if (i0 == 0) *a.ticket = 0;
 }
 
-namespace {
-
-__device__ __forceinline__ uint32_t window_from_variance(double var) {
-    if (!(var > 0.0)) return 1u;
-    const double C0 = 0x1.5b16bd46a1a0cp+9;
-    // var in [2^e, 2^(e+1)) and C0 in [2^9, 2^10) bound the answer to
-    // floor((e-10)/2) .. floor((e-8)/2); step down to the first k that fits.
-    const int e = ilogb(var);
-    int k = (e - 8) >> 1;
-    while (var < ldexp(C0, 2 * k)) --k;
-    const int L = 127 + k;
-    return (uint32_t)(L < 1 ? 1 : (L > 248 ? 248 : L));
-}
-
-constexpr int kMaxLevels = 10;  // up to 8 * 512 leaves per thread
-
-}  // namespace
-
-// One workgroup (1024 threads) per segment: joins the moment blocks, picks the
-// window, writes the header fields known before encoding and resets the
-// encoder's work counter.  With forced_L != 0 the moments are skipped.
-__global__ __launch_bounds__(1024) void zc_sigma_finalize(FinalizeArgs a) {
-    const uint32_t seg = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-    const SegDesc sd = a.segs[seg];
-    __shared__ double s_v1[16], s_v2[16];
-    __shared__ unsigned long long s_n[16];
-
-    if (seg == 0 && tid == 0) *a.ticket = 0;
-
-    double s1 = 0.0, s2 = 0.0, var = 0.0;
-    uint64_t n = 0;
-    uint32_t L;
-    if (a.forced_L) {
-        L = a.forced_L;
-    } else {
-        const uint32_t B = sd.nsb;
-        uint32_t P = 1;
-        while (P < B) P <<= 1;
-        const uint32_t T = P < 1024 ? P : 1024;
-        const uint32_t m = P / T;  // leaves per thread, a power of two
-        const Partial* pp = a.partials + sd.sb_base;
-        // thread t: pairwise sum of leaves [t*m, (t+1)*m): runs of 8 by an
-        // unrolled tree (a shorter run is padded with +0.0), runs joined by a
-        // binary counter whose level h holds a finished subtree of 2^h runs
-        double r1 = 0.0, r2 = 0.0;
-        uint64_t rn = 0;
-        if (tid < T) {
-            const uint32_t runs = m > 8 ? m / 8 : 1u, len = m > 8 ? 8u : m;
-            double st1[kMaxLevels], st2[kMaxLevels];
-            for (uint32_t r = 0; r < runs; ++r) {
-                double v1[8], v2[8];
-#pragma unroll
-                for (uint32_t i = 0; i < 8; ++i) {
-                    const uint32_t leaf = tid * m + r * len + i;
-                    const bool ok = i < len && leaf < B;
-                    v1[i] = ok ? pp[leaf].s1 : 0.0;
-                    v2[i] = ok ? pp[leaf].s2 : 0.0;
-                    rn += ok ? pp[leaf].n : 0;
-                }
-                double c1 = tree8(v1), c2 = tree8(v2);
-                bool carry = true;
-#pragma unroll
-                for (int h = 0; h < kMaxLevels; ++h) {
-                    if (carry) {
-                        if ((r >> h) & 1u) {
-                            c1 = st1[h] + c1;
-                            c2 = st2[h] + c2;
-                        } else {
-                            st1[h] = c1;
-                            st2[h] = c2;
-                            carry = false;
-                        }
-                    }
-                }
-            }
-            const int top = 31 - __builtin_clz(runs);
-#pragma unroll
-            for (int h = 0; h < kMaxLevels; ++h)
-                if (h == top) {
-                    r1 = st1[h];
-                    r2 = st2[h];
-                }
-        }
-        r1 = wave_tree(r1);
-        r2 = wave_tree(r2);
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) rn += __shfl_xor(rn, d, 64);
-        if (lane == 0) {
-            s_v1[wave] = r1;
-            s_v2[wave] = r2;
-            s_n[wave] = rn;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            double t1[16], t2[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                t1[i] = s_v1[i];
-                t2[i] = s_v2[i];
-                n += s_n[i];
-            }
-#pragma unroll
-            for (int s = 1; s < 16; s <<= 1)
-#pragma unroll
-                for (int i = 0; i < 16; i += 2 * s) {
-                    t1[i] = t1[i] + t1[i + s];
-                    t2[i] = t2[i] + t2[i + s];
-                }
-            s1 = t1[0];
-            s2 = t2[0];
-            if (n > 0) {
-                const double d = (double)n;
-                const double mean = s1 / d;
-                const double ex2 = s2 / d;
-                const double sq = mean * mean;
-                var = ex2 - sq;
-                if (!(var > 0.0)) var = 0.0;
-            }
-        }
-        L = window_from_variance(var);
-    }
-
+// Streams of empty segments: no chunk exists to write them.
+__global__ __launch_bounds__(64) void zc_empty_headers(EmptyArgs a) {
+    const SegDesc sd = a.segs[blockIdx.x];
+    if (sd.k != 0 || threadIdx.x != 0) return;
     uint8_t* st = a.out + sd.out_off;
-    if (tid == 0) {
-        SegStat s;
-        s.s1 = s1;
-        s.s2 = s2;
-        s.var = var;
-        s.n = n;
-        s.L = L;
-        s.pad[0] = s.pad[1] = s.pad[2] = 0;
-        a.stats[seg] = s;
-        *reinterpret_cast<uint32_t*>(st + 0) = kMagic;
-        *reinterpret_cast<uint32_t*>(st + 4) = kVersion | (L << 16);  // flags byte = 0
-        *reinterpret_cast<uint64_t*>(st + 8) = sd.n;
-        *reinterpret_cast<uint32_t*>(st + 16) = a.chunk_elems;
-        *reinterpret_cast<uint32_t*>(st + 20) = sd.k;
-        *reinterpret_cast<uint64_t*>(st + 40) = sd.code_off;
-        *reinterpret_cast<uint64_t*>(st + 48) = sd.sm_off;
-        *reinterpret_cast<uint64_t*>(st + 56) = sd.esc_off;
-        if (sd.k == 0) {
-            *reinterpret_cast<uint32_t*>(st + kHeaderBytes) = 0;  // chunk table entry 0 = E
-            *reinterpret_cast<uint64_t*>(st + 24) = 0;
-            *reinterpret_cast<uint64_t*>(st + 32) = sd.esc_off;
-            a.stream_bytes[seg] = sd.esc_off;
-        }
-    }
-    // zero the gap between the group table and the code region
-    for (uint64_t i = sd.gtab_off + 2ull * sd.g + tid; i < sd.code_off; i += 1024) st[i] = 0;
+    const uint32_t L = a.forced_L ? a.forced_L : 1u;  // no finite values: var = 0
+    write_static_header(st, sd, a.chunk_elems, L);
+    *reinterpret_cast<uint32_t*>(st + kHeaderBytes) = 0;  // chunk table entry 0 = E
+    *reinterpret_cast<uint64_t*>(st + 24) = 0;
+    *reinterpret_cast<uint64_t*>(st + 32) = sd.esc_off;
+    for (uint64_t i = kHeaderBytes + 4; i < sd.code_off; ++i) st[i] = 0;
+    a.stream_bytes[blockIdx.x] = sd.esc_off;
+    SegStat z{};
+    z.L = L;
+    a.stats[blockIdx.x] = z;
 }
 
 template __global__ void zc_sigma_partials<1, 1>(SigmaArgs);
