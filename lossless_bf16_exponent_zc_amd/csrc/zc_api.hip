@@ -1,9 +1,14 @@
 // zc_api.hip -- the C ABI: plans, argument checks and launch sequences.
 //
 // Compress (ZipCCL scribe notes, "Key idea and contribution", technique 1):
-//   zc_sigma_partials  fp64 moments per 16,384-value block; clears encoder state
-//   zc_encode          per segment: variance -> window, header (first chunk);
-//                      codes, sign+mantissa bytes, escapes, tables, sizes
+//   zc_sigma_partials  fp64 moments per 16,384-value block
+//   zc_window          per segment: variance -> window, statistics, header
+//                      fields known before encoding; clears escape counts
+//   zc_encode          codes, sign+mantissa bytes, escape exponents staged
+//                      per group, escape counts per group, chunk and run of
+//                      chunks (one wave per two groups)
+//   zc_place_escapes   group table, chunk offsets, escapes to their place,
+//                      chunk table, sizes
 // Decompress: zc_decode.  Decompress-reduce: zc_decode<REDUCE>.
 // Every call enqueues on the caller's stream and returns; nothing here reads
 // device memory except the two zc_read_* helpers, which synchronise.
@@ -19,16 +24,16 @@
 using namespace zc;
 
 struct zc_plan {
-    uint32_t nseg = 0, chunk = 0, block = 0;
-    bool has_empty = false;
+    uint32_t nseg = 0, chunk = 0, block = 0, nsums = 0;
     std::vector<SegDesc> segs;
-    std::vector<ItemDesc> blocks, chunks, groups;
+    std::vector<ItemDesc> blocks, chunks, groups, pairs;  // pairs: encoder waves
     uint64_t input_elems = 0, out_bytes = 0;
     WsLayout ws{};
     SegDesc* d_segs = nullptr;
     ItemDesc* d_blocks = nullptr;
     ItemDesc* d_chunks = nullptr;
     ItemDesc* d_groups = nullptr;
+    ItemDesc* d_pairs = nullptr;
 };
 
 namespace {
@@ -80,35 +85,34 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
 
     Partial* partials = ws_ptr<Partial>(p, d_ws, p->ws.partials);
     SegStat* stats = ws_ptr<SegStat>(p, d_ws, p->ws.stats);
-    uint64_t* flags = ws_ptr<uint64_t>(p, d_ws, p->ws.flags);
-    uint32_t* ticket = ws_ptr<uint32_t>(p, d_ws, p->ws.ticket);
-    uint32_t* lflags = ws_ptr<uint32_t>(p, d_ws, p->ws.lflags);
+    uint32_t* sums = ws_ptr<uint32_t>(p, d_ws, p->ws.sums);
+    uint32_t* gcnt = ws_ptr<uint32_t>(p, d_ws, p->ws.gcnt);
+    unsigned long long* cacc = ws_ptr<unsigned long long>(p, d_ws, p->ws.cacc);
+    uint8_t* staging = ws_ptr<uint8_t>(p, d_ws, p->ws.staging);
     const uint16_t* in = static_cast<const uint16_t*>(d_in);
     uint8_t* out = static_cast<uint8_t*>(d_out);
 
     if (!forced_L && nblocks(p)) {
-        SigmaArgs sa{p->d_segs, p->d_blocks, in, partials, flags, lflags, ticket, p->block, p->chunk};
+        SigmaArgs sa{p->d_segs, p->d_blocks, in, partials, p->block};
         launch_sigma(p, sa, stream);
-    } else if (nchunks(p)) {
-        ResetArgs ra{flags, lflags, ticket, nchunks(p), p->nseg};
-        const uint32_t n = nchunks(p) > p->nseg ? nchunks(p) : p->nseg;
-        const uint32_t grid = (n + 255) / 256;
-        hipLaunchKernelGGL(zc_reset_flags, dim3(grid < 1024 ? grid : 1024), dim3(256), 0, stream, ra);
     }
-    if (p->has_empty) {
-        EmptyArgs ma{p->d_segs, out, d_stream_bytes, stats, p->chunk, forced_L};
-        hipLaunchKernelGGL(zc_empty_headers, dim3(p->nseg), dim3(64), 0, stream, ma);
-    }
+    WindowArgs wa{p->d_segs, partials, stats, out, d_stream_bytes, cacc, sums, p->chunk, forced_L};
+    hipLaunchKernelGGL(zc_window, dim3(p->nseg), dim3(1024), 0, stream, wa);
     if (nchunks(p)) {
-        EncodeArgs ea{p->d_segs, p->d_chunks, in, out, d_stream_bytes, partials, stats, lflags,
-                      flags, ticket, p->chunk, forced_L};
-        // one wave per group up to 16 waves, then two groups per wave
+        EncodeArgs ea{p->d_segs, p->d_pairs, in, out, stats, staging, gcnt, cacc, sums, p->chunk};
+        PlaceArgs pa{p->d_segs, p->d_chunks, out, d_stream_bytes, staging, gcnt, cacc, sums, p->chunk};
         const uint32_t gpc = p->chunk / kGroup;
-        const dim3 grid(nchunks(p)), block(64 * (gpc < 16 ? gpc : 16));
-        if (gpc > 16)
-            hipLaunchKernelGGL((zc_encode<2>), grid, block, 0, stream, ea);
-        else
-            hipLaunchKernelGGL((zc_encode<1>), grid, block, 0, stream, ea);
+        const dim3 grid(nchunks(p));
+        hipLaunchKernelGGL(zc_encode, dim3((uint32_t)(p->pairs.size() / 4)), dim3(256), 0, stream, ea);
+        // placement: up to 4 waves, each with gpc / waves groups
+        const uint32_t pw = gpc < 4 ? gpc : 4;
+        const dim3 pblock(64 * pw);
+        switch (gpc / pw) {
+            case 1: hipLaunchKernelGGL((zc_place_escapes<1>), grid, pblock, 0, stream, pa); break;
+            case 2: hipLaunchKernelGGL((zc_place_escapes<2>), grid, pblock, 0, stream, pa); break;
+            case 4: hipLaunchKernelGGL((zc_place_escapes<4>), grid, pblock, 0, stream, pa); break;
+            default: hipLaunchKernelGGL((zc_place_escapes<8>), grid, pblock, 0, stream, pa); break;
+        }
     }
     return launch_status();
 }
@@ -152,7 +156,6 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
         }
         SegDesc d{};
         d.n = n;
-        if (n == 0) p->has_empty = true;
         d.k = (uint32_t)cdiv(n, C);
         d.g = (uint32_t)cdiv(n, kGroup);
         d.nsb = (uint32_t)cdiv(n, p->block);
@@ -166,11 +169,15 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
         d.sb_base = (uint32_t)p->blocks.size();
         d.group_base = (uint32_t)p->groups.size();
         d.chunk_base = (uint32_t)p->chunks.size();
+        d.c1_base = p->nsums;
+        d.c2_base = d.c1_base + (uint32_t)cdiv(d.k, 256);
+        p->nsums = d.c2_base + (uint32_t)cdiv(d.k, 65536);
         in_off += (n + 7) & ~uint64_t(7);
         out_off += a256(d.max_bytes);
         for (uint32_t b = 0; b < d.nsb; ++b) p->blocks.push_back(ItemDesc{s, b});
         for (uint32_t k = 0; k < d.k; ++k) p->chunks.push_back(ItemDesc{s, k});
         for (uint32_t g = 0; g < d.g; ++g) p->groups.push_back(ItemDesc{s, g});
+        for (uint32_t q = 0; q < (d.g + 1) / 2; ++q) p->pairs.push_back(ItemDesc{s, q});
         if (p->groups.size() >= (1ull << 31)) {
             delete p;
             return ZC_ERR_UNSUPPORTED;
@@ -179,20 +186,24 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
     }
     p->input_elems = in_off;
     p->out_bytes = out_off;
+    while (p->pairs.size() % 4) p->pairs.push_back(ItemDesc{0xFFFFFFFFu, 0});  // whole workgroups
     const uint64_t G = p->groups.size(), B = p->blocks.size(), K = p->chunks.size();
+    const uint64_t W = p->pairs.size();
     uint64_t o = 0;
     p->ws.status = o;   o += a256(4 * G);
     p->ws.partials = o; o += a256(sizeof(Partial) * B);
-    p->ws.flags = o;    o += a256(8 * K);
     p->ws.stats = o;    o += a256(sizeof(SegStat) * num_segments);
-    p->ws.lflags = o;   o += a256(4ull * num_segments);
-    p->ws.ticket = o;   o += 256;
+    p->ws.gcnt = o;     o += a256(4 * G);
+    p->ws.cacc = o;     o += a256(8 * K);
+    p->ws.sums = o;     o += a256(4ull * p->nsums);
+    p->ws.staging = o;  o += a256((uint64_t)kGroup * G + 16);
     p->ws.total = o;
 
     if (hipMalloc(&p->d_segs, sizeof(SegDesc) * p->segs.size()) != hipSuccess ||
         hipMalloc(&p->d_blocks, sizeof(ItemDesc) * (B ? B : 1)) != hipSuccess ||
         hipMalloc(&p->d_chunks, sizeof(ItemDesc) * (K ? K : 1)) != hipSuccess ||
         hipMalloc(&p->d_groups, sizeof(ItemDesc) * (G ? G : 1)) != hipSuccess ||
+        hipMalloc(&p->d_pairs, sizeof(ItemDesc) * (W ? W : 1)) != hipSuccess ||
         hipMemcpy(p->d_segs, p->segs.data(), sizeof(SegDesc) * p->segs.size(),
                   hipMemcpyHostToDevice) != hipSuccess ||
         (B && hipMemcpy(p->d_blocks, p->blocks.data(), sizeof(ItemDesc) * B,
@@ -200,6 +211,8 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
         (K && hipMemcpy(p->d_chunks, p->chunks.data(), sizeof(ItemDesc) * K,
                         hipMemcpyHostToDevice) != hipSuccess) ||
         (G && hipMemcpy(p->d_groups, p->groups.data(), sizeof(ItemDesc) * G,
+                        hipMemcpyHostToDevice) != hipSuccess) ||
+        (W && hipMemcpy(p->d_pairs, p->pairs.data(), sizeof(ItemDesc) * W,
                         hipMemcpyHostToDevice) != hipSuccess)) {
         zc_plan_destroy(p);
         return ZC_ERR_HIP;
@@ -214,6 +227,7 @@ void zc_plan_destroy(zc_plan* p) {
     if (p->d_blocks) (void)hipFree(p->d_blocks);
     if (p->d_chunks) (void)hipFree(p->d_chunks);
     if (p->d_groups) (void)hipFree(p->d_groups);
+    if (p->d_pairs) (void)hipFree(p->d_pairs);
     delete p;
 }
 

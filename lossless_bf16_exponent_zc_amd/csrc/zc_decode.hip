@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void zc_decode(DecodeArgs a) {
             const uint32_t cnt = __builtin_popcount(M);
             const uint32_t incl = wave_inclusive_scan(cnt);
             if (__ballot(padbad)) bad |= kBadPad;
-            if (__shfl(incl, 63, 64) != cur.span) bad |= kBadCount;
+            if (readlane(incl, 63) != cur.span) bad |= kBadCount;
             if (!bad) {
                 u32x4 o[4];
                 rebuild(cur, M, first + incl - cnt, escb, s_stage[wave], lane, o);

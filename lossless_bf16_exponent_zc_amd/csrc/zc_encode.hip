@@ -5,24 +5,26 @@
 // stay raw, other exponents are kept whole in a separate stream) and
 // technique 2 (GPU kernel with a communication-aware, aligned layout).
 //
-// One workgroup per chunk; each wave owns GPW consecutive 2048-value groups.
-//  0. the workgroup of a segment's first chunk joins the segment's moment
-//     partials (fp64, pairwise) into the variance, picks the window and
-//     publishes it; the other workgroups issue their loads first and then
-//     wait for the window (that chunk always holds an earlier ticket);
-//  1. one 16-byte load per lane per tile; packed 16-bit ops give (e - L)
-//     clamped to 7 for two values at a time; nibble packing and a 4-way bit
-//     interleave turn the lane's 32 codes into its three plane words;
-//  2. sign+mantissa bytes from two byte permutes and a bit select; planes and
-//     sign+mantissa bytes go out at once (their offsets are static);
-//  3. the lane's 32 exponent bytes go to LDS in plane-bit order, so only its
-//     escape mask (code 7 = all three plane bits set) stays in registers;
-//  4. escape counts are scanned across the wave (shuffles) and across the
-//     chunk (LDS), which gives the group table; the chunk's offset in the
-//     segment's escape stream comes from a decoupled look-back in which one
-//     wave reads 64 earlier chunks per round (an atomic work counter orders
-//     the workgroups, so every chunk waited on is already running);
-//  5. each lane writes its escape exponents, contiguous in code order.
+// Two kernels, so that the streaming one never waits on another wave:
+//
+// zc_encode, one workgroup per chunk, each wave GPW consecutive 2048-value
+// groups, both loaded at once.  Per group: one 16-byte load per lane and
+// tile; packed 16-bit ops give (e - L) clamped to 7 for two values at a
+// time; nibble packing and a 4-way bit interleave turn the lane's 32 codes
+// into its three plane words; plane words and sign+mantissa bytes go out at
+// once (static offsets).  Escapes (code 7 = all three plane bits set) are
+// counted and ranked across the wave with ballots; the lanes' escape
+// exponents are packed in code order into the wave's LDS area and go out in
+// aligned dwords to the group's staging slot.  The chunk's count is summed
+// with one LDS atomic per wave; the last wave stores it and adds it to the
+// coarse counts (per 256 and per 65,536 chunks).
+//
+// zc_place_escapes, one workgroup per chunk, one wave per encoder wave: the
+// group counts give the group table; the counts before the chunk (coarse
+// counts, then chunk counts: at most 32 + 255 + 255 independent loads) give
+// its offset in the segment's escape stream; each wave's runs, whose source
+// dwords are loaded before that offset is known, go to their place.  The
+// chunk table, the header's sizes and the stream size are written here.
 #include "zc_kernels.h"
 #include "zc_moments.h"
 
@@ -66,174 +68,185 @@ __device__ __forceinline__ void exponent_bytes(const u32x4 (&w)[4], uint32_t (&Q
     }
 }
 
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) v += __shfl_xor(v, d, 64);
-    return v;
+// Byte p of the lane's 32 exponent bytes (plane-bit order).  Selects between
+// values, not array elements: a conditional over array lvalues would select
+// addresses and keep the array in scratch memory.
+__device__ __forceinline__ uint32_t exponent_byte(const uint32_t (&Q)[8], uint32_t p) {
+    const uint32_t q0 = Q[0], q1 = Q[1], q2 = Q[2], q3 = Q[3];
+    const uint32_t q4 = Q[4], q5 = Q[5], q6 = Q[6], q7 = Q[7];
+    const uint32_t d = p >> 2;
+    const uint32_t lo = (d & 2) ? ((d & 1) ? q3 : q2) : ((d & 1) ? q1 : q0);
+    const uint32_t hi = (d & 2) ? ((d & 1) ? q7 : q6) : ((d & 1) ? q5 : q4);
+    return ((d & 4) ? hi : lo) >> (8 * (p & 3));
 }
 
-__device__ __forceinline__ uint64_t load_flag(const uint64_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void store_flag(uint64_t* p, uint64_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Run by one whole wave.  Publishes the chunk's count, then finds the
-// exclusive escape prefix of chunk `ci` (local index `local` in its segment):
-// lane i of a round looks at the chunk base + i + 1 places back; a round is
-// usable once every chunk before the nearest published prefix has at least
-// published its count.
-__device__ uint32_t look_back(uint64_t* flags, uint32_t ci, uint32_t local, uint32_t total) {
+// One wave stores a run of n bytes (a group's escape exponents) from `src`
+// (the group's 2048-byte staging slot) to `dst`.  The caller has loaded, for
+// output dwords k = lane + 64 r (r < R), lo[r] = source dword k and hi[r] =
+// source dword k+1: output dword k starts at source byte head + 4k, where
+// head (0..3) brings dst to a 4-byte boundary, so those two dwords serve
+// whatever dst is.  The head bytes come from lane 0's first source dword,
+// the tail bytes from the lane owning the last partial dword; dwords past
+// 64 R (runs over 256 R bytes) are loaded here.
+template <int R>
+__device__ __forceinline__ void store_run(uint8_t* dst, const uint32_t* src, uint32_t n,
+                                          const uint32_t (&lo)[R], const uint32_t (&hi)[R]) {
     const uint32_t lane = lane_id();
-    if (local == 0) {
-        if (lane == 0) store_flag(flags + ci, kFlagPrefix | total);
-        return 0;
+    const uint32_t head = min(n, (4u - (uint32_t)(reinterpret_cast<uintptr_t>(dst) & 3u)) & 3u);
+    const uint32_t nd = (n - head) >> 2, tail = (n - head) & 3u;
+    uint32_t* d32 = reinterpret_cast<uint32_t*>(dst + head);
+    if (lane == 0)
+        for (uint32_t i = 0; i < head; ++i) dst[i] = (uint8_t)(lo[0] >> (8 * i));
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t k = lane + 64 * r;
+        const uint32_t v = (uint32_t)((((uint64_t)hi[r] << 32) | lo[r]) >> (8 * head));
+        if (k < nd) d32[k] = v;
+        if (k == nd)  // the partial last dword: `tail` bytes
+            for (uint32_t i = 0; i < tail; ++i) dst[head + 4 * nd + i] = (uint8_t)(v >> (8 * i));
     }
-    if (lane == 0) store_flag(flags + ci, kFlagAggregate | total);
-    uint32_t acc = 0;
-    for (uint32_t base = 0;; base += 64) {
-        const uint32_t d = base + lane + 1;
-        const bool valid = d <= local;
-        uint64_t f;
-        uint32_t fp;
-        for (;;) {
-            f = valid ? load_flag(flags + ci - d) : 0;
-            const uint32_t st = (uint32_t)(f >> 62);
-            const uint64_t valid_m = __ballot(valid);
-            const uint64_t pre_m = __ballot(valid && st == 2);
-            const uint64_t rdy_m = __ballot(valid && st != 0);
-            fp = pre_m ? (uint32_t)__builtin_ctzll(pre_m) : 64u;
-            const uint64_t need = fp == 64 ? valid_m : ((1ull << fp) - 1);
-            if ((rdy_m & need) == need && (fp < 64 || valid_m == ~0ull)) break;
-            __builtin_amdgcn_s_sleep(1);
-        }
-        acc += wave_sum(valid && lane <= fp ? (uint32_t)f : 0u);
-        if (fp < 64) break;
+    for (uint32_t k = lane + 64 * R; k <= nd; k += 64) {
+        const uint32_t v = (uint32_t)((((uint64_t)src[k + 1] << 32) | src[k]) >> (8 * head));
+        if (k < nd)
+            d32[k] = v;
+        else
+            for (uint32_t i = 0; i < tail; ++i) dst[head + 4 * nd + i] = (uint8_t)(v >> (8 * i));
     }
-    if (lane == 0) store_flag(flags + ci, kFlagPrefix | (acc + total));
-    return acc;
 }
 
 }  // namespace
 
-template <int GPW>
-__global__ __launch_bounds__(1024) void zc_encode(EncodeArgs a) {
-    __shared__ uint32_t s_ticket, s_prefix, s_L;
-    __shared__ uint32_t s_gbase[32];
-    __shared__ MomentScratch s_mom;
-    // per wave and group: the 32 exponent bytes of each lane at a 36-byte
-    // stride (9 dwords, so byte reads at lane-dependent offsets spread banks)
-    __shared__ uint32_t s_q[16][GPW * 64 * 9];
-
-    const uint32_t lane = lane_id(), wave = wave_id(), nwaves = blockDim.x >> 6;
-    if (threadIdx.x == 0) s_ticket = atomicAdd(a.ticket, 1u);
-    __syncthreads();
-    const uint32_t ci = uniform(s_ticket);
-    const ItemDesc cd = a.chunks[ci];
-    const SegDesc sd = a.segs[cd.seg];
+// Four waves per workgroup, each with two consecutive groups of one segment
+// (item list: one entry per wave-pair of groups), no workgroup barrier.
+// LDS: 2048 + 16 bytes per wave (every value of a group may escape).
+__global__ __launch_bounds__(256) void zc_encode(EncodeArgs a) {
+    __shared__ uint32_t s_e[4][(kGroup + 16) / 4];
+    const uint32_t lane = lane_id(), wave = wave_id();
+    const ItemDesc it = a.pairs[blockIdx.x * 4 + wave];  // (segment, first group / 2)
+    if (it.seg == 0xFFFFFFFFu) return;                   // grid padding
+    const SegDesc sd = a.segs[it.seg];
     const uint16_t* __restrict__ x = a.in + sd.in_off;
     uint8_t* __restrict__ st = a.out + sd.out_off;
     const uint32_t gpc = a.chunk_elems / kGroup;
-    const uint64_t g0 = (uint64_t)cd.local * gpc + (uint64_t)wave * GPW;
+    const uint64_t g0 = 2ull * it.local;
 
-    // The segment's window: its first chunk joins the moment partials (before
-    // issuing its own loads, to keep registers free); the others load first,
-    // then wait for the window word.
-    if (cd.local == 0) {
-        double s1 = 0.0, s2 = 0.0;
-        uint64_t n = 0;
-        if (!a.forced_L) reduce_partials(a.partials + sd.sb_base, sd.nsb, blockDim.x, s_mom, s1, s2, n);
-        if (threadIdx.x == 0) {
-            SegStat ss{};
-            ss.s1 = s1;
-            ss.s2 = s2;
-            ss.n = n;
-            ss.var = a.forced_L ? 0.0 : variance(s1, s2, n);
-            ss.L = a.forced_L ? a.forced_L : window_from_variance(ss.var);
-            a.stats[cd.seg] = ss;
-            s_L = ss.L;
-            __hip_atomic_store(a.lflags + cd.seg, 0x100u | ss.L, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            write_static_header(st, sd, a.chunk_elems, ss.L);
+    u32x4 w[2][4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        if (g0 + q < sd.g) {
+            load_group(x, sd.n, g0 + q, lane, w[q]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[q][k] = u32x4{0, 0, 0, 0};
         }
-        // zero the gap between the group table and the code region
-        for (uint64_t i = sd.gtab_off + 2ull * sd.g + threadIdx.x; i < sd.code_off; i += blockDim.x)
-            st[i] = 0;
     }
-
-    // the first group's loads go out before the window is known; later groups
-    // are loaded one at a time (fewer registers, two workgroups per CU)
-    u32x4 w[GPW][4];
-#pragma unroll
-    for (int q = 0; q < GPW; ++q)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) w[q][k] = u32x4{0, 0, 0, 0};
-    if (g0 < sd.g) load_group(x, sd.n, g0, lane, w[0]);
-
-    if (cd.local != 0 && threadIdx.x == 0) {
-        uint32_t f;
-        while ((f = __hip_atomic_load(a.lflags + cd.seg, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT)) == 0)
-            __builtin_amdgcn_s_sleep(2);
-        s_L = f & 0xFFu;
-    }
-    __syncthreads();
-    const uint32_t L = uniform(s_L);
+    const uint32_t L = a.stats[it.seg].L;
     const uint32_t L7 = (L << 7) | (L << 23);
 
-    uint32_t M[GPW], excl[GPW];
+    uint8_t* ew = reinterpret_cast<uint8_t*>(s_e[wave]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const uint64_t g = g0 + q;
+        if (g >= sd.g) break;  // uniform
+        uint32_t P[3];
+        u32x2 sm[4];
+        encode_group(w[q], L7, P, sm);
+        if ((uint64_t)kGroup * (g + 1) > sd.n) {  // last, partial group: padding codes are 0
+            const uint32_t V = valid_bits(lane, (uint32_t)(sd.n - (uint64_t)kGroup * g));
+#pragma unroll
+            for (int b = 0; b < 3; ++b) P[b] &= V;
+        }
+        uint8_t* cw = st + sd.code_off + 768ull * g + 4u * lane;
+#pragma unroll
+        for (int b = 0; b < 3; ++b) *reinterpret_cast<uint32_t*>(cw + 256 * b) = P[b];
+        uint8_t* sw = st + sd.sm_off + 2048ull * g + 8u * lane;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x2*>(sw + 512 * k) = sm[k];
+        const uint32_t M = P[0] & P[1] & P[2];
+        uint32_t tot;
+        const uint32_t excl = wave_prefix_small(__builtin_popcount(M), tot);
+        const uint64_t gg = sd.group_base + g;
+        const uint32_t chunk = sd.chunk_base + (uint32_t)(g / gpc);
+        uint64_t old = 0;
+        if (lane == 0) {
+            a.gcnt[gg] = tot;
+            old = atomicAdd(a.cacc + chunk, (1ull << 32) | tot);  // (groups done, escapes)
+        }
+        uint32_t Q[8];
+        exponent_bytes(w[q], Q);
+        for (uint32_t m = M, i = 0; m; m &= m - 1, ++i)
+            ew[excl + i] = (uint8_t)exponent_byte(Q, __builtin_ctz(m));
+        uint32_t* slot = reinterpret_cast<uint32_t*>(a.staging + gg * kGroup);
+        for (uint32_t k = lane; k < (tot + 3) / 4; k += 64) slot[k] = s_e[wave][k];
+        if (lane == 0) {
+            const uint32_t local = (uint32_t)(g / gpc);
+            const uint32_t ng = (uint32_t)min((uint64_t)gpc, sd.g - (uint64_t)local * gpc);
+            if ((uint32_t)(old >> 32) == ng - 1) {  // this group completed its chunk
+                const uint32_t t = (uint32_t)old + tot;
+                atomicAdd(a.sums + sd.c1_base + (local >> 8), t);
+                atomicAdd(a.sums + sd.c2_base + (local >> 16), t);
+            }
+        }
+    }
+}
+
+
+// One workgroup of up to 4 waves per chunk; wave w owns the chunk's groups
+// w, w + nw, ... (GPW = groups per wave).
+template <int GPW>
+__global__ __launch_bounds__(256) void zc_place_escapes(PlaceArgs a) {
+    constexpr int R = 2;  // source dword pairs per lane and group loaded ahead
+    __shared__ uint32_t s_gb[32], s_gn[32], s_prefix;  // group offsets in the chunk, counts
+    const uint32_t ci = blockIdx.x, lane = lane_id(), wave = wave_id(), nw = blockDim.x >> 6;
+    const ItemDesc cd = a.chunks[ci];
+    const SegDesc sd = a.segs[cd.seg];
+    uint8_t* st = a.out + sd.out_off;
+    const uint32_t gpc = a.chunk_elems / kGroup;
+    const uint64_t gc0 = (uint64_t)cd.local * gpc;  // the chunk's first group in the segment
+    const uint32_t ng = (uint32_t)min((uint64_t)gpc, sd.g - gc0);
+    const uint32_t* slot0 = reinterpret_cast<const uint32_t*>(a.staging) +
+                            (uint64_t)(sd.group_base + gc0) * (kGroup / 4);
+
+    // source dwords of this wave's groups: unconditional (inside the slots)
+    uint32_t lo[GPW][R], hi[GPW][R];
 #pragma unroll
     for (int q = 0; q < GPW; ++q) {
-        const uint64_t g = g0 + q;
-        M[q] = 0;
-        if (q > 0 && g < sd.g) load_group(x, sd.n, g, lane, w[q]);
-        if (g < sd.g) {
-            uint32_t P[3];
-            u32x2 sm[4];
-            encode_group(w[q], L7, P, sm);
-            if ((uint64_t)kGroup * (g + 1) > sd.n) {  // last, partial group: padding codes are 0
-                const uint32_t V = valid_bits(lane, (uint32_t)(sd.n - (uint64_t)kGroup * g));
+        const uint32_t j = wave + nw * q;
+        const uint32_t* s32 = slot0 + (uint64_t)j * (kGroup / 4);
 #pragma unroll
-                for (int b = 0; b < 3; ++b) P[b] &= V;
-            }
-            uint8_t* cw = st + sd.code_off + 768ull * g + 4u * lane;
-#pragma unroll
-            for (int b = 0; b < 3; ++b) *reinterpret_cast<uint32_t*>(cw + 256 * b) = P[b];
-            uint8_t* sw = st + sd.sm_off + 2048ull * g + 8u * lane;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x2*>(sw + 512 * k) = sm[k];
-            M[q] = P[0] & P[1] & P[2];
-            uint32_t Q[8];
-            exponent_bytes(w[q], Q);
-            uint32_t* qs = s_q[wave] + 9 * (64 * q + lane);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) qs[i] = Q[i];
+        for (int r = 0; r < R; ++r) {
+            lo[q][r] = j < ng ? s32[lane + 64 * r] : 0u;
+            hi[q][r] = j < ng ? s32[lane + 64 * r + 1] : 0u;
         }
-        const uint32_t cnt = __builtin_popcount(M[q]);
-        const uint32_t incl = wave_inclusive_scan(cnt);
-        excl[q] = incl - cnt;
-        if (lane == 63) s_gbase[wave * GPW + q] = incl;
     }
-    __syncthreads();
-
     if (wave == 0) {
-        const uint32_t ng = nwaves * GPW;
-        const uint32_t v = lane < ng ? s_gbase[lane] : 0u;
-        const uint32_t incl = wave_inclusive_scan(v);
-        const uint32_t total = __shfl(incl, 63, 64);
-        const uint64_t g = (uint64_t)cd.local * gpc + lane;
-        if (lane < ng) {
-            s_gbase[lane] = incl - v;
-            if (g < sd.g) reinterpret_cast<uint16_t*>(st + sd.gtab_off)[g] = (uint16_t)(incl - v);
+        const uint32_t l = cd.local;
+        uint32_t v = 0;
+        if (lane < (l >> 16)) v += a.sums[sd.c2_base + lane];
+#pragma unroll
+        for (uint32_t r = 0; r < 4; ++r) {
+            const uint32_t j = ((l >> 16) << 8) + lane + 64 * r;
+            if (j < (l >> 8)) v += a.sums[sd.c1_base + j];
         }
-        const uint32_t prefix = look_back(a.flags, ci, cd.local, total);
+#pragma unroll
+        for (uint32_t r = 0; r < 4; ++r) {
+            const uint32_t j = ((l >> 8) << 8) + lane + 64 * r;
+            if (j < l) v += (uint32_t)a.cacc[sd.chunk_base + j];
+        }
+        const uint32_t c = lane < ng ? a.gcnt[sd.group_base + gc0 + lane] : 0u;
+        const uint32_t incl = wave_inclusive_scan(c);
+        if (lane < ng) {
+            reinterpret_cast<uint16_t*>(st + sd.gtab_off)[gc0 + lane] = (uint16_t)(incl - c);
+            s_gb[lane] = incl - c;
+            s_gn[lane] = c;
+        }
+        const uint32_t prefix = wave_sum(v);
         if (lane == 0) {
+            const uint32_t t = readlane(incl, 63);
             s_prefix = prefix;
-            reinterpret_cast<uint32_t*>(st + kHeaderBytes)[cd.local] = prefix;
-            if (cd.local + 1 == sd.k) {
-                const uint64_t E = (uint64_t)prefix + total;
+            reinterpret_cast<uint32_t*>(st + kHeaderBytes)[l] = prefix;
+            if (l + 1 == sd.k) {
+                const uint64_t E = (uint64_t)prefix + t;
                 reinterpret_cast<uint32_t*>(st + kHeaderBytes)[sd.k] = (uint32_t)E;
                 *reinterpret_cast<uint64_t*>(st + 24) = E;
                 *reinterpret_cast<uint64_t*>(st + 32) = sd.esc_off + E;
@@ -242,23 +255,17 @@ __global__ __launch_bounds__(1024) void zc_encode(EncodeArgs a) {
         }
     }
     __syncthreads();
-
-    // escape exponents: each lane's are contiguous, in plane-bit order
-    const uint32_t prefix = s_prefix;
+    uint8_t* esc = st + sd.esc_off + s_prefix;
 #pragma unroll
     for (int q = 0; q < GPW; ++q) {
-        const uint8_t* qb = reinterpret_cast<const uint8_t*>(s_q[wave] + 9 * (64 * q + lane));
-        uint8_t* esc = st + sd.esc_off + prefix + s_gbase[wave * GPW + q] + excl[q];
-        uint32_t m = M[q], i = 0;
-        while (m) {
-            const uint32_t p = __builtin_ctz(m);
-            m &= m - 1;
-            esc[i++] = qb[p];
-        }
+        const uint32_t j = wave + nw * q;
+        if (j < ng) store_run<R>(esc + s_gb[j], slot0 + (uint64_t)j * (kGroup / 4), s_gn[j], lo[q], hi[q]);
     }
 }
 
-template __global__ void zc_encode<1>(EncodeArgs);
-template __global__ void zc_encode<2>(EncodeArgs);
+template __global__ void zc_place_escapes<1>(PlaceArgs);
+template __global__ void zc_place_escapes<2>(PlaceArgs);
+template __global__ void zc_place_escapes<4>(PlaceArgs);
+template __global__ void zc_place_escapes<8>(PlaceArgs);
 
 }  // namespace zc

@@ -44,6 +44,8 @@ struct SegDesc {
     uint32_t sb_base;    // first moment block of this segment in the plan's list
     uint32_t group_base; // first group of this segment in the plan's list
     uint32_t chunk_base; // first chunk of this segment in the plan's list
+    uint32_t c1_base;    // first escape count per 256 chunks of this segment
+    uint32_t c2_base;    // first escape count per 65,536 chunks of this segment
 };
 
 struct ItemDesc {  // a moment block, chunk or group: its segment and index inside it
@@ -68,18 +70,14 @@ struct SegStat {  // per-segment window statistics
 struct WsLayout {
     uint64_t status;    // u32 per group: rejection bits of the last decode
     uint64_t partials;  // Partial per moment block
-    uint64_t flags;     // u64 per chunk: look-back state of the encoder
     uint64_t stats;     // SegStat per segment
-    uint64_t lflags;    // u32 per segment: the encoder's window word
-    uint64_t ticket;    // u32: encoder work counter
+    uint64_t gcnt;      // u32 per group: escape count
+    uint64_t cacc;      // u64 per chunk: (groups done << 32) | escapes
+    uint64_t sums;      // u32: escape counts per 256 and per 65,536 chunks
+    uint64_t staging;   // 2048 bytes per group (+16): escape exponents before placement
     uint64_t total;
 };
 
-// Look-back flag word of a chunk: state in bits 62-63, count in bits 0-31.
-//   aggregate: the chunk's escape count
-//   prefix:    escapes of the segment up to and including the chunk
-constexpr uint64_t kFlagAggregate = 1ull << 62;
-constexpr uint64_t kFlagPrefix = 2ull << 62;
 
 // ---------------------------------------------------------------- helpers
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -115,15 +113,70 @@ __device__ __forceinline__ uint32_t wave_id() {
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Cross-lane exchange without LDS addresses: DPP moves within 16-lane rows
+// (plus the row broadcasts of the GFX9 family) and a 32-lane swizzle.  Every
+// lane of the wave must be active.
+enum : int {
+    kDppQuadX1 = 0xB1,       // quad_perm [1,0,3,2]: lane ^ 1
+    kDppQuadX2 = 0x4E,       // quad_perm [2,3,0,1]: lane ^ 2
+    kDppMirror = 0x140,      // row_mirror: lane 15 - i of the row
+    kDppHalfMirror = 0x141,  // row_half_mirror: lane 7 - i of the half row
+    kDppBcast15 = 0x142,     // row_bcast:15: lane 15 of the previous row
+    kDppBcast31 = 0x143,     // row_bcast:31: lane 31
+};
+__device__ __forceinline__ constexpr int dpp_row_shr(int n) { return 0x110 + n; }
+
+// DPP move; lanes whose source is out of range, or whose row is not in
+// `rows`, read 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
+}
+
+// Lane ^ 16 inside each 32-lane half (swizzle bit mode: and 0x1F, xor 0x10).
+__device__ __forceinline__ uint32_t swizzle_x16(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+}
+
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (row shifts, then the
+// row totals carried across rows by the two broadcasts).
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
-    const uint32_t lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t t = __shfl_up(x, d, 64);
-        if (lane >= (uint32_t)d) x += t;
-    }
+    x += dpp<dpp_row_shr(1)>(x);
+    x += dpp<dpp_row_shr(2)>(x);
+    x += dpp<dpp_row_shr(4)>(x);
+    x += dpp<dpp_row_shr(8)>(x);
+    x += dpp<kDppBcast15, 0xA>(x);
+    x += dpp<kDppBcast31, 0xC>(x);
     return x;
+}
+
+// Sum over the wave, as a wave-uniform value.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+    v += dpp<kDppQuadX1>(v);
+    v += dpp<kDppQuadX2>(v);
+    v += dpp<kDppHalfMirror>(v);  // each quad holds one value: the mirror pairs quads
+    v += dpp<kDppMirror>(v);      // each half row holds one value
+    return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
+}
+
+// Exclusive prefix over the wave of per-lane counts below 64, one ballot per
+// bit of the count; `total` is the wave's sum (wave-uniform).
+__device__ __forceinline__ uint32_t wave_prefix_small(uint32_t c, uint32_t& total) {
+    uint32_t excl = 0, tot = 0;
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {
+        const uint64_t m = __ballot((c >> b) & 1u);
+        const uint32_t below =
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        excl += below << b;
+        tot += (uint32_t)__builtin_popcountll(m) << b;
+    }
+    total = tot;
+    return excl;
 }
 
 // Value index inside a group of the value at (lane, plane bit p).

@@ -10,43 +10,44 @@ struct SigmaArgs {
     const ItemDesc* blocks;  // moment blocks
     const uint16_t* in;
     Partial* partials;
-    uint64_t* flags;         // encoder state, cleared here: look-back words,
-    uint32_t* lflags;        // window words,
-    uint32_t* ticket;        // work counter
     uint32_t block_elems;
-    uint32_t chunk_elems;
 };
 
-struct ResetArgs {
-    uint64_t* flags;
-    uint32_t* lflags;
-    uint32_t* ticket;
-    uint32_t nchunks;
-    uint32_t nseg;
-};
-
-struct EmptyArgs {
+struct WindowArgs {
     const SegDesc* segs;
-    uint8_t* out;
-    uint64_t* stream_bytes;
+    const Partial* partials;
     SegStat* stats;
+    uint8_t* out;
+    uint64_t* stream_bytes;  // written here for empty segments
+    unsigned long long* cacc;  // per-chunk escape accumulators, cleared here
+    uint32_t* sums;          // coarse escape counts, cleared here
     uint32_t chunk_elems;
-    uint32_t forced_L;
+    uint32_t forced_L;       // 0: window from the moments
 };
 
 struct EncodeArgs {
     const SegDesc* segs;
-    const ItemDesc* chunks;
+    const ItemDesc* pairs;  // per wave: (segment, pair index); segment ~0 pads the grid
     const uint16_t* in;
     uint8_t* out;
-    uint64_t* stream_bytes;
-    const Partial* partials;
-    SegStat* stats;
-    uint32_t* lflags;   // per segment: 0x100 | L once the window is known
-    uint64_t* flags;
-    uint32_t* ticket;
+    const SegStat* stats;   // the window of each segment
+    uint8_t* staging;       // 2048 bytes per group (+16): the group's escape exponents
+    uint32_t* gcnt;         // per group: its escape count
+    unsigned long long* cacc;  // per chunk: (groups done << 32) | escapes, atomic adds
+    uint32_t* sums;         // per 256 and per 65,536 chunks: escape counts, atomic adds
     uint32_t chunk_elems;
-    uint32_t forced_L;  // 0: window from the moments
+};
+
+struct PlaceArgs {
+    const SegDesc* segs;
+    const ItemDesc* chunks;
+    uint8_t* out;
+    uint64_t* stream_bytes;
+    const uint8_t* staging;
+    const uint32_t* gcnt;
+    const unsigned long long* cacc;
+    const uint32_t* sums;
+    uint32_t chunk_elems;
 };
 
 struct DecodeArgs {
@@ -63,10 +64,10 @@ struct DecodeArgs {
 
 template <int NWV, int BPW>
 __global__ void zc_sigma_partials(SigmaArgs a);
-__global__ void zc_reset_flags(ResetArgs a);
-__global__ void zc_empty_headers(EmptyArgs a);
-template <int GPW>
+__global__ void zc_window(WindowArgs a);
 __global__ void zc_encode(EncodeArgs a);
+template <int GPW>
+__global__ void zc_place_escapes(PlaceArgs a);
 template <bool REDUCE>
 __global__ void zc_decode(DecodeArgs a);
 

@@ -19,12 +19,48 @@ __device__ __forceinline__ double tree8(double (&v)[8]) {
     return v[0];
 }
 
-// After distance d every lane holds the sum of its aligned 2d-lane block
-// (fp64 addition is commutative, so both lanes of a pair compute one value).
-__device__ __forceinline__ double wave_tree(double v) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) v = v + __shfl_xor(v, d, 64);
+__device__ __forceinline__ double make_f64(uint32_t lo, uint32_t hi) {
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    return make_f64(dpp<CTRL>((uint32_t)u), dpp<CTRL>((uint32_t)(u >> 32)));
+}
+
+__device__ __forceinline__ double swizzle_x16_f64(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    return make_f64(swizzle_x16((uint32_t)u), swizzle_x16((uint32_t)(u >> 32)));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    return make_f64(readlane((uint32_t)u, l), readlane((uint32_t)(u >> 32), l));
+}
+
+// Pairwise tree over the lanes of a 16-lane row: afterwards every lane of
+// the row holds the row's sum.  Each step adds the partner block's sum; once
+// a block is uniform, the half-row and row mirrors reach the partner block
+// (fp64 addition is commutative, so both blocks of a pair compute one value).
+__device__ __forceinline__ double row_tree(double v) {
+    v = v + dpp_f64<kDppQuadX1>(v);
+    v = v + dpp_f64<kDppQuadX2>(v);
+    v = v + dpp_f64<kDppHalfMirror>(v);
+    v = v + dpp_f64<kDppMirror>(v);
     return v;
+}
+
+// Pairwise tree over lanes 0..31 (valid in every lane of that half).
+__device__ __forceinline__ double half_tree(double v) {
+    v = row_tree(v);
+    return v + swizzle_x16_f64(v);
+}
+
+// Pairwise tree over the 64 lanes, as a wave-uniform value.
+__device__ __forceinline__ double wave_tree(double v) {
+    v = half_tree(v);
+    return readlane_f64(v, 0) + readlane_f64(v, 32);
 }
 
 // L = 127 + max{k : var >= C0 * 4^k}, clamped to 1..248; var = 0 gives 1.
@@ -45,15 +81,15 @@ __device__ __forceinline__ uint32_t window_from_variance(double var) {
 struct MomentScratch {  // LDS for one workgroup's reduction
     double v1[16], v2[16];
     unsigned long long n[16];
-    double r1[32], r2[32];
+    double r1[64], r2[64];
 };
 
 // Pairwise sums over B leaf partials (padded with +0.0 to P = 2^ceil(log2 B)),
 // by the whole workgroup of `nthreads` (a power of two, 64..1024) threads.
 // A round covers an aligned run of T*m leaves: thread t sums m <= 4 of them
 // pairwise (a shorter run padded with +0.0), a wave butterfly and a tree over
-// the waves join the threads.  Rounds (at most 32, for segments of more than
-// 4*nthreads leaves) are joined by a last pairwise tree.  The
+// the waves join the threads.  Rounds (at most 64: 2^32 values are 2^18
+// leaves, and nthreads >= 1024 here) are joined by a last pairwise tree.  The
 // result is valid in thread 0.  Contains __syncthreads: call from uniform
 // control flow only.
 __device__ __forceinline__ void reduce_partials(const Partial* pp, uint32_t B, uint32_t nthreads,
@@ -76,7 +112,7 @@ __device__ __forceinline__ void reduce_partials(const Partial* pp, uint32_t B, u
     uint64_t nn = 0;
     for (uint32_t r = 0; r < rounds; ++r) {
         double r1 = 0.0, r2 = 0.0;
-        uint64_t rn = 0;
+        uint32_t rn = 0;  // at most 4 * 16384 values per thread and round
         if (tid < T) {
             double v1[4], v2[4];
 #pragma unroll
@@ -92,8 +128,7 @@ __device__ __forceinline__ void reduce_partials(const Partial* pp, uint32_t B, u
         }
         r1 = wave_tree(r1);
         r2 = wave_tree(r2);
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) rn += __shfl_xor(rn, d, 64);
+        rn = wave_sum(rn);
         if (lane == 0) {
             sh.v1[wave] = r1;
             sh.v2[wave] = r2;
@@ -102,11 +137,8 @@ __device__ __forceinline__ void reduce_partials(const Partial* pp, uint32_t B, u
         __syncthreads();
         if (wave == 0) {  // lanes 0..15 join the waves' sums: a 16-leaf butterfly
             double t1 = lane < nw ? sh.v1[lane] : 0.0, t2 = lane < nw ? sh.v2[lane] : 0.0;
-#pragma unroll
-            for (int d = 1; d < 16; d <<= 1) {
-                t1 = t1 + __shfl_xor(t1, d, 64);
-                t2 = t2 + __shfl_xor(t2, d, 64);
-            }
+            t1 = row_tree(t1);
+            t2 = row_tree(t2);
             if (lane == 0) {
                 sh.r1[r] = t1;
                 sh.r2[r] = t2;
@@ -115,13 +147,10 @@ __device__ __forceinline__ void reduce_partials(const Partial* pp, uint32_t B, u
         }
         __syncthreads();
     }
-    if (wave == 0) {  // lanes 0..31 join the rounds: a 32-leaf butterfly
+    if (wave == 0) {  // the wave joins the rounds: a 64-leaf tree
         double t1 = lane < rounds ? sh.r1[lane] : 0.0, t2 = lane < rounds ? sh.r2[lane] : 0.0;
-#pragma unroll
-        for (int d = 1; d < 32; d <<= 1) {
-            t1 = t1 + __shfl_xor(t1, d, 64);
-            t2 = t2 + __shfl_xor(t2, d, 64);
-        }
+        t1 = wave_tree(t1);
+        t2 = wave_tree(t2);
         if (lane == 0) {
             s1 = t1;
             s2 = t2;

@@ -84,10 +84,7 @@ __device__ __forceinline__ void load32(const uint16_t* __restrict__ x, uint64_t 
 }  // namespace
 
 // One workgroup per moment block: NWV waves own BPW consecutive 2048-value
-// blocks each (lane l: values 32l .. 32l+31 of a block).  It also clears the
-// encoder's state for this call: the block that opens a chunk clears that
-// chunk's look-back word, the first block of a segment its window word, and
-// block 0 the work counter.
+// blocks each (lane l: values 32l .. 32l+31 of a block).
 template <int NWV, int BPW>
 __global__ __launch_bounds__(256) void zc_sigma_partials(SigmaArgs a) {
     const uint32_t blk = blockIdx.x;
@@ -98,12 +95,6 @@ __global__ __launch_bounds__(256) void zc_sigma_partials(SigmaArgs a) {
     __shared__ double s_s1[NWV], s_s2[NWV];
     __shared__ uint32_t s_n[NWV];
 
-    if (threadIdx.x == 0) {
-        const uint64_t first = (uint64_t)bd.local * a.block_elems;
-        if (first % a.chunk_elems == 0) a.flags[sd.chunk_base + first / a.chunk_elems] = 0;
-        if (bd.local == 0) a.lflags[bd.seg] = 0;
-        if (blk == 0) *a.ticket = 0;
-    }
     if (wave < NWV) {
         double b1[BPW], b2[BPW];
         uint32_t cnt = 0;
@@ -132,8 +123,7 @@ __global__ __launch_bounds__(256) void zc_sigma_partials(SigmaArgs a) {
                 b1[i] = b1[i] + b1[i + s];
                 b2[i] = b2[i] + b2[i + s];
             }
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) cnt += __shfl_xor(cnt, d, 64);
+        cnt = wave_sum(cnt);
         if (lane == 0) {
             s_s1[wave] = b1[0];
             s_s2[wave] = b2[0];
@@ -166,29 +156,42 @@ __global__ __launch_bounds__(256) void zc_sigma_partials(SigmaArgs a) {
     }
 }
 
-// Clears the encoder's state when the moment pass is skipped (fixed window).
-__global__ __launch_bounds__(256) void zc_reset_flags(ResetArgs a) {
-    const uint32_t i0 = blockIdx.x * 256 + threadIdx.x, step = gridDim.x * 256;
-    for (uint32_t i = i0; i < a.nchunks; i += step) a.flags[i] = 0;
-    for (uint32_t i = i0; i < a.nseg; i += step) a.lflags[i] = 0;
-    if (i0 == 0) *a.ticket = 0;
-}
-
-// Streams of empty segments: no chunk exists to write them.
-__global__ __launch_bounds__(64) void zc_empty_headers(EmptyArgs a) {
-    const SegDesc sd = a.segs[blockIdx.x];
-    if (sd.k != 0 || threadIdx.x != 0) return;
+// One workgroup of 1024 threads per segment, after the moment pass: joins the
+// segment's moment partials (the tree's top levels) into the variance and
+// the window, and writes the statistics, the header fields known before
+// encoding and the zero bytes before the code region.  It also clears the
+// segment's escape accumulators (per chunk, per 256 and 65,536 chunks).  A segment without values
+// gets its whole stream here (no chunk exists to write it).
+__global__ __launch_bounds__(1024) void zc_window(WindowArgs a) {
+    __shared__ MomentScratch s_mom;
+    const uint32_t seg = blockIdx.x;
+    const SegDesc sd = a.segs[seg];
     uint8_t* st = a.out + sd.out_off;
-    const uint32_t L = a.forced_L ? a.forced_L : 1u;  // no finite values: var = 0
-    write_static_header(st, sd, a.chunk_elems, L);
-    *reinterpret_cast<uint32_t*>(st + kHeaderBytes) = 0;  // chunk table entry 0 = E
-    *reinterpret_cast<uint64_t*>(st + 24) = 0;
-    *reinterpret_cast<uint64_t*>(st + 32) = sd.esc_off;
-    for (uint64_t i = kHeaderBytes + 4; i < sd.code_off; ++i) st[i] = 0;
-    a.stream_bytes[blockIdx.x] = sd.esc_off;
-    SegStat z{};
-    z.L = L;
-    a.stats[blockIdx.x] = z;
+    double s1 = 0.0, s2 = 0.0;
+    uint64_t n = 0;
+    if (!a.forced_L && sd.nsb)
+        reduce_partials(a.partials + sd.sb_base, sd.nsb, blockDim.x, s_mom, s1, s2, n);
+    if (threadIdx.x == 0) {
+        SegStat ss{};
+        ss.s1 = s1;
+        ss.s2 = s2;
+        ss.n = n;
+        ss.var = a.forced_L ? 0.0 : variance(s1, s2, n);
+        ss.L = a.forced_L ? a.forced_L : window_from_variance(ss.var);
+        a.stats[seg] = ss;
+        write_static_header(st, sd, a.chunk_elems, ss.L);
+        if (sd.k == 0) {  // empty: chunk table entry 0 = E = 0
+            *reinterpret_cast<uint32_t*>(st + kHeaderBytes) = 0;
+            *reinterpret_cast<uint64_t*>(st + 24) = 0;
+            *reinterpret_cast<uint64_t*>(st + 32) = sd.esc_off;
+            a.stream_bytes[seg] = sd.esc_off;
+        }
+    }
+    for (uint64_t i = sd.gtab_off + 2ull * sd.g + threadIdx.x; i < sd.code_off; i += blockDim.x)
+        st[i] = 0;
+    const uint32_t nsum = (uint32_t)((sd.k + 255) / 256 + (sd.k + 65535) / 65536);
+    for (uint32_t i = threadIdx.x; i < nsum; i += blockDim.x) a.sums[sd.c1_base + i] = 0;
+    for (uint32_t i = threadIdx.x; i < sd.k; i += blockDim.x) a.cacc[sd.chunk_base + i] = 0;
 }
 
 template __global__ void zc_sigma_partials<1, 1>(SigmaArgs);
