@@ -48,22 +48,45 @@ __device__ __forceinline__ uint32_t check_header(const uint8_t* st, uint64_t cap
     return bad;
 }
 
-__device__ __forceinline__ void decode_group(const uint32_t (&P)[3], const u32x2 (&sm)[4],
-                                             uint32_t L7, u32x4 (&o)[4]) {
+// Nibble words of tile k: nibble n of Z[k] = code of the value at plane bit
+// 4n + k.
+__device__ __forceinline__ void code_nibbles(const uint32_t (&P)[3], uint32_t (&Z)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        Z[k] = ((P[0] >> k) & 0x11111111u) | (((P[1] >> k) & 0x11111111u) << 1) |
+               (((P[2] >> k) & 0x11111111u) << 2);
+}
+
+// Exponent bytes in plane-bit order: byte k of Q[n] = L + code of the value
+// at plane bit 4n + k (byte j of Z[k] holds nibbles 2j and 2j+1; codes <= 7
+// and L <= 248, so the bytewise add never carries).
+__device__ __forceinline__ void exponent_rows(const uint32_t (&Z)[4], uint32_t L, uint32_t (&Q)[8]) {
+    const uint32_t LL = L * 0x01010101u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t T = perm(Z[1], Z[0], 0x0C0C0400u | (j << 8) | j) |
+                           perm(Z[3], Z[2], 0x04000C0Cu | (j << 24) | (j << 16));
+        Q[2 * j] = (T & 0x0F0F0F0Fu) + LL;
+        Q[2 * j + 1] = ((T >> 4) & 0x0F0F0F0Fu) + LL;
+    }
+}
+
+// BF16 words from exponent bytes (plane-bit order) and sign+mantissa bytes.
+// Word m of tile k holds the values at plane bits 4m + k (low half) and
+// 4(m+4) + k (high half).
+__device__ __forceinline__ void assemble(const uint32_t (&Q)[8], const u32x2 (&sm)[4], u32x4 (&o)[4]) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        // nibble n of Z = code of the value at plane bit 4n + k
-        const uint32_t Z = ((P[0] >> k) & 0x11111111u) | (((P[1] >> k) & 0x11111111u) << 1) |
-                           (((P[2] >> k) & 0x11111111u) << 2);
-        // code of values 2m / 2m+1 (nibbles m / m+4) moved to bits 7 / 23
-        const uint32_t c0 = (Z << 7) & 0x03800380u, c1 = (Z << 3) & 0x03800380u;
-        const uint32_t c2 = (Z >> 1) & 0x03800380u, c3 = (Z >> 5) & 0x03800380u;
-        // sign+mantissa bytes of values 2m, 2m, 2m+1, 2m+1 -> bits 0-6 and 15 of each half
         const uint32_t lo = sm[k].x, hi = sm[k].y;
-        o[k][0] = bitsel(0x7F807F80u, c0 + L7, perm(hi, lo, 0x01010000u));
-        o[k][1] = bitsel(0x7F807F80u, c1 + L7, perm(hi, lo, 0x03030202u));
-        o[k][2] = bitsel(0x7F807F80u, c2 + L7, perm(hi, lo, 0x05050404u));
-        o[k][3] = bitsel(0x7F807F80u, c3 + L7, perm(hi, lo, 0x07070606u));
+        // exponent of the low value to bits 7-14, of the high one to bits 23-30
+        const uint32_t sel = 0x0C000C00u | ((4u + k) << 16) | (uint32_t)k;
+        const uint32_t e0 = perm(Q[4], Q[0], sel) << 7, e1 = perm(Q[5], Q[1], sel) << 7;
+        const uint32_t e2 = perm(Q[6], Q[2], sel) << 7, e3 = perm(Q[7], Q[3], sel) << 7;
+        // sign+mantissa bytes of values 2m, 2m, 2m+1, 2m+1 -> bits 0-6 and 15 of each half
+        o[k][0] = bitsel(0x7F807F80u, e0, perm(hi, lo, 0x01010000u));
+        o[k][1] = bitsel(0x7F807F80u, e1, perm(hi, lo, 0x03030202u));
+        o[k][2] = bitsel(0x7F807F80u, e2, perm(hi, lo, 0x05050404u));
+        o[k][3] = bitsel(0x7F807F80u, e3, perm(hi, lo, 0x07070606u));
     }
 }
 
@@ -82,10 +105,11 @@ __device__ __forceinline__ uint64_t sm_pad_mask(uint32_t lane, uint32_t valid, i
     return ~0ull << (8 * left);
 }
 
+template <bool TAIL>
 __device__ __forceinline__ void store_values(uint16_t* __restrict__ out, uint64_t n, uint64_t g,
                                              uint32_t lane, const u32x4 (&o)[4]) {
     const uint64_t base = (uint64_t)kGroup * g + 8u * lane;
-    if ((uint64_t)kGroup * (g + 1) <= n) {
+    if (!TAIL) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(out + base + 512u * k) = o[k];
         return;
@@ -165,45 +189,34 @@ __device__ __forceinline__ uint32_t fetch_escapes(const uint8_t* st, uint64_t ca
     return (uint32_t)(at - a0);
 }
 
-// Rebuild the group's values into o, with escaped exponents patched.
+// Rebuild the group's values into o.  The lane's exponent bytes go to its
+// 32-byte LDS row in plane-bit order; each escape overwrites its byte there
+// with the next escape byte (the lane's escapes are contiguous from `first`).
 __device__ __forceinline__ void rebuild(const GroupData& d, uint32_t M, uint32_t first,
-                                        const uint8_t* esc, u32x4* stage4, uint32_t lane,
-                                        u32x4 (&o)[4]) {
-    decode_group(d.P, d.sm, (d.L << 7) | (d.L << 23), o);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) stage4[64 * k + lane] = o[k];
-    __builtin_amdgcn_wave_barrier();
-    uint16_t* stage = reinterpret_cast<uint16_t*>(stage4);
-    uint32_t m = M, i = first;
-    while (m) {
-        const uint32_t p = __builtin_ctz(m);
-        m &= m - 1;
-        const uint32_t r = group_index(lane, p);
-        stage[r] = (uint16_t)((stage[r] & 0x807Fu) | ((uint32_t)esc[i++] << 7));
-    }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = stage4[64 * k + lane];
+                                        const uint8_t* esc, u32x4* row, u32x4 (&o)[4]) {
+    __builtin_amdgcn_wave_barrier();  // the escape bytes are in LDS
+    uint32_t Z[4], Q[8];
+    code_nibbles(d.P, Z);
+    exponent_rows(Z, d.L, Q);
+    row[0] = u32x4{Q[0], Q[1], Q[2], Q[3]};
+    row[1] = u32x4{Q[4], Q[5], Q[6], Q[7]};
+    uint8_t* rb = reinterpret_cast<uint8_t*>(row);
+    for (uint32_t m = M, i = first; m; m &= m - 1, ++i) rb[__builtin_ctz(m)] = esc[i];
+    const u32x4 r0 = row[0], r1 = row[1];
+    const uint32_t Qe[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+    assemble(Qe, d.sm, o);
     __builtin_amdgcn_wave_barrier();
 }
 
 }  // namespace
 
-template <bool REDUCE>
-__global__ __launch_bounds__(256) void zc_decode(DecodeArgs a) {
-    __shared__ u32x4 s_stage[4][256];   // decoded group per wave
-    __shared__ uint32_t s_esc[4][520];  // the group's escape bytes per wave (whole dwords)
-
-    const uint32_t lane = lane_id(), wave = wave_id();
-    const uint32_t gg = blockIdx.x * 4 + wave;
-    if (gg >= a.ngroups) return;
-    const ItemDesc gd = a.groups[gg];
-    const SegDesc sd = a.segs[gd.seg];
-    const uint32_t g = gd.local;
-    const bool tail = (uint64_t)kGroup * (g + 1) > sd.n;
-    const uint32_t valid = (uint32_t)(sd.n - (uint64_t)kGroup * g);  // meaningful when tail
-    const uint8_t* escb = reinterpret_cast<const uint8_t*>(s_esc[wave]);
-
+// One group of every stream: decode (REDUCE: and sum in shard order).  TAIL
+// is the segment's last, partial group: padding checks and partial stores.
+template <bool REDUCE, bool TAIL>
+__device__ __forceinline__ uint32_t decode_group_all(const DecodeArgs& a, const SegDesc& sd, uint32_t g,
+                                                     uint32_t lane, uint32_t* esc_lds, u32x4* row) {
+    const uint32_t valid = TAIL ? (uint32_t)(sd.n - (uint64_t)kGroup * g) : kGroup;
+    const uint8_t* escb = reinterpret_cast<const uint8_t*>(esc_lds);
     float acc[REDUCE ? 32 : 1];
     uint32_t bad_all = 0;
 
@@ -224,8 +237,7 @@ __global__ __launch_bounds__(256) void zc_decode(DecodeArgs a) {
     for (uint32_t s = 0; s < a.nstreams; ++s) {
         // escape bytes of this stream, then the next stream's loads
         uint32_t first = 0;
-        if (!cur.bad)
-            first = fetch_escapes(st, cap, sd.esc_off + cur.t0 + cur.rel, cur.span, lane, s_esc[wave]);
+        if (!cur.bad) first = fetch_escapes(st, cap, sd.esc_off + cur.t0 + cur.rel, cur.span, lane, esc_lds);
         GroupData nxt;
         uint64_t ncap = 0;
         const uint8_t* nst = nullptr;
@@ -236,22 +248,21 @@ __global__ __launch_bounds__(256) void zc_decode(DecodeArgs a) {
 
         uint32_t bad = cur.bad;
         if (!bad) {
-            bool padbad = false;
-            if (tail) {
+            if (TAIL) {
                 const uint32_t V = valid_bits(lane, valid);
-                padbad = ((cur.P[0] | cur.P[1] | cur.P[2]) & ~V) != 0;
+                bool padbad = ((cur.P[0] | cur.P[1] | cur.P[2]) & ~V) != 0;
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
                     padbad |= (__builtin_bit_cast(uint64_t, cur.sm[k]) & sm_pad_mask(lane, valid, k)) != 0;
+                if (__ballot(padbad)) bad |= kBadPad;
             }
             const uint32_t M = cur.P[0] & cur.P[1] & cur.P[2];
             const uint32_t cnt = __builtin_popcount(M);
             const uint32_t incl = wave_inclusive_scan(cnt);
-            if (__ballot(padbad)) bad |= kBadPad;
             if (readlane(incl, 63) != cur.span) bad |= kBadCount;
             if (!bad) {
                 u32x4 o[4];
-                rebuild(cur, M, first + incl - cnt, escb, s_stage[wave], lane, o);
+                rebuild(cur, M, first + incl - cnt, escb, row, o);
                 if (REDUCE) {
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
@@ -265,7 +276,7 @@ __global__ __launch_bounds__(256) void zc_decode(DecodeArgs a) {
                             a1 = s == 0 ? hi : a1 + hi;
                         }
                 } else {
-                    store_values(a.out + sd.in_off, sd.n, g, lane, o);
+                    store_values<TAIL>(a.out + sd.in_off, sd.n, g, lane, o);
                 }
             }
         }
@@ -285,10 +296,28 @@ __global__ __launch_bounds__(256) void zc_decode(DecodeArgs a) {
             for (int mm = 0; mm < 4; ++mm)
                 o[k][mm] = to_bf16(acc[REDUCE ? 8 * k + 2 * mm : 0]) |
                            (to_bf16(acc[REDUCE ? 8 * k + 2 * mm + 1 : 0]) << 16);
-        store_values(a.out + sd.in_off, sd.n, g, lane, o);
+        store_values<TAIL>(a.out + sd.in_off, sd.n, g, lane, o);
     }
-    if (lane == 0) a.status[gg] = bad_all;
+    return bad_all;
 }
+
+template <bool REDUCE>
+__global__ __launch_bounds__(256) void zc_decode(DecodeArgs a) {
+    __shared__ u32x4 s_row[4][64][2];   // per wave and lane: 32 exponent bytes
+    __shared__ uint32_t s_esc[4][520];  // the group's escape bytes per wave (whole dwords)
+
+    const uint32_t lane = lane_id(), wave = wave_id();
+    const uint32_t gg = blockIdx.x * 4 + wave;
+    if (gg >= a.ngroups) return;
+    const ItemDesc gd = a.groups[gg];
+    const SegDesc sd = a.segs[gd.seg];
+    const uint32_t g = gd.local;
+    const uint32_t bad = (uint64_t)kGroup * (g + 1) > sd.n
+                             ? decode_group_all<REDUCE, true>(a, sd, g, lane, s_esc[wave], s_row[wave][lane])
+                             : decode_group_all<REDUCE, false>(a, sd, g, lane, s_esc[wave], s_row[wave][lane]);
+    if (lane == 0) a.status[gg] = bad;
+}
+
 
 template __global__ void zc_decode<false>(DecodeArgs);
 template __global__ void zc_decode<true>(DecodeArgs);
