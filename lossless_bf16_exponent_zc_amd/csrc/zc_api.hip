@@ -9,7 +9,7 @@
 //                      chunks (one wave per two groups)
 //   zc_place_escapes   group table, chunk offsets, escapes to their place,
 //                      chunk table, sizes
-// Decompress: zc_decode.  Decompress-reduce: zc_decode<REDUCE>.
+// Decompress: zc_decode.  Decompress-reduce: zc_decode_reduce.
 // Every call enqueues on the caller's stream and returns; nothing here reads
 // device memory except the two zc_read_* helpers, which synchronise.
 #include <stdlib.h>
@@ -24,7 +24,7 @@
 using namespace zc;
 
 struct zc_plan {
-    uint32_t nseg = 0, chunk = 0, block = 0, nsums = 0;
+    uint32_t nseg = 0, chunk = 0, block = 0;
     std::vector<SegDesc> segs;
     std::vector<ItemDesc> blocks, chunks, groups, pairs;  // pairs: encoder waves
     uint64_t input_elems = 0, out_bytes = 0;
@@ -85,9 +85,8 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
 
     Partial* partials = ws_ptr<Partial>(p, d_ws, p->ws.partials);
     SegStat* stats = ws_ptr<SegStat>(p, d_ws, p->ws.stats);
-    uint32_t* sums = ws_ptr<uint32_t>(p, d_ws, p->ws.sums);
     uint32_t* gcnt = ws_ptr<uint32_t>(p, d_ws, p->ws.gcnt);
-    unsigned long long* cacc = ws_ptr<unsigned long long>(p, d_ws, p->ws.cacc);
+    uint32_t* ctot = ws_ptr<uint32_t>(p, d_ws, p->ws.ctot);
     uint8_t* staging = ws_ptr<uint8_t>(p, d_ws, p->ws.staging);
     const uint16_t* in = static_cast<const uint16_t*>(d_in);
     uint8_t* out = static_cast<uint8_t*>(d_out);
@@ -96,11 +95,11 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
         SigmaArgs sa{p->d_segs, p->d_blocks, in, partials, p->block};
         launch_sigma(p, sa, stream);
     }
-    WindowArgs wa{p->d_segs, partials, stats, out, d_stream_bytes, cacc, sums, p->chunk, forced_L};
+    WindowArgs wa{p->d_segs, partials, stats, out, d_stream_bytes, ctot, p->chunk, forced_L};
     hipLaunchKernelGGL(zc_window, dim3(p->nseg), dim3(1024), 0, stream, wa);
     if (nchunks(p)) {
-        EncodeArgs ea{p->d_segs, p->d_pairs, in, out, stats, staging, gcnt, cacc, sums, p->chunk};
-        PlaceArgs pa{p->d_segs, p->d_chunks, out, d_stream_bytes, staging, gcnt, cacc, sums, p->chunk};
+        EncodeArgs ea{p->d_segs, p->d_pairs, in, out, stats, staging, gcnt, ctot, p->chunk};
+        PlaceArgs pa{p->d_segs, p->d_chunks, out, d_stream_bytes, staging, gcnt, ctot, p->chunk};
         const uint32_t gpc = p->chunk / kGroup;
         const dim3 grid(nchunks(p));
         hipLaunchKernelGGL(zc_encode, dim3((uint32_t)(p->pairs.size() / 4)), dim3(256), 0, stream, ea);
@@ -169,15 +168,13 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
         d.sb_base = (uint32_t)p->blocks.size();
         d.group_base = (uint32_t)p->groups.size();
         d.chunk_base = (uint32_t)p->chunks.size();
-        d.c1_base = p->nsums;
-        d.c2_base = d.c1_base + (uint32_t)cdiv(d.k, 256);
-        p->nsums = d.c2_base + (uint32_t)cdiv(d.k, 65536);
         in_off += (n + 7) & ~uint64_t(7);
         out_off += a256(d.max_bytes);
         for (uint32_t b = 0; b < d.nsb; ++b) p->blocks.push_back(ItemDesc{s, b});
         for (uint32_t k = 0; k < d.k; ++k) p->chunks.push_back(ItemDesc{s, k});
         for (uint32_t g = 0; g < d.g; ++g) p->groups.push_back(ItemDesc{s, g});
         for (uint32_t q = 0; q < (d.g + 1) / 2; ++q) p->pairs.push_back(ItemDesc{s, q});
+        while (p->pairs.size() % 4) p->pairs.push_back(ItemDesc{0xFFFFFFFFu, 0});  // whole workgroups
         if (p->groups.size() >= (1ull << 31)) {
             delete p;
             return ZC_ERR_UNSUPPORTED;
@@ -186,7 +183,6 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
     }
     p->input_elems = in_off;
     p->out_bytes = out_off;
-    while (p->pairs.size() % 4) p->pairs.push_back(ItemDesc{0xFFFFFFFFu, 0});  // whole workgroups
     const uint64_t G = p->groups.size(), B = p->blocks.size(), K = p->chunks.size();
     const uint64_t W = p->pairs.size();
     uint64_t o = 0;
@@ -194,8 +190,7 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
     p->ws.partials = o; o += a256(sizeof(Partial) * B);
     p->ws.stats = o;    o += a256(sizeof(SegStat) * num_segments);
     p->ws.gcnt = o;     o += a256(4 * G);
-    p->ws.cacc = o;     o += a256(8 * K);
-    p->ws.sums = o;     o += a256(4ull * p->nsums);
+    p->ws.ctot = o;     o += a256(4 * K);
     p->ws.staging = o;  o += a256((uint64_t)kGroup * G + 16);
     p->ws.total = o;
 
@@ -275,7 +270,7 @@ zc_status zc_decompress(const zc_plan* p, const void* d_in, uint64_t in_capacity
     a.ngroups = ngroups(p);
     a.out = static_cast<uint16_t*>(d_out);
     a.status = ws_ptr<uint32_t>(p, d_ws, p->ws.status);
-    hipLaunchKernelGGL((zc_decode<false>), dim3(group_grid(p)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(zc_decode, dim3(group_grid(p)), dim3(256), 0, stream, a);
     return launch_status();
 }
 
@@ -299,7 +294,7 @@ zc_status zc_decompress_reduce(const zc_plan* p, const void* const* d_streams, u
     a.ngroups = ngroups(p);
     a.out = static_cast<uint16_t*>(d_out);
     a.status = ws_ptr<uint32_t>(p, d_ws, p->ws.status);
-    hipLaunchKernelGGL((zc_decode<true>), dim3(group_grid(p)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(zc_decode_reduce, dim3(group_grid(p)), dim3(256), 0, stream, a);
     return launch_status();
 }
 

@@ -302,7 +302,7 @@ __device__ __forceinline__ uint32_t decode_group_all(const DecodeArgs& a, const 
 }
 
 template <bool REDUCE>
-__global__ __launch_bounds__(256) void zc_decode(DecodeArgs a) {
+__device__ __forceinline__ void decode_kernel(const DecodeArgs& a) {
     __shared__ u32x4 s_row[4][64][2];   // per wave and lane: 32 exponent bytes
     __shared__ uint32_t s_esc[4][520];  // the group's escape bytes per wave (whole dwords)
 
@@ -318,8 +318,15 @@ __global__ __launch_bounds__(256) void zc_decode(DecodeArgs a) {
     if (lane == 0) a.status[gg] = bad;
 }
 
+// Eight waves per SIMD for the plain decoder (it fits in 64 VGPRs).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void zc_decode(DecodeArgs a) {
+    decode_kernel<false>(a);
+}
 
-template __global__ void zc_decode<false>(DecodeArgs);
-template __global__ void zc_decode<true>(DecodeArgs);
+// Four waves per SIMD for the fused reduce (32 accumulators per lane).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void zc_decode_reduce(
+    DecodeArgs a) {
+    decode_kernel<true>(a);
+}
 
 }  // namespace zc

@@ -13,9 +13,10 @@
 // time; nibble packing and a 4-way bit interleave turn the lane's 32 codes
 // into its three plane words; plane words and sign+mantissa bytes go out at
 // once (static offsets).  Escapes (code 7 = all three plane bits set) are
-// counted and ranked across the wave with ballots; the lanes' escape
-// exponents are packed in code order into the wave's LDS area and go out in
-// aligned dwords to the group's staging slot.  The chunk's count is summed
+// counted and ranked across the wave with ballots; each lane puts its 32
+// exponent bytes in an LDS row (plane-bit order) and copies its escapes'
+// bytes from there, in code order, into the wave's packed LDS area, which
+// goes out in aligned dwords to the group's staging slot.  The chunk's count is summed
 // with one LDS atomic per wave; the last wave stores it and adds it to the
 // coarse counts (per 256 and per 65,536 chunks).
 //
@@ -68,18 +69,6 @@ __device__ __forceinline__ void exponent_bytes(const u32x4 (&w)[4], uint32_t (&Q
     }
 }
 
-// Byte p of the lane's 32 exponent bytes (plane-bit order).  Selects between
-// values, not array elements: a conditional over array lvalues would select
-// addresses and keep the array in scratch memory.
-__device__ __forceinline__ uint32_t exponent_byte(const uint32_t (&Q)[8], uint32_t p) {
-    const uint32_t q0 = Q[0], q1 = Q[1], q2 = Q[2], q3 = Q[3];
-    const uint32_t q4 = Q[4], q5 = Q[5], q6 = Q[6], q7 = Q[7];
-    const uint32_t d = p >> 2;
-    const uint32_t lo = (d & 2) ? ((d & 1) ? q3 : q2) : ((d & 1) ? q1 : q0);
-    const uint32_t hi = (d & 2) ? ((d & 1) ? q7 : q6) : ((d & 1) ? q5 : q4);
-    return ((d & 4) ? hi : lo) >> (8 * (p & 3));
-}
-
 // One wave stores a run of n bytes (a group's escape exponents) from `src`
 // (the group's 2048-byte staging slot) to `dst`.  The caller has loaded, for
 // output dwords k = lane + 64 r (r < R), lo[r] = source dword k and hi[r] =
@@ -117,10 +106,14 @@ __device__ __forceinline__ void store_run(uint8_t* dst, const uint32_t* src, uin
 }  // namespace
 
 // Four waves per workgroup, each with two consecutive groups of one segment
-// (item list: one entry per wave-pair of groups), no workgroup barrier.
-// LDS: 2048 + 16 bytes per wave (every value of a group may escape).
+// (item list: one entry per wave; segment ~0 pads the grid), no barrier.
+// Each wave adds its escape count to its chunk's count with a non-returning
+// atomic (a chunk's count gets at most 16 such adds).
+// LDS per wave: 2048 + 16 bytes of packed escapes (every value of a group may
+// escape) and a 32-byte exponent row per lane.
 __global__ __launch_bounds__(256) void zc_encode(EncodeArgs a) {
-    __shared__ uint32_t s_e[4][(kGroup + 16) / 4];
+    __shared__ uint32_t s_e[4][(kGroup + 16) / 4];  // per wave: the group's packed escapes
+    __shared__ u32x4 s_row[4][64][2];                 // per wave and lane: 32 exponent bytes
     const uint32_t lane = lane_id(), wave = wave_id();
     const ItemDesc it = a.pairs[blockIdx.x * 4 + wave];  // (segment, first group / 2)
     if (it.seg == 0xFFFFFFFFu) return;                   // grid padding
@@ -144,6 +137,7 @@ __global__ __launch_bounds__(256) void zc_encode(EncodeArgs a) {
     const uint32_t L7 = (L << 7) | (L << 23);
 
     uint8_t* ew = reinterpret_cast<uint8_t*>(s_e[wave]);
+    uint32_t ctot = 0;  // escapes of the current chunk (a wave's two groups share one unless gpc = 1)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const uint64_t g = g0 + q;
@@ -166,30 +160,26 @@ __global__ __launch_bounds__(256) void zc_encode(EncodeArgs a) {
         uint32_t tot;
         const uint32_t excl = wave_prefix_small(__builtin_popcount(M), tot);
         const uint64_t gg = sd.group_base + g;
-        const uint32_t chunk = sd.chunk_base + (uint32_t)(g / gpc);
-        uint64_t old = 0;
-        if (lane == 0) {
-            a.gcnt[gg] = tot;
-            old = atomicAdd(a.cacc + chunk, (1ull << 32) | tot);  // (groups done, escapes)
-        }
+        if (lane == 0) a.gcnt[gg] = tot;
         uint32_t Q[8];
         exponent_bytes(w[q], Q);
-        for (uint32_t m = M, i = 0; m; m &= m - 1, ++i)
-            ew[excl + i] = (uint8_t)exponent_byte(Q, __builtin_ctz(m));
+        s_row[wave][lane][0] = u32x4{Q[0], Q[1], Q[2], Q[3]};
+        s_row[wave][lane][1] = u32x4{Q[4], Q[5], Q[6], Q[7]};
+        const uint8_t* rb = reinterpret_cast<const uint8_t*>(s_row[wave][lane]);
+        for (uint32_t m = M, i = 0; m; m &= m - 1, ++i) ew[excl + i] = rb[__builtin_ctz(m)];
+        __builtin_amdgcn_wave_barrier();  // the wave's packed bytes are complete
         uint32_t* slot = reinterpret_cast<uint32_t*>(a.staging + gg * kGroup);
         for (uint32_t k = lane; k < (tot + 3) / 4; k += 64) slot[k] = s_e[wave][k];
-        if (lane == 0) {
-            const uint32_t local = (uint32_t)(g / gpc);
-            const uint32_t ng = (uint32_t)min((uint64_t)gpc, sd.g - (uint64_t)local * gpc);
-            if ((uint32_t)(old >> 32) == ng - 1) {  // this group completed its chunk
-                const uint32_t t = (uint32_t)old + tot;
-                atomicAdd(a.sums + sd.c1_base + (local >> 8), t);
-                atomicAdd(a.sums + sd.c2_base + (local >> 16), t);
-            }
+        __builtin_amdgcn_wave_barrier();  // before the next group reuses the area
+        ctot += tot;
+        if ((g + 1) % gpc == 0 || q == 1 || g + 1 == sd.g) {  // last group of this wave in its chunk
+            if (lane == 0 && ctot)
+                __hip_atomic_fetch_add(a.ctot + sd.chunk_base + (uint32_t)(g / gpc), ctot,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ctot = 0;
         }
     }
 }
-
 
 // One workgroup of up to 4 waves per chunk; wave w owns the chunk's groups
 // w, w + nw, ... (GPW = groups per wave).
@@ -197,6 +187,7 @@ template <int GPW>
 __global__ __launch_bounds__(256) void zc_place_escapes(PlaceArgs a) {
     constexpr int R = 2;  // source dword pairs per lane and group loaded ahead
     __shared__ uint32_t s_gb[32], s_gn[32], s_prefix;  // group offsets in the chunk, counts
+    __shared__ uint32_t s_part[4];                     // per wave: partial sums of earlier chunks
     const uint32_t ci = blockIdx.x, lane = lane_id(), wave = wave_id(), nw = blockDim.x >> 6;
     const ItemDesc cd = a.chunks[ci];
     const SegDesc sd = a.segs[cd.seg];
@@ -219,31 +210,28 @@ __global__ __launch_bounds__(256) void zc_place_escapes(PlaceArgs a) {
             hi[q][r] = j < ng ? s32[lane + 64 * r + 1] : 0u;
         }
     }
+    // escapes of the segment's earlier chunks: a strided sum by all threads
+    const uint32_t l = cd.local;
+    uint32_t v = 0;
+    for (uint32_t j = threadIdx.x; j < l; j += blockDim.x) v += a.ctot[sd.chunk_base + j];
+    v = wave_sum(v);
+    if (lane == 0) s_part[wave] = v;
+    __syncthreads();
     if (wave == 0) {
-        const uint32_t l = cd.local;
-        uint32_t v = 0;
-        if (lane < (l >> 16)) v += a.sums[sd.c2_base + lane];
-#pragma unroll
-        for (uint32_t r = 0; r < 4; ++r) {
-            const uint32_t j = ((l >> 16) << 8) + lane + 64 * r;
-            if (j < (l >> 8)) v += a.sums[sd.c1_base + j];
-        }
-#pragma unroll
-        for (uint32_t r = 0; r < 4; ++r) {
-            const uint32_t j = ((l >> 8) << 8) + lane + 64 * r;
-            if (j < l) v += (uint32_t)a.cacc[sd.chunk_base + j];
-        }
         const uint32_t c = lane < ng ? a.gcnt[sd.group_base + gc0 + lane] : 0u;
         const uint32_t incl = wave_inclusive_scan(c);
         if (lane < ng) {
             reinterpret_cast<uint16_t*>(st + sd.gtab_off)[gc0 + lane] = (uint16_t)(incl - c);
             s_gb[lane] = incl - c;
-            s_gn[lane] = c;
+            s_gn[lane] = min(c, kGroup);
         }
-        const uint32_t prefix = wave_sum(v);
+        uint32_t prefix = 0;
+        for (uint32_t i = 0; i < nw; ++i) prefix += s_part[i];
         if (lane == 0) {
             const uint32_t t = readlane(incl, 63);
-            s_prefix = prefix;
+            // counts that would leave the escape region mean no copy (never
+            // the case when the encoder wrote them)
+            s_prefix = (uint64_t)prefix + t <= sd.n ? prefix : 0xFFFFFFFFu;
             reinterpret_cast<uint32_t*>(st + kHeaderBytes)[l] = prefix;
             if (l + 1 == sd.k) {
                 const uint64_t E = (uint64_t)prefix + t;
@@ -255,6 +243,7 @@ __global__ __launch_bounds__(256) void zc_place_escapes(PlaceArgs a) {
         }
     }
     __syncthreads();
+    if (s_prefix == 0xFFFFFFFFu) return;
     uint8_t* esc = st + sd.esc_off + s_prefix;
 #pragma unroll
     for (int q = 0; q < GPW; ++q) {

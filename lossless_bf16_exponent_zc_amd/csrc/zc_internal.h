@@ -44,8 +44,6 @@ struct SegDesc {
     uint32_t sb_base;    // first moment block of this segment in the plan's list
     uint32_t group_base; // first group of this segment in the plan's list
     uint32_t chunk_base; // first chunk of this segment in the plan's list
-    uint32_t c1_base;    // first escape count per 256 chunks of this segment
-    uint32_t c2_base;    // first escape count per 65,536 chunks of this segment
 };
 
 struct ItemDesc {  // a moment block, chunk or group: its segment and index inside it
@@ -72,8 +70,7 @@ struct WsLayout {
     uint64_t partials;  // Partial per moment block
     uint64_t stats;     // SegStat per segment
     uint64_t gcnt;      // u32 per group: escape count
-    uint64_t cacc;      // u64 per chunk: (groups done << 32) | escapes
-    uint64_t sums;      // u32: escape counts per 256 and per 65,536 chunks
+    uint64_t ctot;      // u32 per chunk: escape count
     uint64_t staging;   // 2048 bytes per group (+16): escape exponents before placement
     uint64_t total;
 };

@@ -19,22 +19,20 @@ struct WindowArgs {
     SegStat* stats;
     uint8_t* out;
     uint64_t* stream_bytes;  // written here for empty segments
-    unsigned long long* cacc;  // per-chunk escape accumulators, cleared here
-    uint32_t* sums;          // coarse escape counts, cleared here
+    uint32_t* ctot;          // per-chunk escape counts, cleared here
     uint32_t chunk_elems;
     uint32_t forced_L;       // 0: window from the moments
 };
 
 struct EncodeArgs {
     const SegDesc* segs;
-    const ItemDesc* pairs;  // per wave: (segment, pair index); segment ~0 pads the grid
+    const ItemDesc* pairs;  // per wave: (segment, pair index); segment ~0 pads a segment's workgroups
     const uint16_t* in;
     uint8_t* out;
     const SegStat* stats;   // the window of each segment
     uint8_t* staging;       // 2048 bytes per group (+16): the group's escape exponents
     uint32_t* gcnt;         // per group: its escape count
-    unsigned long long* cacc;  // per chunk: (groups done << 32) | escapes, atomic adds
-    uint32_t* sums;         // per 256 and per 65,536 chunks: escape counts, atomic adds
+    uint32_t* ctot;         // per chunk: escape count, atomic adds
     uint32_t chunk_elems;
 };
 
@@ -45,8 +43,7 @@ struct PlaceArgs {
     uint64_t* stream_bytes;
     const uint8_t* staging;
     const uint32_t* gcnt;
-    const unsigned long long* cacc;
-    const uint32_t* sums;
+    const uint32_t* ctot;
     uint32_t chunk_elems;
 };
 
@@ -68,7 +65,7 @@ __global__ void zc_window(WindowArgs a);
 __global__ void zc_encode(EncodeArgs a);
 template <int GPW>
 __global__ void zc_place_escapes(PlaceArgs a);
-template <bool REDUCE>
 __global__ void zc_decode(DecodeArgs a);
+__global__ void zc_decode_reduce(DecodeArgs a);
 
 }  // namespace zc

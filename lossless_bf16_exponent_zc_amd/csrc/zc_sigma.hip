@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void zc_sigma_partials(SigmaArgs a) {
 // segment's moment partials (the tree's top levels) into the variance and
 // the window, and writes the statistics, the header fields known before
 // encoding and the zero bytes before the code region.  It also clears the
-// segment's escape accumulators (per chunk, per 256 and 65,536 chunks).  A segment without values
+// segment's per-chunk escape counts.  A segment without values
 // gets its whole stream here (no chunk exists to write it).
 __global__ __launch_bounds__(1024) void zc_window(WindowArgs a) {
     __shared__ MomentScratch s_mom;
@@ -189,9 +189,7 @@ __global__ __launch_bounds__(1024) void zc_window(WindowArgs a) {
     }
     for (uint64_t i = sd.gtab_off + 2ull * sd.g + threadIdx.x; i < sd.code_off; i += blockDim.x)
         st[i] = 0;
-    const uint32_t nsum = (uint32_t)((sd.k + 255) / 256 + (sd.k + 65535) / 65536);
-    for (uint32_t i = threadIdx.x; i < nsum; i += blockDim.x) a.sums[sd.c1_base + i] = 0;
-    for (uint32_t i = threadIdx.x; i < sd.k; i += blockDim.x) a.cacc[sd.chunk_base + i] = 0;
+    for (uint32_t i = threadIdx.x; i < sd.k; i += blockDim.x) a.ctot[sd.chunk_base + i] = 0;
 }
 
 template __global__ void zc_sigma_partials<1, 1>(SigmaArgs);
