@@ -99,18 +99,20 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     hipLaunchKernelGGL(zc_window, dim3(p->nseg), dim3(1024), 0, stream, wa);
     if (nchunks(p)) {
         EncodeArgs ea{p->d_segs, p->d_pairs, in, out, stats, staging, gcnt, ctot, p->chunk};
-        PlaceArgs pa{p->d_segs, p->d_chunks, out, d_stream_bytes, staging, gcnt, ctot, p->chunk};
+        PlaceArgs pa{p->d_segs, p->d_chunks, out, d_stream_bytes, staging, gcnt, ctot, p->chunk,
+                     nchunks(p)};
         const uint32_t gpc = p->chunk / kGroup;
         const dim3 grid(nchunks(p));
         hipLaunchKernelGGL(zc_encode, dim3((uint32_t)(p->pairs.size() / 4)), dim3(256), 0, stream, ea);
         // placement: up to 4 waves, each with gpc / waves groups
         const uint32_t pw = gpc < 4 ? gpc : 4;
         const dim3 pblock(64 * pw);
+        const dim3 pgrid(nchunks(p));  // one chunk per workgroup: latency hides across chunks
         switch (gpc / pw) {
-            case 1: hipLaunchKernelGGL((zc_place_escapes<1>), grid, pblock, 0, stream, pa); break;
-            case 2: hipLaunchKernelGGL((zc_place_escapes<2>), grid, pblock, 0, stream, pa); break;
-            case 4: hipLaunchKernelGGL((zc_place_escapes<4>), grid, pblock, 0, stream, pa); break;
-            default: hipLaunchKernelGGL((zc_place_escapes<8>), grid, pblock, 0, stream, pa); break;
+            case 1: hipLaunchKernelGGL((zc_place_escapes<1>), pgrid, pblock, 0, stream, pa); break;
+            case 2: hipLaunchKernelGGL((zc_place_escapes<2>), pgrid, pblock, 0, stream, pa); break;
+            case 4: hipLaunchKernelGGL((zc_place_escapes<4>), pgrid, pblock, 0, stream, pa); break;
+            default: hipLaunchKernelGGL((zc_place_escapes<8>), pgrid, pblock, 0, stream, pa); break;
         }
     }
     return launch_status();

@@ -70,13 +70,14 @@ __device__ __forceinline__ void exponent_bytes(const u32x4 (&w)[4], uint32_t (&Q
 }
 
 // One wave stores a run of n bytes (a group's escape exponents) from `src`
-// (the group's 2048-byte staging slot) to `dst`.  The caller has loaded, for
-// output dwords k = lane + 64 r (r < R), lo[r] = source dword k and hi[r] =
-// source dword k+1: output dword k starts at source byte head + 4k, where
-// head (0..3) brings dst to a 4-byte boundary, so those two dwords serve
-// whatever dst is.  The head bytes come from lane 0's first source dword,
-// the tail bytes from the lane owning the last partial dword; dwords past
-// 64 R (runs over 256 R bytes) are loaded here.
+// (the group's 2048-byte staging slot) to `dst` (global memory or LDS).  The
+// caller has loaded, for output dwords k = lane + 64 r (r < R), lo[r] =
+// source dword k and hi[r] = source dword k+1: output dword k starts at
+// source byte head + 4k, where head (0..3) brings dst to a 4-byte boundary,
+// so those two dwords serve whatever dst is.  The head bytes (from lane 0's
+// first source dword) and the tail bytes (from the dword of the lane owning
+// the partial last output dword) go out as one byte store each, by lanes
+// 0..2; dwords past 64 R (runs over 256 R bytes) are loaded here.
 template <int R>
 __device__ __forceinline__ void store_run(uint8_t* dst, const uint32_t* src, uint32_t n,
                                           const uint32_t (&lo)[R], const uint32_t (&hi)[R]) {
@@ -84,23 +85,22 @@ __device__ __forceinline__ void store_run(uint8_t* dst, const uint32_t* src, uin
     const uint32_t head = min(n, (4u - (uint32_t)(reinterpret_cast<uintptr_t>(dst) & 3u)) & 3u);
     const uint32_t nd = (n - head) >> 2, tail = (n - head) & 3u;
     uint32_t* d32 = reinterpret_cast<uint32_t*>(dst + head);
-    if (lane == 0)
-        for (uint32_t i = 0; i < head; ++i) dst[i] = (uint8_t)(lo[0] >> (8 * i));
+    const uint32_t first = readlane(lo[0], 0);
+    if (lane < head) dst[lane] = (uint8_t)(first >> (8 * lane));
+    uint32_t last = 0;  // the partial last output dword (wave-uniform)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint32_t k = lane + 64 * r;
         const uint32_t v = (uint32_t)((((uint64_t)hi[r] << 32) | lo[r]) >> (8 * head));
         if (k < nd) d32[k] = v;
-        if (k == nd)  // the partial last dword: `tail` bytes
-            for (uint32_t i = 0; i < tail; ++i) dst[head + 4 * nd + i] = (uint8_t)(v >> (8 * i));
+        if ((nd >> 6) == (uint32_t)r) last = readlane(v, (int)(nd & 63));
     }
-    for (uint32_t k = lane + 64 * R; k <= nd; k += 64) {
-        const uint32_t v = (uint32_t)((((uint64_t)src[k + 1] << 32) | src[k]) >> (8 * head));
-        if (k < nd)
-            d32[k] = v;
-        else
-            for (uint32_t i = 0; i < tail; ++i) dst[head + 4 * nd + i] = (uint8_t)(v >> (8 * i));
+    for (uint32_t k = lane + 64 * R; k < nd + 64; k += 64) {  // long runs; also their last dword
+        const uint32_t v = k <= nd ? (uint32_t)((((uint64_t)src[k + 1] << 32) | src[k]) >> (8 * head)) : 0u;
+        if (k < nd) d32[k] = v;
+        if (nd >= 64 * R && k - lane == (nd & ~63u)) last = readlane(v, (int)(nd & 63));
     }
+    if (lane < tail) dst[head + 4 * nd + lane] = (uint8_t)(last >> (8 * lane));
 }
 
 }  // namespace
@@ -182,13 +182,17 @@ __global__ __launch_bounds__(256) void zc_encode(EncodeArgs a) {
 }
 
 // One workgroup of up to 4 waves per chunk; wave w owns the chunk's groups
-// w, w + nw, ... (GPW = groups per wave).
+// w, w + nw, ... (GPW = groups per wave).  The chunk's escape run is
+// gathered in LDS at its final alignment modulo 16 and leaves in 16-byte
+// stores (a run longer than the LDS buffer is stored group by group).
 template <int GPW>
-__global__ __launch_bounds__(256) void zc_place_escapes(PlaceArgs a) {
+__device__ __forceinline__ void place_chunk(const PlaceArgs& a, uint32_t ci) {
     constexpr int R = 2;  // source dword pairs per lane and group loaded ahead
-    __shared__ uint32_t s_gb[32], s_gn[32], s_prefix;  // group offsets in the chunk, counts
-    __shared__ uint32_t s_part[4];                     // per wave: partial sums of earlier chunks
-    const uint32_t ci = blockIdx.x, lane = lane_id(), wave = wave_id(), nw = blockDim.x >> 6;
+    constexpr uint32_t kBuf = 4u * GPW * kGroup + 16u < 19584u ? 4u * GPW * kGroup + 16u : 19584u;  // 8 workgroups per CU
+    __shared__ u32x4 s_buf[kBuf / 16];
+    __shared__ uint32_t s_gb[32], s_gn[32], s_prefix, s_t;  // group offsets in the chunk, counts
+    __shared__ uint32_t s_part[4];                          // per wave: partial sums of earlier chunks
+    const uint32_t lane = lane_id(), wave = wave_id(), nw = blockDim.x >> 6;
     const ItemDesc cd = a.chunks[ci];
     const SegDesc sd = a.segs[cd.seg];
     uint8_t* st = a.out + sd.out_off;
@@ -198,25 +202,45 @@ __global__ __launch_bounds__(256) void zc_place_escapes(PlaceArgs a) {
     const uint32_t* slot0 = reinterpret_cast<const uint32_t*>(a.staging) +
                             (uint64_t)(sd.group_base + gc0) * (kGroup / 4);
 
-    // source dwords of this wave's groups: unconditional (inside the slots)
-    uint32_t lo[GPW][R], hi[GPW][R];
+    // source dwords of this wave's groups, loaded once (inside the slots); the
+    // next dword of each comes from the next lane, lane 63's from the next
+    // round or, for the last round, from one scalar load
+    // (all loads first, branch-free: groups past the chunk's end read its
+    // last group's slot and are not stored)
+    uint32_t lo[GPW][R], hi[GPW][R], past[GPW];
 #pragma unroll
     for (int q = 0; q < GPW; ++q) {
-        const uint32_t j = wave + nw * q;
+        const uint32_t j = min(wave + nw * q, ng - 1);
         const uint32_t* s32 = slot0 + (uint64_t)j * (kGroup / 4);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            lo[q][r] = j < ng ? s32[lane + 64 * r] : 0u;
-            hi[q][r] = j < ng ? s32[lane + 64 * r + 1] : 0u;
-        }
+        for (int r = 0; r < R; ++r) lo[q][r] = s32[lane + 64 * r];
+        past[q] = s32[64 * R];  // wave-uniform address
     }
-    // escapes of the segment's earlier chunks: a strided sum by all threads
+#pragma unroll
+    for (int q = 0; q < GPW; ++q)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t nxt = r + 1 < R ? readlane(lo[q][r + 1 < R ? r + 1 : r], 0) : past[q];
+            const uint32_t sh = dpp<kDppWaveShl1>(lo[q][r]);
+            hi[q][r] = lane == 63 ? nxt : sh;
+        }
+    // escapes of the segment's earlier chunks: a strided sum by all threads,
+    // eight loads in flight per thread
     const uint32_t l = cd.local;
     uint32_t v = 0;
-    for (uint32_t j = threadIdx.x; j < l; j += blockDim.x) v += a.ctot[sd.chunk_base + j];
+    for (uint32_t base = 0; base < l; base += 8 * blockDim.x) {
+        uint32_t c8[8];
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u) {
+            const uint32_t j = base + threadIdx.x + u * blockDim.x;
+            c8[u] = j < l ? a.ctot[sd.chunk_base + j] : 0u;
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u) v += c8[u];
+    }
     v = wave_sum(v);
     if (lane == 0) s_part[wave] = v;
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
         const uint32_t c = lane < ng ? a.gcnt[sd.group_base + gc0 + lane] : 0u;
         const uint32_t incl = wave_inclusive_scan(c);
@@ -232,6 +256,7 @@ __global__ __launch_bounds__(256) void zc_place_escapes(PlaceArgs a) {
             // counts that would leave the escape region mean no copy (never
             // the case when the encoder wrote them)
             s_prefix = (uint64_t)prefix + t <= sd.n ? prefix : 0xFFFFFFFFu;
+            s_t = t;
             reinterpret_cast<uint32_t*>(st + kHeaderBytes)[l] = prefix;
             if (l + 1 == sd.k) {
                 const uint64_t E = (uint64_t)prefix + t;
@@ -242,14 +267,50 @@ __global__ __launch_bounds__(256) void zc_place_escapes(PlaceArgs a) {
             }
         }
     }
-    __syncthreads();
-    if (s_prefix == 0xFFFFFFFFu) return;
-    uint8_t* esc = st + sd.esc_off + s_prefix;
+    lds_barrier();
+    const uint32_t prefix = s_prefix, t = s_t;
+    if (prefix == 0xFFFFFFFFu) {
+        lds_barrier();  // s_* are rewritten by the next chunk
+        return;
+    }
+    uint8_t* esc = st + sd.esc_off + prefix;
+    const uint32_t off = prefix & 15u;  // esc_off and the stream start are multiples of 256
+    if (off + t > kBuf) {
+#pragma unroll
+        for (int q = 0; q < GPW; ++q) {
+            const uint32_t j = wave + nw * q;
+            if (j < ng) store_run<R>(esc + s_gb[j], slot0 + (uint64_t)j * (kGroup / 4), s_gn[j], lo[q], hi[q]);
+        }
+        lds_barrier();  // s_* are rewritten by the next chunk
+        return;
+    }
+    uint8_t* buf = reinterpret_cast<uint8_t*>(s_buf);
 #pragma unroll
     for (int q = 0; q < GPW; ++q) {
         const uint32_t j = wave + nw * q;
-        if (j < ng) store_run<R>(esc + s_gb[j], slot0 + (uint64_t)j * (kGroup / 4), s_gn[j], lo[q], hi[q]);
+        if (j < ng) store_run<R>(buf + off + s_gb[j], slot0 + (uint64_t)j * (kGroup / 4), s_gn[j], lo[q], hi[q]);
     }
+    lds_barrier();
+    // bytes [off, off + t) of the buffer go to esc - off (16-byte aligned):
+    // whole 16-byte blocks, then the partial first and last blocks bytewise
+    uint8_t* base = esc - off;
+    const uint32_t end = off + t, nblk = (end + 15) >> 4;
+    for (uint32_t b = threadIdx.x; b < nblk; b += blockDim.x)
+        if ((b << 4) >= off && (b << 4) + 16 <= end) *reinterpret_cast<u32x4*>(base + (b << 4)) = s_buf[b];
+    if (threadIdx.x < 32 && t) {
+        const uint32_t p = threadIdx.x < 16 ? threadIdx.x : 16 * (nblk - 1) + (threadIdx.x - 16);
+        const bool first_partial = off > 0 || end < 16;
+        const bool last_partial = nblk > 1 && (end & 15u) != 0;
+        const bool mine = threadIdx.x < 16 ? first_partial && p >= off && p < end
+                                           : last_partial && p < end;
+        if (mine) base[p] = buf[p];
+    }
+    lds_barrier();  // s_buf and s_* are rewritten by the next chunk
+}
+
+template <int GPW>
+__global__ __launch_bounds__(256) void zc_place_escapes(PlaceArgs a) {
+    for (uint32_t ci = blockIdx.x; ci < a.nchunks; ci += gridDim.x) place_chunk<GPW>(a, ci);
 }
 
 template __global__ void zc_place_escapes<1>(PlaceArgs);

@@ -110,6 +110,14 @@ __device__ __forceinline__ uint32_t wave_id() {
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads it
+// does not wait for the waves' outstanding global stores.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Cross-lane exchange without LDS addresses: DPP moves within 16-lane rows
 // (plus the row broadcasts of the GFX9 family) and a 32-lane swizzle.  Every
 // lane of the wave must be active.
@@ -120,6 +128,7 @@ enum : int {
     kDppHalfMirror = 0x141,  // row_half_mirror: lane 7 - i of the half row
     kDppBcast15 = 0x142,     // row_bcast:15: lane 15 of the previous row
     kDppBcast31 = 0x143,     // row_bcast:31: lane 31
+    kDppWaveShl1 = 0x130,    // wave_shl:1: lane i + 1 of the wave (lane 63 reads 0)
 };
 __device__ __forceinline__ constexpr int dpp_row_shr(int n) { return 0x110 + n; }
 

@@ -45,6 +45,7 @@ struct PlaceArgs {
     const uint32_t* gcnt;
     const uint32_t* ctot;
     uint32_t chunk_elems;
+    uint32_t nchunks;
 };
 
 struct DecodeArgs {
