@@ -24,6 +24,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12  # bytes/s, MI355X
+# counter summary of the decode kernel on this workload (FETCH_SIZE and
+# WRITE_SIZE per dispatch, scaled by a plain copy's readings), valid while the
+# decoder's sources hash to the value recorded there
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "zc_decode_gradient64M_hbm_traffic.txt")
+DECODER_SOURCES = ["zc_decode.hip", "zc_internal.h", "zc_kernels.h"]
 
 
 def log(*a):
@@ -42,6 +47,27 @@ def timed(fn, steps, warmup, stream):
         b.record(stream)
     torch.cuda.synchronize()
     return [a.elapsed_time(b) * 1e-3 for a, b in evs]  # seconds
+
+
+def decoder_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODER_SOURCES:
+        with open(os.path.join(ROOT, "lossless_bf16_exponent_zc_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when the decoder has changed since it was taken."""
+    try:
+        kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
+        if kv.get("decoder_sources_sha256", "").strip() != decoder_hash():
+            return None
+        return int(kv["traffic_bytes_per_launch"].strip())
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(x, chunk):
@@ -144,7 +170,11 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "zc_decode",
                      "achieved": round(dec_bytes / t_d / 1e9, 1),
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(dec_bytes / t_d / HBM_PEAK, 4), "traffic": None},
+                     "frac": round(dec_bytes / t_d / HBM_PEAK, 4),
+                     # HBM bytes per launch (counters); algorithmic bytes beside it
+                     "traffic": measured_traffic(),
+                     "algorithmic_bytes": dec_bytes,
+                     "launch_us": round(t_d * 1e6, 2)},
     }
 
     if args.copy_ref:
