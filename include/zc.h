@@ -11,10 +11,14 @@
  * asks for GPU kernels with a communication-aware, aligned layout; the
  * stream format (version 1) is:
  *
- *   [0,64) header | chunk table (K+1 u32) | code planes (768 B per 2048
- *   values) | sign+mantissa bytes (2048 B per 2048 values) | escape bytes
+ *   [0,64) header | chunk table (K+1 u32) | group table (one u16 per 2048
+ *   values) | code planes (768 B per 2048 values) | sign+mantissa bytes
+ *   (2048 B per 2048 values) | escape bytes
  *
- * with every region after the table 256-byte aligned.  Field by field:
+ * with the code planes and every region after them 256-byte aligned.  Chunk
+ * table entry k is the number of escapes before chunk k (entry K = E); group
+ * table entry g is the number of escapes in group g's chunk before group g.
+ * Field by field:
  *   u32 magic "ZCB1" @0, u16 version=1 @4, u8 L @6, u8 flags=0 @7,
  *   u64 N @8, u32 C @16, u32 K @20, u64 E @24, u64 total @32,
  *   u64 code_off @40, u64 sm_off @48, u64 esc_off @56.
@@ -62,8 +66,9 @@ typedef enum zc_status {
 #define ZC_FMT_WINDOW 0x02u /* L outside 1..248                           */
 #define ZC_FMT_SHAPE  0x04u /* N, C, K or a region offset disagree        */
 #define ZC_FMT_SIZE   0x08u /* E > N, or total bytes past the buffer      */
-#define ZC_FMT_TABLE  0x10u /* chunk table not 0..E and non-decreasing    */
-#define ZC_FMT_COUNT  0x20u /* a chunk's escape count differs from codes  */
+#define ZC_FMT_TABLE  0x10u /* chunk table not 0..E and non-decreasing, or
+                               a chunk's first group entry is not 0        */
+#define ZC_FMT_COUNT  0x20u /* a group's escape count differs from codes */
 #define ZC_FMT_PAD    0x40u /* nonzero code bits or sm bytes past N       */
 
 typedef struct zc_plan zc_plan; /* opaque, host-owned, immutable */
@@ -94,7 +99,9 @@ uint64_t zc_plan_stream_offset(const zc_plan *plan, uint32_t s);
 uint64_t zc_plan_max_stream_bytes(const zc_plan *plan, uint32_t s);
 /* Bytes the compressed buffer must hold for every segment's worst case. */
 uint64_t zc_plan_out_bytes(const zc_plan *plan);
-/* Workspace bytes needed by any call with this plan. */
+/* Workspace bytes needed by any call with this plan: about one byte per
+ * value (compress stages escape exponents there, 2048 bytes per 2048-value
+ * group) plus a few bytes per group and chunk. */
 uint64_t zc_plan_workspace_bytes(const zc_plan *plan);
 
 /*
