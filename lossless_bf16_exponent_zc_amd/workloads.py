@@ -99,14 +99,21 @@ def zipf_counts(total: int = 65536, experts: int = 256,
 
 
 def moe(tokens: int = 65536, hidden: int = 7168, experts: int = 256,
-        seed: int = 0):
+        seed: int = 0, device: str = "cpu"):
     """Returns (flat bits, per-segment value counts).  Draw order:
     z = randn(tokens, hidden), then the token scale exp(0.5 * randn(tokens, 1)).
-    Rows are grouped into contiguous expert segments by ``zipf_counts``."""
-    g = _gen(seed)
-    z = torch.randn(tokens, hidden, generator=g)
-    scale = torch.exp(0.5 * torch.randn(tokens, 1, generator=g))
-    bits = to_bits(z * scale)
+    Rows are grouped into contiguous expert segments by ``zipf_counts``.
+    device="cuda" draws the same recipe with torch's CUDA generator (seeded
+    the same way; other values, same distribution), which is much faster for
+    the full 469,762,048-value tensor."""
+    if device == "cpu":
+        g = _gen(seed)
+    else:
+        g = torch.Generator(device=device)
+        g.manual_seed(seed)
+    z = torch.randn(tokens, hidden, generator=g, device=device)
+    scale = torch.exp(0.5 * torch.randn(tokens, 1, generator=g, device=device))
+    bits = to_bits((z * scale).cpu() if device != "cpu" else z * scale)
     counts = zipf_counts(tokens, experts)
     return bits, [c * hidden for c in counts]
 

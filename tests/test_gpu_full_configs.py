@@ -1,0 +1,79 @@
+"""GPU parity at the full sizes of the workloads, in the launch configuration
+the benchmark times (one plan per workload, 65,536-value chunks): every
+stream byte-identical to the oracle's, window statistics bit-identical,
+round trips bit-exact, and the fixed-order reduce bit-exact against the
+oracle's.  The 1,048,576-value workload is in test_gpu_parity.
+
+The oracle runs segment by segment in a thread pool (its C calls release the
+interpreter lock).
+"""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+import oracle
+from lossless_bf16_exponent_zc_amd import workloads as W
+
+from gpu_util import gpu_compress, gpu_decompress, gpu_reduce, say
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+CHUNK = 65536
+
+
+def pool_map(fn, items):
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        return list(ex.map(fn, items))
+
+
+def check_full(segs, name):
+    say(f"  {name}: {len(segs)} segment(s), {sum(s.size for s in segs):,} values")
+    streams, plan, out, ws = gpu_compress(segs, CHUNK)
+    refs = pool_map(lambda s: oracle.compress(s, C=CHUNK), segs)
+    for s, (a, b) in enumerate(zip(streams, refs)):
+        if a != b:
+            x, y = np.frombuffer(a, np.uint8), np.frombuffer(b, np.uint8)
+            m = min(x.size, y.size)
+            d = np.nonzero(x[:m] != y[:m])[0]
+            raise AssertionError(f"{name} segment {s}: {x.size} vs {y.size} bytes, "
+                                 f"first differences at {d[:8].tolist()}")
+    say(f"  {name}: streams identical ({sum(len(r) for r in refs):,} bytes)")
+    sig = pool_map(oracle.sigma, segs)
+    for s, o in enumerate(sig):
+        assert plan.read_sigma(ws, s) == o, (name, s)
+    bits, dec = gpu_decompress(plan, out, ws)
+    assert bits == 0, hex(bits)
+    for s, (seg, d) in enumerate(zip(segs, dec)):
+        assert np.array_equal(seg, d), (name, s)
+    say(f"  {name}: round trip exact")
+
+
+def test_gradient_64M():
+    check_full([W.gradient()], "gradient 67,108,864")
+
+
+def test_llama_mlp_layer():
+    check_full(W.llama_mlp(), "Llama3-8B MLP matrices")
+
+
+def test_moe_all_to_all_segments():
+    bits, sizes = W.moe(device="cuda")
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    segs = [bits[offs[i]:offs[i + 1]] for i in range(len(sizes))]
+    check_full(segs, "MoE 256 experts")
+
+
+def test_reduce_scatter_receive_8_shards():
+    shards = W.shards()
+    n = shards[0].size
+    say(f"  reduce: 8 shards of {n:,} values")
+    refs = pool_map(lambda s: oracle.compress(s, C=CHUNK), shards)
+    for i, sh in enumerate(shards):  # the GPU's own streams are the oracle's
+        got, _, _, _ = gpu_compress([sh], CHUNK)
+        assert got[0] == refs[i], i
+    bits, out = gpu_reduce(refs, n, CHUNK)
+    assert bits == 0, hex(bits)
+    assert np.array_equal(out, oracle.decompress_reduce(refs, n, C=CHUNK))
+    say("  reduce: bit-exact")
