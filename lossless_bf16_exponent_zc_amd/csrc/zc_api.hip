@@ -1,20 +1,21 @@
 // zc_api.hip -- the C ABI: plans, argument checks and launch sequences.
 //
 // Compress (ZipCCL scribe notes, "Key idea and contribution", technique 1):
-//   zc_sigma_partials  fp64 moments per 16,384-value block
+//   zc_encode          fp64 moment partials per 16,384-value block, and the
+//                      codes, sign+mantissa bytes, staged escape exponents
+//                      and escape counts, with each segment's previous window
+//                      as the prediction (or the caller's fixed window)
 //   zc_window          per segment: variance -> window, statistics, header
-//                      fields known before encoding; clears escape counts
-//   zc_encode          codes, sign+mantissa bytes, escape exponents staged
-//                      per group, escape counts per group, chunk and run of
-//                      chunks (one wave per two groups)
-//   zc_place_escapes   group table, chunk offsets, escapes to their place,
-//                      chunk table, sizes
+//                      fields known before encoding; where the prediction
+//                      failed, the segment's codes again; chunk table, sizes
+//   zc_place_escapes   group table, escapes to their place
 // Decompress: zc_decode.  Decompress-reduce: zc_decode_reduce.
 // Every call enqueues on the caller's stream and returns; nothing here reads
 // device memory except the two zc_read_* helpers, which synchronise.
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -26,14 +27,14 @@ using namespace zc;
 struct zc_plan {
     uint32_t nseg = 0, chunk = 0, block = 0;
     std::vector<SegDesc> segs;
-    std::vector<ItemDesc> blocks, chunks, groups, pairs;  // pairs: encoder waves
+    std::vector<ItemDesc> chunks, groups, pairs, witems;  // pairs: encoder waves; witems: window workgroups
     uint64_t input_elems = 0, out_bytes = 0;
     WsLayout ws{};
     SegDesc* d_segs = nullptr;
-    ItemDesc* d_blocks = nullptr;
     ItemDesc* d_chunks = nullptr;
     ItemDesc* d_groups = nullptr;
     ItemDesc* d_pairs = nullptr;
+    ItemDesc* d_witems = nullptr;
 };
 
 namespace {
@@ -42,7 +43,6 @@ uint64_t a256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
 uint64_t cdiv(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-uint32_t nblocks(const zc_plan* p) { return (uint32_t)p->blocks.size(); }
 uint32_t nchunks(const zc_plan* p) { return (uint32_t)p->chunks.size(); }
 uint32_t ngroups(const zc_plan* p) { return (uint32_t)p->groups.size(); }
 uint32_t group_grid(const zc_plan* p) { return (ngroups(p) + 3) / 4; }
@@ -62,17 +62,6 @@ T* ws_ptr(const zc_plan* p, void* d_ws, uint64_t off) {
     return reinterpret_cast<T*>(static_cast<uint8_t*>(d_ws) + off);
 }
 
-// moment block = NWV waves x BPW blocks of 2048 values
-void launch_sigma(const zc_plan* p, const SigmaArgs& a, hipStream_t s) {
-    const dim3 grid(nblocks(p));
-    switch (p->block / kGroup) {
-        case 1: hipLaunchKernelGGL((zc_sigma_partials<1, 1>), grid, dim3(64), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((zc_sigma_partials<2, 1>), grid, dim3(128), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((zc_sigma_partials<4, 1>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((zc_sigma_partials<4, 2>), grid, dim3(256), 0, s, a); break;
-    }
-}
-
 zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
                         uint64_t* d_stream_bytes, uint32_t forced_L, void* d_ws, uint64_t ws_bytes,
                         hipStream_t stream) {
@@ -83,27 +72,36 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     if (out_capacity < p->out_bytes) return ZC_ERR_CAPACITY;
     if (zc_status e = check_ws(p, d_ws, ws_bytes)) return e;
 
-    Partial* partials = ws_ptr<Partial>(p, d_ws, p->ws.partials);
-    SegStat* stats = ws_ptr<SegStat>(p, d_ws, p->ws.stats);
-    uint32_t* gcnt = ws_ptr<uint32_t>(p, d_ws, p->ws.gcnt);
-    uint32_t* ctot = ws_ptr<uint32_t>(p, d_ws, p->ws.ctot);
-    uint8_t* staging = ws_ptr<uint8_t>(p, d_ws, p->ws.staging);
-    const uint16_t* in = static_cast<const uint16_t*>(d_in);
-    uint8_t* out = static_cast<uint8_t*>(d_out);
-
-    if (!forced_L && nblocks(p)) {
-        SigmaArgs sa{p->d_segs, p->d_blocks, in, partials, p->block};
-        launch_sigma(p, sa, stream);
+    const uint32_t nwg = (uint32_t)(p->pairs.size() / 4);
+    EncodeArgs ea{};
+    ea.segs = p->d_segs;
+    ea.pairs = p->d_pairs;
+    ea.in = static_cast<const uint16_t*>(d_in);
+    ea.out = static_cast<uint8_t*>(d_out);
+    ea.stats = ws_ptr<SegStat>(p, d_ws, p->ws.stats);
+    ea.part.s1 = ws_ptr<double>(p, d_ws, p->ws.ps1);
+    ea.part.s2 = ws_ptr<double>(p, d_ws, p->ws.ps2);
+    ea.part.n = ws_ptr<uint32_t>(p, d_ws, p->ws.pn);
+    ea.part.esc = ws_ptr<uint32_t>(p, d_ws, p->ws.pesc);
+    ea.pred = ws_ptr<uint32_t>(p, d_ws, p->ws.pred);
+    ea.done = ws_ptr<uint32_t>(p, d_ws, p->ws.done);
+    ea.staging = ws_ptr<uint8_t>(p, d_ws, p->ws.staging);
+    ea.gcnt = ws_ptr<uint32_t>(p, d_ws, p->ws.gcnt);
+    ea.block_elems = p->block;
+    ea.forced_L = forced_L;
+    if (nwg) {
+        if (forced_L) hipLaunchKernelGGL((zc_encode<false>), dim3(nwg), dim3(256), 0, stream, ea);
+        else hipLaunchKernelGGL((zc_encode<true>), dim3(nwg), dim3(256), 0, stream, ea);
     }
-    WindowArgs wa{p->d_segs, partials, stats, out, d_stream_bytes, ctot, p->chunk, forced_L};
-    hipLaunchKernelGGL(zc_window, dim3(p->nseg), dim3(1024), 0, stream, wa);
+    WindowArgs wa{ea, p->d_witems, ws_ptr<SegStat>(p, d_ws, p->ws.stats), d_stream_bytes,
+                  p->chunk, p->chunk / p->block};
+    hipLaunchKernelGGL(zc_window, dim3((uint32_t)p->witems.size()), dim3(256), 0, stream, wa);
+    uint8_t* out = static_cast<uint8_t*>(d_out);
+    uint8_t* staging = ea.staging;
+    uint32_t* gcnt = ea.gcnt;
     if (nchunks(p)) {
-        EncodeArgs ea{p->d_segs, p->d_pairs, in, out, stats, staging, gcnt, ctot, p->chunk};
-        PlaceArgs pa{p->d_segs, p->d_chunks, out, d_stream_bytes, staging, gcnt, ctot, p->chunk,
-                     nchunks(p)};
+        PlaceArgs pa{p->d_segs, p->d_chunks, out, staging, gcnt, p->chunk, nchunks(p)};
         const uint32_t gpc = p->chunk / kGroup;
-        const dim3 grid(nchunks(p));
-        hipLaunchKernelGGL(zc_encode, dim3((uint32_t)(p->pairs.size() / 4)), dim3(256), 0, stream, ea);
         // placement: up to 4 waves, each with gpc / waves groups
         const uint32_t pw = gpc < 4 ? gpc : 4;
         const dim3 pblock(64 * pw);
@@ -148,7 +146,7 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
     p->nseg = num_segments;
     p->chunk = C;
     p->block = C < kSigmaBlock ? C : kSigmaBlock;
-    uint64_t in_off = 0, out_off = 0;
+    uint64_t in_off = 0, out_off = 0, sb = 0;
     for (uint32_t s = 0; s < num_segments; ++s) {
         const uint64_t n = segment_elems[s];
         if (n >= (1ull << 32)) {
@@ -167,16 +165,24 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
         d.max_bytes = d.esc_off + n;
         d.in_off = in_off;
         d.out_off = out_off;
-        d.sb_base = (uint32_t)p->blocks.size();
+        d.sb_base = (uint32_t)sb;
+        uint64_t pb = 1;
+        while (pb < d.nsb) pb <<= 1;
+        sb += d.nsb ? pb : 0;  // leaf slots span the power of two
         d.group_base = (uint32_t)p->groups.size();
         d.chunk_base = (uint32_t)p->chunks.size();
         in_off += (n + 7) & ~uint64_t(7);
         out_off += a256(d.max_bytes);
-        for (uint32_t b = 0; b < d.nsb; ++b) p->blocks.push_back(ItemDesc{s, b});
         for (uint32_t k = 0; k < d.k; ++k) p->chunks.push_back(ItemDesc{s, k});
         for (uint32_t g = 0; g < d.g; ++g) p->groups.push_back(ItemDesc{s, g});
+        d.wg_base = (uint32_t)(p->pairs.size() / 4);
         for (uint32_t q = 0; q < (d.g + 1) / 2; ++q) p->pairs.push_back(ItemDesc{s, q});
         while (p->pairs.size() % 4) p->pairs.push_back(ItemDesc{0xFFFFFFFFu, 0});  // whole workgroups
+        d.nwg = (uint32_t)(p->pairs.size() / 4) - d.wg_base;
+        // window workgroups: enough to code the segment again at about 16
+        // items each, at most 256 (each joins all of the segment's partials)
+        d.wr = (uint32_t)std::min<uint64_t>(256, std::max<uint64_t>(1, cdiv(d.nwg, 16)));
+        for (uint32_t r = 0; r < d.wr; ++r) p->witems.push_back(ItemDesc{s, r});
         if (p->groups.size() >= (1ull << 31)) {
             delete p;
             return ZC_ERR_UNSUPPORTED;
@@ -185,32 +191,36 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
     }
     p->input_elems = in_off;
     p->out_bytes = out_off;
-    const uint64_t G = p->groups.size(), B = p->blocks.size(), K = p->chunks.size();
+    const uint64_t G = p->groups.size(), B = sb, K = p->chunks.size();
     const uint64_t W = p->pairs.size();
     uint64_t o = 0;
     p->ws.status = o;   o += a256(4 * G);
-    p->ws.partials = o; o += a256(sizeof(Partial) * B);
+    p->ws.ps1 = o;      o += a256(8 * B);
+    p->ws.ps2 = o;      o += a256(8 * B);
+    p->ws.pn = o;       o += a256(4 * B);
+    p->ws.pesc = o;     o += a256(4 * B);
     p->ws.stats = o;    o += a256(sizeof(SegStat) * num_segments);
     p->ws.gcnt = o;     o += a256(4 * G);
-    p->ws.ctot = o;     o += a256(4 * K);
+    p->ws.pred = o;     o += a256(4ull * num_segments);
+    p->ws.done = o;     o += a256(4ull * num_segments);
     p->ws.staging = o;  o += a256((uint64_t)kGroup * G + 16);
     p->ws.total = o;
 
     if (hipMalloc(&p->d_segs, sizeof(SegDesc) * p->segs.size()) != hipSuccess ||
-        hipMalloc(&p->d_blocks, sizeof(ItemDesc) * (B ? B : 1)) != hipSuccess ||
         hipMalloc(&p->d_chunks, sizeof(ItemDesc) * (K ? K : 1)) != hipSuccess ||
         hipMalloc(&p->d_groups, sizeof(ItemDesc) * (G ? G : 1)) != hipSuccess ||
         hipMalloc(&p->d_pairs, sizeof(ItemDesc) * (W ? W : 1)) != hipSuccess ||
+        hipMalloc(&p->d_witems, sizeof(ItemDesc) * p->witems.size()) != hipSuccess ||
         hipMemcpy(p->d_segs, p->segs.data(), sizeof(SegDesc) * p->segs.size(),
                   hipMemcpyHostToDevice) != hipSuccess ||
-        (B && hipMemcpy(p->d_blocks, p->blocks.data(), sizeof(ItemDesc) * B,
-                        hipMemcpyHostToDevice) != hipSuccess) ||
         (K && hipMemcpy(p->d_chunks, p->chunks.data(), sizeof(ItemDesc) * K,
                         hipMemcpyHostToDevice) != hipSuccess) ||
         (G && hipMemcpy(p->d_groups, p->groups.data(), sizeof(ItemDesc) * G,
                         hipMemcpyHostToDevice) != hipSuccess) ||
         (W && hipMemcpy(p->d_pairs, p->pairs.data(), sizeof(ItemDesc) * W,
-                        hipMemcpyHostToDevice) != hipSuccess)) {
+                        hipMemcpyHostToDevice) != hipSuccess) ||
+        hipMemcpy(p->d_witems, p->witems.data(), sizeof(ItemDesc) * p->witems.size(),
+                  hipMemcpyHostToDevice) != hipSuccess) {
         zc_plan_destroy(p);
         return ZC_ERR_HIP;
     }
@@ -221,10 +231,10 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
 void zc_plan_destroy(zc_plan* p) {
     if (!p) return;
     if (p->d_segs) (void)hipFree(p->d_segs);
-    if (p->d_blocks) (void)hipFree(p->d_blocks);
     if (p->d_chunks) (void)hipFree(p->d_chunks);
     if (p->d_groups) (void)hipFree(p->d_groups);
     if (p->d_pairs) (void)hipFree(p->d_pairs);
+    if (p->d_witems) (void)hipFree(p->d_witems);
     delete p;
 }
 

@@ -1,0 +1,226 @@
+// zc_encoder.h -- one encoder workgroup item: exponent codes, sign+mantissa
+// bytes, staged escape exponents and escape counts of 16,384 values, and
+// optionally the moment partials of the window's pairwise tree.
+//
+// ZipCCL scribe notes, "Key idea and contribution": technique 1 (each value
+// whose exponent lies in the 7-exponent window [L, L+6] becomes a 3-bit
+// code, sign and mantissa stay raw, other exponents are kept whole in a
+// separate stream; the window comes from the standard deviation) and
+// technique 2 (GPU kernel with an aligned, communication-aware layout).
+//
+// Per group (2048 values, one wave): one 16-byte load per lane and tile;
+// packed 16-bit ops give (e - L) clamped to 7 for two values at a time;
+// nibble packing and a 4-way bit interleave turn the lane's 32 codes into
+// its three plane words; plane words and sign+mantissa bytes go out at once
+// (static offsets).  Escapes (code 7 = all three plane bits set) are counted
+// and ranked across the wave with ballots; each lane puts its 32 exponent
+// bytes in an LDS row (plane-bit order) and copies its escapes' bytes from
+// there, in code order, into the wave's packed LDS area, which goes out in
+// aligned dwords to the group's staging slot.
+#pragma once
+
+#include "zc_kernels.h"
+#include "zc_moments.h"
+
+namespace zc {
+
+__device__ __forceinline__ void encode_group(const u32x4 (&w)[4], uint32_t L7, uint32_t (&P)[3],
+                                             u32x2 (&sm)[4]) {
+    uint32_t Z[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t c[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)  // (e - L) << 7 per half, wrapped values clamp to 7 << 7
+            c[m] = pk_min_u16(pk_sub_u16(w[k][m] & 0x7F807F80u, L7), 0x03800380u);
+        // code of value 2m -> nibble m, of value 2m+1 -> nibble m + 4
+        Z[k] = (c[0] >> 7) | (c[1] >> 3) | (c[2] << 1) | (c[3] << 5);
+        sm[k].x = bitsel(0x80808080u, perm(w[k][1], w[k][0], 0x07050301u),
+                         perm(w[k][1], w[k][0], 0x06040200u));
+        sm[k].y = bitsel(0x80808080u, perm(w[k][3], w[k][2], 0x07050301u),
+                         perm(w[k][3], w[k][2], 0x06040200u));
+    }
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+        P[b] = ((Z[0] >> b) & 0x11111111u) | (((Z[1] >> b) & 0x11111111u) << 1) |
+               (((Z[2] >> b) & 0x11111111u) << 2) | (((Z[3] >> b) & 0x11111111u) << 3);
+}
+
+// Exponent bytes of the lane's 32 values in plane-bit order: byte p of the
+// 32-byte array belongs to bit p (p = 4n + k: tile k, nibble n).
+__device__ __forceinline__ void exponent_bytes(const u32x4 (&w)[4], uint32_t (&Q)[8]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        // after << 1 the exponent of the low value is byte 1, of the high one byte 3
+        const uint32_t A = w[0][m] << 1, B = w[1][m] << 1, C = w[2][m] << 1, D = w[3][m] << 1;
+        const uint32_t X = perm(B, A, 0x07030501u);  // A.b1 B.b1 A.b3 B.b3
+        const uint32_t Y = perm(D, C, 0x07030501u);  // C.b1 D.b1 C.b3 D.b3
+        Q[m] = perm(Y, X, 0x05040100u);              // low values of tiles 0..3
+        Q[m + 4] = perm(Y, X, 0x07060302u);          // high values of tiles 0..3
+    }
+}
+
+// Moments of one group (the wave's LDS area holds its 2048 values in index
+// order; lane l takes values 32l .. 32l + 31): per lane the 8-value trees of
+// its four runs joined as (r0 + r1) + (r2 + r3), then the lane butterfly.
+// One run at a time, to keep the fp64 temporaries of a single run live.
+__device__ __forceinline__ void group_moments(const u32x4* area, uint32_t lane, uint64_t base,
+                                              uint64_t n, double& g1, double& g2, uint32_t& gn) {
+    double e1 = 0.0, e2 = 0.0, c1 = 0.0, c2 = 0.0;
+    uint32_t cnt = 0;
+#pragma unroll 1
+    for (uint32_t t = 0; t < 4; ++t) {
+        double r1, r2;
+        uint32_t c;
+        moments8(area[4 * lane + t], base + 8 * t, n, r1, r2, c);
+        cnt += c;
+        if (t & 1) {  // uniform
+            const double p1 = e1 + r1, p2 = e2 + r2;
+            c1 = t == 1 ? p1 : c1 + p1;
+            c2 = t == 1 ? p2 : c2 + p2;
+        } else {
+            e1 = r1;
+            e2 = r2;
+        }
+    }
+    g1 = wave_tree(c1);
+    g2 = wave_tree(c2);
+    gn = wave_sum(cnt);
+}
+
+// The window the first pass uses: the previous call's window recorded in the
+// workspace, clamped to 1..248 (whatever the workspace held: it is only a
+// prediction, checked by the window kernel).
+__device__ __forceinline__ uint32_t predicted_L(uint32_t raw) {
+    return raw < 1u ? 1u : (raw > 248u ? 248u : raw);
+}
+
+// One workgroup item: four waves, each with two consecutive groups of one
+// segment (item list: one entry per wave; each segment's list is padded to
+// whole workgroups with entries of segment ~0, whose waves do no work), so
+// the item covers 16,384 aligned values of one segment: one moment block, or
+// several whole ones when the chunk is smaller.  Codes with window L; each
+// group's escape count and each block's total; with MOMENTS, the blocks'
+// moment partials: the tree needs each lane to hold 32 consecutive values,
+// so a group is transposed through the wave's LDS area first, and groups
+// join pairwise into blocks.
+// LDS per wave: 4112 bytes, the group's values for the transpose, then a
+// 32-byte exponent row per lane and the packed escapes (every value may
+// escape).  Every thread of the 256-thread workgroup calls this (barriers).
+template <bool MOMENTS>
+__device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint32_t L) {
+    __shared__ u32x4 s_area[4][257];  // per wave, 4112 bytes
+    __shared__ double s_g1[8], s_g2[8];
+    __shared__ uint32_t s_gn[8], s_gc[8];
+    const uint32_t lane = lane_id(), wave = wave_id();
+    uint8_t* area = reinterpret_cast<uint8_t*>(s_area[wave]);
+    u32x4* rowp = s_area[wave] + 2 * lane;  // the lane's exponent row
+    uint8_t* ew = area + 2048;              // the wave's packed escapes
+    const uint32_t* ew32 = reinterpret_cast<const uint32_t*>(ew);
+    const ItemDesc first = a.pairs[wg * 4];  // a live entry: its segment is the workgroup's
+    const ItemDesc it = a.pairs[wg * 4 + wave];
+    const bool live = it.seg != 0xFFFFFFFFu;
+    const SegDesc sd = a.segs[first.seg];
+    const uint64_t g0 = 2ull * it.local;
+    u32x4 w[2][4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        if (live && g0 + q < sd.g) {
+            load_group(a.in + sd.in_off, sd.n, g0 + q, lane, w[q]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[q][k] = u32x4{0, 0, 0, 0};
+        }
+    }
+    double m1[2] = {0.0, 0.0}, m2[2] = {0.0, 0.0};  // group moments (wave-uniform)
+    uint32_t mn[2] = {0, 0}, ec[2] = {0, 0};       // values, escapes
+    if (live) {
+        uint8_t* __restrict__ st = a.out + sd.out_off;
+        const uint32_t L7 = (L << 7) | (L << 23);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint64_t g = g0 + q;
+            if (g >= sd.g) break;  // uniform
+            if (MOMENTS) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) s_area[wave][64 * k + lane] = w[q][k];
+                __builtin_amdgcn_wave_barrier();
+                group_moments(s_area[wave], lane, (uint64_t)kGroup * g + 32u * lane, sd.n,
+                              m1[q], m2[q], mn[q]);
+                __builtin_amdgcn_wave_barrier();  // before the area is reused
+            }
+            uint32_t P[3];
+            u32x2 sm[4];
+            encode_group(w[q], L7, P, sm);
+            if ((uint64_t)kGroup * (g + 1) > sd.n) {  // last, partial group: padding codes are 0
+                const uint32_t V = valid_bits(lane, (uint32_t)(sd.n - (uint64_t)kGroup * g));
+#pragma unroll
+                for (int b = 0; b < 3; ++b) P[b] &= V;
+            }
+            uint8_t* cw = st + sd.code_off + 768ull * g + 4u * lane;
+#pragma unroll
+            for (int b = 0; b < 3; ++b) *reinterpret_cast<uint32_t*>(cw + 256 * b) = P[b];
+            uint8_t* sw = st + sd.sm_off + 2048ull * g + 8u * lane;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x2*>(sw + 512 * k) = sm[k];
+            const uint32_t M = P[0] & P[1] & P[2];
+            uint32_t tot;
+            const uint32_t excl = wave_prefix_small(__builtin_popcount(M), tot);
+            ec[q] = tot;
+            const uint64_t gg = sd.group_base + g;
+            if (lane == 0) a.gcnt[gg] = tot;
+            uint32_t Q[8];
+            exponent_bytes(w[q], Q);
+            rowp[0] = u32x4{Q[0], Q[1], Q[2], Q[3]};
+            rowp[1] = u32x4{Q[4], Q[5], Q[6], Q[7]};
+            const uint8_t* rb = reinterpret_cast<const uint8_t*>(rowp);
+            for (uint32_t m = M, i = 0; m; m &= m - 1, ++i) ew[excl + i] = rb[__builtin_ctz(m)];
+            __builtin_amdgcn_wave_barrier();  // the wave's packed bytes are complete
+            uint32_t* slot = reinterpret_cast<uint32_t*>(a.staging + gg * kGroup);
+            for (uint32_t k = lane; k < (tot + 3) / 4; k += 64) slot[k] = ew32[k];
+            __builtin_amdgcn_wave_barrier();  // before the next group reuses the area
+        }
+    }
+    // the workgroup's blocks (all four waves reach this)
+    if (lane == 0) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            s_gc[2 * wave + q] = ec[q];
+            if (MOMENTS) {
+                s_g1[2 * wave + q] = m1[q];
+                s_g2[2 * wave + q] = m2[q];
+                s_gn[2 * wave + q] = mn[q];
+            }
+        }
+    }
+    lds_barrier();
+    const uint32_t per = a.block_elems / kGroup;  // groups per block: 1, 2, 4 or 8
+    const uint32_t b = threadIdx.x;
+    const uint32_t blk = (uint32_t)(2ull * first.local / per) + b;
+    if (b < 8 / per && blk < sd.nsb) {
+        uint32_t e = 0;
+        for (uint32_t i = 0; i < per; ++i) e += s_gc[b * per + i];
+        a.part.esc[sd.sb_base + blk] = e;
+        if (MOMENTS) {
+            double t1[8], t2[8];
+            uint32_t n = 0;
+            for (uint32_t i = 0; i < per; ++i) {
+                t1[i] = s_g1[b * per + i];
+                t2[i] = s_g2[b * per + i];
+                n += s_gn[b * per + i];
+            }
+            for (uint32_t h = 1; h < per; h <<= 1)
+                for (uint32_t i = 0; i < per; i += 2 * h) {
+                    t1[i] = t1[i] + t1[i + h];
+                    t2[i] = t2[i] + t2[i + h];
+                }
+            const uint32_t slot = sd.sb_base + leaf_slot(blk, leaf_order(sd.nsb));
+            a.part.s1[slot] = t1[0];
+            a.part.s2[slot] = t2[0];
+            a.part.n[slot] = n;
+        }
+    }
+    lds_barrier();  // s_g* are rewritten by the next workgroup item
+}
+
+}  // namespace zc

@@ -41,9 +41,13 @@ struct SegDesc {
     uint32_t k;          // chunks
     uint32_t g;          // groups
     uint32_t nsb;        // moment blocks
-    uint32_t sb_base;    // first moment block of this segment in the plan's list
+    uint32_t sb_base;    // first entry of this segment's moment block arrays (2^ceil(log2 nsb) entries)
     uint32_t group_base; // first group of this segment in the plan's list
     uint32_t chunk_base; // first chunk of this segment in the plan's list
+    uint32_t wg_base;    // first encoder workgroup item of this segment
+    uint32_t nwg;        // encoder workgroup items (16,384 values each)
+    uint32_t wr;         // window-kernel workgroups of this segment
+    uint32_t pad;
 };
 
 struct ItemDesc {  // a moment block, chunk or group: its segment and index inside it
@@ -51,10 +55,11 @@ struct ItemDesc {  // a moment block, chunk or group: its segment and index insi
     uint32_t local;
 };
 
-struct Partial {  // per-chunk moments
-    double s1, s2;
-    uint64_t n;
-    uint64_t pad;
+struct Partials {  // per moment block, plan-wide arrays (segment s from sb_base)
+    double* s1;     // moments, at the block's leaf slot (leaf_slot)
+    double* s2;
+    uint32_t* n;    // finite values, at the leaf slot
+    uint32_t* esc;  // escapes of the last encoder pass, at the block index
 };
 
 struct SegStat {  // per-segment window statistics
@@ -67,10 +72,14 @@ struct SegStat {  // per-segment window statistics
 // Workspace carve-up (all offsets 256-aligned), computed on the host.
 struct WsLayout {
     uint64_t status;    // u32 per group: rejection bits of the last decode
-    uint64_t partials;  // Partial per moment block
+    uint64_t ps1;       // f64 per moment block slot
+    uint64_t ps2;       // f64 per moment block slot
+    uint64_t pn;        // u32 per moment block slot
+    uint64_t pesc;      // u32 per moment block
     uint64_t stats;     // SegStat per segment
     uint64_t gcnt;      // u32 per group: escape count
-    uint64_t ctot;      // u32 per chunk: escape count
+    uint64_t pred;      // u32 per segment: the window of the first encoder pass
+    uint64_t done;      // u32 per segment: window workgroups done re-coding
     uint64_t staging;   // 2048 bytes per group (+16): escape exponents before placement
     uint64_t total;
 };

@@ -5,45 +5,36 @@
 
 namespace zc {
 
-struct SigmaArgs {
-    const SegDesc* segs;
-    const ItemDesc* blocks;  // moment blocks
-    const uint16_t* in;
-    Partial* partials;
-    uint32_t block_elems;
-};
-
-struct WindowArgs {
-    const SegDesc* segs;
-    const Partial* partials;
-    SegStat* stats;
-    uint8_t* out;
-    uint64_t* stream_bytes;  // written here for empty segments
-    uint32_t* ctot;          // per-chunk escape counts, cleared here
-    uint32_t chunk_elems;
-    uint32_t forced_L;       // 0: window from the moments
-};
-
 struct EncodeArgs {
     const SegDesc* segs;
     const ItemDesc* pairs;  // per wave: (segment, pair index); segment ~0 pads a segment's workgroups
     const uint16_t* in;
     uint8_t* out;
-    const SegStat* stats;   // the window of each segment
+    const SegStat* stats;   // the previous window (the first pass's prediction)
+    Partials part;          // per block: escape count; with moments, the moments
+    uint32_t* pred;         // per segment: the window the first pass used
+    uint32_t* done;         // per segment: window workgroups done re-coding (first pass clears)
     uint8_t* staging;       // 2048 bytes per group (+16): the group's escape exponents
     uint32_t* gcnt;         // per group: its escape count
-    uint32_t* ctot;         // per chunk: escape count, atomic adds
+    uint32_t block_elems;   // moment block (16,384 values, or the chunk if smaller)
+    uint32_t forced_L;      // nonzero: this window for every segment, no moments
+};
+
+struct WindowArgs {
+    EncodeArgs enc;           // for segments the first pass coded with another window
+    const ItemDesc* items;    // per workgroup: (segment, index among the segment's wr)
+    SegStat* stats;           // written by each segment's workgroup 0
+    uint64_t* stream_bytes;
     uint32_t chunk_elems;
+    uint32_t chunk_blocks;    // moment blocks per chunk: 1, 2 or 4
 };
 
 struct PlaceArgs {
     const SegDesc* segs;
     const ItemDesc* chunks;
     uint8_t* out;
-    uint64_t* stream_bytes;
     const uint8_t* staging;
     const uint32_t* gcnt;
-    const uint32_t* ctot;
     uint32_t chunk_elems;
     uint32_t nchunks;
 };
@@ -60,9 +51,8 @@ struct DecodeArgs {
     uint32_t* status;                // per group
 };
 
-template <int NWV, int BPW>
-__global__ void zc_sigma_partials(SigmaArgs a);
 __global__ void zc_window(WindowArgs a);
+template <bool MOMENTS>
 __global__ void zc_encode(EncodeArgs a);
 template <int GPW>
 __global__ void zc_place_escapes(PlaceArgs a);

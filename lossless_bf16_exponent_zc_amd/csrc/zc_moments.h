@@ -19,6 +19,46 @@ __device__ __forceinline__ double tree8(double (&v)[8]) {
     return v[0];
 }
 
+// fp64 value of the BF16 pattern in the high / low half of a word.
+__device__ __forceinline__ double bf16_hi(uint32_t w) {
+    return (double)__uint_as_float(w & 0xFFFF0000u);
+}
+__device__ __forceinline__ double bf16_lo(uint32_t w) {
+    return (double)__uint_as_float(w << 16);
+}
+
+// Moments of 8 consecutive values (one 16-byte word).  Values at or past n
+// are zero; an Inf or NaN among them is replaced by +0.0 and not counted.
+__device__ __forceinline__ void moments8(const u32x4 w, uint64_t base, uint64_t n, double& s1,
+                                         double& s2, uint32_t& cnt) {
+    double v[8], q[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        v[2 * m] = bf16_lo(w[m]);
+        v[2 * m + 1] = bf16_hi(w[m]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = v[i] * v[i];
+    s1 = tree8(v);
+    s2 = tree8(q);
+    cnt = base >= n ? 0u : (n - base >= 8 ? 8u : (uint32_t)(n - base));
+    if (!__builtin_isfinite(s2)) {  // rare: redo without the non-finite values
+        cnt = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t d = w[i >> 1];
+            const float f = __uint_as_float((i & 1) ? (d & 0xFFFF0000u) : (d << 16));
+            const bool ok = __builtin_isfinite(f) && base + i < n;
+            v[i] = ok ? (double)f : 0.0;
+            q[i] = v[i] * v[i];
+            cnt += ok ? 1u : 0u;
+        }
+        s1 = tree8(v);
+        s2 = tree8(q);
+    }
+}
+
+
 __device__ __forceinline__ double make_f64(uint32_t lo, uint32_t hi) {
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
@@ -81,50 +121,77 @@ __device__ __forceinline__ uint32_t window_from_variance(double var) {
 struct MomentScratch {  // LDS for one workgroup's reduction
     double v1[16], v2[16];
     unsigned long long n[16];
-    double r1[64], r2[64];
+    double r1[512], r2[512];
 };
 
+// The reduction below runs on 256 threads; a round covers T*m leaves
+// (T <= 256 threads, m <= 16 leaves each).  The encoder stores block b's
+// moments at the slot where the round's loads are lane-consecutive.
+constexpr uint32_t kReduceThreads = 256;
+
+struct LeafOrder {
+    uint32_t lt, lm;  // log2 T, log2 m
+};
+
+__device__ __forceinline__ LeafOrder leaf_order(uint32_t B) {
+    const uint32_t lp = B <= 1 ? 0u : 32u - (uint32_t)__builtin_clz(B - 1);  // log2 P
+    const uint32_t lt = lp < 8u ? lp : 8u;
+    const uint32_t lm = lp - lt < 4u ? lp - lt : 4u;
+    return LeafOrder{lt, lm};
+}
+
+// Leaf b = (r T + t) m + i (round r, thread t, position i) lives at slot
+// r T m + i T + t.  Both lie in [0, P), P = 2^ceil(log2 B).
+__device__ __forceinline__ uint32_t leaf_slot(uint32_t b, LeafOrder o) {
+    const uint32_t lr = o.lt + o.lm;
+    const uint32_t w = b & ((1u << lr) - 1u);
+    return ((b >> lr) << lr) | ((w & ((1u << o.lm) - 1u)) << o.lt) | (w >> o.lm);
+}
+
 // Pairwise sums over B leaf partials (padded with +0.0 to P = 2^ceil(log2 B)),
-// by the whole workgroup of `nthreads` (a power of two, 64..1024) threads.
-// A round covers an aligned run of T*m leaves: thread t sums m <= 4 of them
-// pairwise (a shorter run padded with +0.0), a wave butterfly and a tree over
-// the waves join the threads.  Rounds (at most 64: 2^32 values are 2^18
-// leaves, and nthreads >= 1024 here) are joined by a last pairwise tree.  The
-// result is valid in thread 0.  Contains __syncthreads: call from uniform
-// control flow only.
-__device__ __forceinline__ void reduce_partials(const Partial* pp, uint32_t B, uint32_t nthreads,
+// by a workgroup of kReduceThreads threads.  A round covers an aligned run
+// of T*m leaves: thread t sums m <= 16 of them pairwise (a shorter run
+// padded with +0.0), a wave butterfly and a tree over the waves join the
+// threads.  Rounds (at most 512: a segment has fewer than 2^32 values, 2^21
+// leaves of 2048, and T*m = 4096 when there are several rounds) are joined
+// by a last pairwise tree.  Inputs at leaf slots (leaf_slot), so each load
+// instruction reads consecutive slots.  The result is valid in thread 0.
+// Contains __syncthreads: call from uniform control flow only.
+__device__ __forceinline__ void reduce_partials(const double* ps1, const double* ps2,
+                                                const uint32_t* pn, uint32_t B,
                                                 MomentScratch& sh, double& s1, double& s2,
                                                 uint64_t& n) {
     const uint32_t tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-    const uint32_t nw = nthreads / 64;
-    uint32_t P = 1;
-    while (P < B) P <<= 1;
-    uint32_t T, m, rounds;
-    if (P <= 4 * nthreads) {
-        T = P < nthreads ? P : nthreads;
-        m = P / T;
-        rounds = 1;
-    } else {
-        T = nthreads;
-        m = 4;
-        rounds = P / (4 * nthreads);
-    }
+    constexpr uint32_t nw = kReduceThreads / 64;
+    const LeafOrder o = leaf_order(B);
+    const uint32_t T = 1u << o.lt, m = 1u << o.lm;
+    const uint32_t rounds = (B <= 1 ? 1u : (1u << (32 - __builtin_clz(B - 1)))) >> (o.lt + o.lm);
     uint64_t nn = 0;
     for (uint32_t r = 0; r < rounds; ++r) {
         double r1 = 0.0, r2 = 0.0;
-        uint32_t rn = 0;  // at most 4 * 16384 values per thread and round
+        uint32_t rn = 0;  // at most 16 * 16384 values per thread and round
         if (tid < T) {
-            double v1[4], v2[4];
+            double v1[16], v2[16];
 #pragma unroll
-            for (uint32_t i = 0; i < 4; ++i) {
+            for (uint32_t i = 0; i < 16; ++i) {  // all loads issued before use
                 const uint32_t leaf = (r * T + tid) * m + i;
                 const bool ok = i < m && leaf < B;
-                v1[i] = ok ? pp[leaf].s1 : 0.0;
-                v2[i] = ok ? pp[leaf].s2 : 0.0;
-                rn += ok ? pp[leaf].n : 0;
+                const uint32_t slot = (r * T * m) + (i < m ? i : 0u) * T + tid;  // < P
+                const double a1 = ps1[slot], a2 = ps2[slot];
+                const uint32_t an = pn[slot];
+                v1[i] = ok ? a1 : 0.0;
+                v2[i] = ok ? a2 : 0.0;
+                rn += ok ? an : 0u;
             }
-            r1 = (v1[0] + v1[1]) + (v1[2] + v1[3]);
-            r2 = (v2[0] + v2[1]) + (v2[2] + v2[3]);
+#pragma unroll
+            for (uint32_t h = 1; h < 16; h <<= 1)
+#pragma unroll
+                for (uint32_t i = 0; i < 16; i += 2 * h) {
+                    v1[i] = v1[i] + v1[i + h];
+                    v2[i] = v2[i] + v2[i + h];
+                }
+            r1 = v1[0];
+            r2 = v2[0];
         }
         r1 = wave_tree(r1);
         r2 = wave_tree(r2);
@@ -147,13 +214,18 @@ __device__ __forceinline__ void reduce_partials(const Partial* pp, uint32_t B, u
         }
         __syncthreads();
     }
-    if (wave == 0) {  // the wave joins the rounds: a 64-leaf tree
-        double t1 = lane < rounds ? sh.r1[lane] : 0.0, t2 = lane < rounds ? sh.r2[lane] : 0.0;
-        t1 = wave_tree(t1);
-        t2 = wave_tree(t2);
+    if (wave == 0) {  // the wave joins the rounds: lane l the 8 rounds 8l .. 8l+7, then the lanes
+        double t1[8], t2[8];
+#pragma unroll
+        for (uint32_t i = 0; i < 8; ++i) {
+            const uint32_t j = 8 * lane + i;
+            t1[i] = j < rounds ? sh.r1[j] : 0.0;
+            t2[i] = j < rounds ? sh.r2[j] : 0.0;
+        }
+        const double u1 = wave_tree(tree8(t1)), u2 = wave_tree(tree8(t2));
         if (lane == 0) {
-            s1 = t1;
-            s2 = t2;
+            s1 = u1;
+            s2 = u2;
             n = nn;
         }
     }
