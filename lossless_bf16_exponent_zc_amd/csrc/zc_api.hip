@@ -89,6 +89,8 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     ea.gcnt = ws_ptr<uint32_t>(p, d_ws, p->ws.gcnt);
     ea.block_elems = p->block;
     ea.forced_L = forced_L;
+    ea.single = p->nseg == 1;
+    ea.seg0 = p->segs[0];
     if (nwg) {
         if (forced_L) hipLaunchKernelGGL((zc_encode<false>), dim3(nwg), dim3(256), 0, stream, ea);
         else hipLaunchKernelGGL((zc_encode<true>), dim3(nwg), dim3(256), 0, stream, ea);
@@ -100,7 +102,8 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     uint8_t* staging = ea.staging;
     uint32_t* gcnt = ea.gcnt;
     if (nchunks(p)) {
-        PlaceArgs pa{p->d_segs, p->d_chunks, out, staging, gcnt, p->chunk, nchunks(p)};
+        PlaceArgs pa{p->d_segs, p->d_chunks, out, staging, gcnt, p->chunk, nchunks(p),
+                     p->nseg == 1, p->segs[0]};
         const uint32_t gpc = p->chunk / kGroup;
         // placement: up to 4 waves, each with gpc / waves groups
         const uint32_t pw = gpc < 4 ? gpc : 4;
@@ -275,6 +278,8 @@ zc_status zc_decompress(const zc_plan* p, const void* d_in, uint64_t in_capacity
     DecodeArgs a{};
     a.segs = p->d_segs;
     a.groups = p->d_groups;
+    a.single = p->nseg == 1;
+    a.seg0 = p->segs[0];
     a.in[0] = static_cast<const uint8_t*>(d_in);
     a.capacity = in_capacity;
     a.nstreams = 1;
@@ -299,6 +304,8 @@ zc_status zc_decompress_reduce(const zc_plan* p, const void* const* d_streams, u
     DecodeArgs a{};
     a.segs = p->d_segs;
     a.groups = p->d_groups;
+    a.single = p->nseg == 1;
+    a.seg0 = p->segs[0];
     for (uint32_t s = 0; s < nstreams; ++s) a.in[s] = static_cast<const uint8_t*>(d_streams[s]);
     a.capacity = stream_capacity;
     a.nstreams = nstreams;

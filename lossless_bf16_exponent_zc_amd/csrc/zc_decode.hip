@@ -134,7 +134,11 @@ struct GroupData {
 };
 
 // Issue the loads of group g of stream st (cap readable bytes).  Plane words
-// and sm bytes are only read when the buffer holds the fixed regions.
+// and sm bytes are only read when the buffer holds the fixed regions.  EARLY:
+// the table words go out with them (one round of loads fewer; the fused
+// reduce, which holds a second stream's loads meanwhile, reads them after the
+// header check instead, to stay within its registers).
+template <bool EARLY>
 __device__ __forceinline__ void fetch(const uint8_t* st, uint64_t cap, const SegDesc& sd,
                                       uint32_t C, uint32_t g, uint32_t lane, GroupData& d) {
     const bool fixed_ok = cap >= sd.esc_off;
@@ -145,26 +149,40 @@ __device__ __forceinline__ void fetch(const uint8_t* st, uint64_t cap, const Seg
 #pragma unroll
     for (int k = 0; k < 4; ++k) d.sm[k] = fixed_ok ? ld<u32x2>(sw + 512 * k) : u32x2{0, 0};
 
+    // header and table words, loaded with the fixed regions (every offset
+    // here lies before esc_off, inside the buffer when fixed_ok), checked after
+    const uint32_t gpc = C / kGroup, k = g / gpc;
+    const uint32_t* table = reinterpret_cast<const uint32_t*>(st + kHeaderBytes);
+    const uint16_t* gtab = reinterpret_cast<const uint16_t*>(st + sd.gtab_off);
+    const bool last_in_chunk = (g + 1) % gpc == 0 || g + 1 == sd.g;
+    uint32_t t0 = 0, t1 = 0, rel = 0, rel1 = 0;
+    if (EARLY && fixed_ok) {
+        t0 = table[k];
+        t1 = table[k + 1];
+        rel = gtab[g];
+        rel1 = gtab[last_in_chunk ? g : g + 1];
+    }
     d.bad = check_header(st, cap, sd, C);
     d.L = d.t0 = d.rel = d.span = 0;
     if (!d.bad) {
-        const uint32_t gpc = C / kGroup, k = g / gpc;
-        const uint32_t* table = reinterpret_cast<const uint32_t*>(st + kHeaderBytes);
-        const uint16_t* gtab = reinterpret_cast<const uint16_t*>(st + sd.gtab_off);
+        if (!EARLY) {
+            t0 = table[k];
+            t1 = table[k + 1];
+            rel = gtab[g];
+            rel1 = gtab[last_in_chunk ? g : g + 1];
+        }
         const uint64_t E = ld<uint64_t>(st + 24);
         d.L = st[6];
-        d.t0 = table[k];
-        const uint32_t t1 = table[k + 1];
-        d.rel = gtab[g];
-        const bool last_in_chunk = (g + 1) % gpc == 0 || g + 1 == sd.g;
-        const uint32_t next = last_in_chunk ? t1 - d.t0 : gtab[g + 1];
-        if (d.t0 > t1 || t1 > E || (k == 0 && d.t0 != 0) || (k + 1 == sd.k && t1 != E) ||
-            (g % gpc == 0 && d.rel != 0))
+        d.t0 = t0;
+        d.rel = rel;
+        const uint32_t next = last_in_chunk ? t1 - t0 : rel1;
+        if (t0 > t1 || t1 > E || (k == 0 && t0 != 0) || (k + 1 == sd.k && t1 != E) ||
+            (g % gpc == 0 && rel != 0))
             d.bad |= kBadTable;
-        else if (d.rel > next || next > t1 - d.t0)
+        else if (rel > next || next > t1 - t0)
             d.bad |= kBadCount;
         else
-            d.span = next - d.rel;
+            d.span = next - rel;
     }
 }
 
@@ -233,7 +251,7 @@ __device__ __forceinline__ uint32_t decode_group_all(const DecodeArgs& a, const 
     uint64_t cap;
     const uint8_t* st = stream_of(0, cap);
     GroupData cur;
-    fetch(st, cap, sd, a.chunk_elems, g, lane, cur);
+    fetch<!REDUCE>(st, cap, sd, a.chunk_elems, g, lane, cur);
     for (uint32_t s = 0; s < a.nstreams; ++s) {
         // escape bytes of this stream, then the next stream's loads
         uint32_t first = 0;
@@ -243,7 +261,7 @@ __device__ __forceinline__ uint32_t decode_group_all(const DecodeArgs& a, const 
         const uint8_t* nst = nullptr;
         if (REDUCE && s + 1 < a.nstreams) {
             nst = stream_of(s + 1, ncap);
-            fetch(nst, ncap, sd, a.chunk_elems, g, lane, nxt);
+            fetch<!REDUCE>(nst, ncap, sd, a.chunk_elems, g, lane, nxt);
         }
 
         uint32_t bad = cur.bad;
@@ -309,8 +327,11 @@ __device__ __forceinline__ void decode_kernel(const DecodeArgs& a) {
     const uint32_t lane = lane_id(), wave = wave_id();
     const uint32_t gg = blockIdx.x * 4 + wave;
     if (gg >= a.ngroups) return;
-    const ItemDesc gd = a.groups[gg];
-    const SegDesc sd = a.segs[gd.seg];
+    // (the fused reduce takes the descriptor from memory: the argument copy
+    // costs it registers it does not have)
+    const bool single = !REDUCE && a.single;
+    const ItemDesc gd = single ? ItemDesc{0u, gg} : a.groups[gg];
+    const SegDesc sd = single ? a.seg0 : a.segs[gd.seg];
     const uint32_t g = gd.local;
     const uint32_t bad = (uint64_t)kGroup * (g + 1) > sd.n
                              ? decode_group_all<REDUCE, true>(a, sd, g, lane, s_esc[wave], s_row[wave][lane])

@@ -55,7 +55,7 @@ __device__ __forceinline__ void store_run(uint8_t* dst, const uint32_t* src, uin
 
 template <bool MOMENTS>
 __global__ __launch_bounds__(256) void zc_encode(EncodeArgs a) {
-    const ItemDesc first = a.pairs[blockIdx.x * 4];
+    const ItemDesc first = a.single ? ItemDesc{0u, 4 * blockIdx.x} : a.pairs[blockIdx.x * 4];
     const uint32_t L = a.forced_L ? a.forced_L : predicted_L(a.stats[first.seg].L);
     encode_wg<MOMENTS>(a, blockIdx.x, L);
     if (first.local == 0 && threadIdx.x == 0) {  // the segment's first item
@@ -78,8 +78,8 @@ __device__ __forceinline__ void place_chunk(const PlaceArgs& a, uint32_t ci) {
     __shared__ u32x4 s_buf[kBuf / 16];
     __shared__ uint32_t s_gb[32], s_gn[32], s_prefix, s_t;  // group offsets in the chunk, counts
     const uint32_t lane = lane_id(), wave = wave_id(), nw = blockDim.x >> 6;
-    const ItemDesc cd = a.chunks[ci];
-    const SegDesc sd = a.segs[cd.seg];
+    const ItemDesc cd = a.single ? ItemDesc{0u, ci} : a.chunks[ci];
+    const SegDesc sd = a.single ? a.seg0 : a.segs[cd.seg];
     uint8_t* st = a.out + sd.out_off;
     const uint32_t gpc = a.chunk_elems / kGroup;
     const uint64_t gc0 = (uint64_t)cd.local * gpc;  // the chunk's first group in the segment

@@ -60,31 +60,63 @@ __device__ __forceinline__ void exponent_bytes(const u32x4 (&w)[4], uint32_t (&Q
     }
 }
 
-// Moments of one group (the wave's LDS area holds its 2048 values in index
-// order; lane l takes values 32l .. 32l + 31): per lane the 8-value trees of
-// its four runs joined as (r0 + r1) + (r2 + r3), then the lane butterfly.
-// One run at a time, to keep the fp64 temporaries of a single run live.
-__device__ __forceinline__ void group_moments(const u32x4* area, uint32_t lane, uint64_t base,
-                                              uint64_t n, double& g1, double& g2, uint32_t& gn) {
-    double e1 = 0.0, e2 = 0.0, c1 = 0.0, c2 = 0.0;
-    uint32_t cnt = 0;
-#pragma unroll 1
-    for (uint32_t t = 0; t < 4; ++t) {
-        double r1, r2;
-        uint32_t c;
-        moments8(area[4 * lane + t], base + 8 * t, n, r1, r2, c);
-        cnt += c;
-        if (t & 1) {  // uniform
-            const double p1 = e1 + r1, p2 = e2 + r2;
-            c1 = t == 1 ? p1 : c1 + p1;
-            c2 = t == 1 ? p2 : c2 + p2;
-        } else {
-            e1 = r1;
-            e2 = r2;
-        }
+// Slot of 16-byte unit u of a wave's transpose area: an XOR swizzle that
+// keeps both the tile-order writes (lane j: units 64k + j) and the run-order
+// reads (lane l: units 4l + t) free of LDS bank conflicts.
+__device__ __forceinline__ uint32_t tslot(uint32_t u) { return u ^ ((u >> 2) & 15u); }
+
+// Moments of 8 consecutive values, all of them real (index < n) and finite
+// or not: the tree8 sums of v and v^2, with the first level of the squares
+// as one fused multiply-add (v^2 of a BF16 value is exact in fp64, so
+// fma(b, b, a*a) rounds a^2 + b^2 once, as the add of the two squares does).
+__device__ __forceinline__ void moments8_full(const u32x4 w, double& s1, double& s2) {
+    double v[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        v[2 * m] = bf16_lo(w[m]);
+        v[2 * m + 1] = bf16_hi(w[m]);
     }
-    g1 = wave_tree(c1);
-    g2 = wave_tree(c2);
+    double a[4], q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = v[2 * i] + v[2 * i + 1];
+        q[i] = __builtin_fma(v[2 * i + 1], v[2 * i + 1], v[2 * i] * v[2 * i]);
+    }
+    s1 = (a[0] + a[1]) + (a[2] + a[3]);
+    s2 = (q[0] + q[1]) + (q[2] + q[3]);
+}
+
+// Moments of one group (the wave's LDS area holds its 2048 values in index
+// order at tslot units; lane l takes values 32l .. 32l + 31): per lane the
+// 8-value trees of its four runs joined as (r0 + r1) + (r2 + r3), then the
+// lane butterfly.  The runs are taken one after the other (scheduling
+// barriers between them keep only one run's fp64 temporaries live).  A full
+// group (all values < n) with only finite values needs no count; otherwise
+// moments8 takes the run again, with values past n and non-finite ones
+// left out.
+__device__ __forceinline__ void run_moments(const u32x4* area, uint32_t lane, uint32_t t,
+                                            uint64_t base, uint64_t n, bool full, double& r1,
+                                            double& r2, uint32_t& cnt) {
+    const u32x4 w = area[tslot(4 * lane + t)];
+    uint32_t c = 8;
+    moments8_full(w, r1, r2);
+    if (!full || !__builtin_isfinite(r2)) moments8(w, base + 8 * t, n, r1, r2, c);
+    cnt += c;
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void group_moments(const u32x4* area, uint32_t lane, uint64_t base,
+                                              uint64_t n, bool full, double& g1, double& g2,
+                                              uint32_t& gn) {
+    uint32_t cnt = 0;
+    double a1, a2, b1, b2;
+    run_moments(area, lane, 0, base, n, full, a1, a2, cnt);
+    run_moments(area, lane, 1, base, n, full, b1, b2, cnt);
+    const double h1 = a1 + b1, h2 = a2 + b2;
+    run_moments(area, lane, 2, base, n, full, a1, a2, cnt);
+    run_moments(area, lane, 3, base, n, full, b1, b2, cnt);
+    g1 = wave_tree(h1 + (a1 + b1));
+    g2 = wave_tree(h2 + (a2 + b2));
     gn = wave_sum(cnt);
 }
 
@@ -117,10 +149,12 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
     u32x4* rowp = s_area[wave] + 2 * lane;  // the lane's exponent row
     uint8_t* ew = area + 2048;              // the wave's packed escapes
     const uint32_t* ew32 = reinterpret_cast<const uint32_t*>(ew);
-    const ItemDesc first = a.pairs[wg * 4];  // a live entry: its segment is the workgroup's
-    const ItemDesc it = a.pairs[wg * 4 + wave];
+    // the workgroup's first entry is live: its segment is the workgroup's
+    const ItemDesc first = a.single ? ItemDesc{0u, 4 * wg} : a.pairs[wg * 4];
+    const SegDesc sd = a.single ? a.seg0 : a.segs[first.seg];
+    const ItemDesc it = a.single ? ItemDesc{4 * wg + wave < (sd.g + 1) / 2 ? 0u : 0xFFFFFFFFu, 4 * wg + wave}
+                                 : a.pairs[wg * 4 + wave];
     const bool live = it.seg != 0xFFFFFFFFu;
-    const SegDesc sd = a.segs[first.seg];
     const uint64_t g0 = 2ull * it.local;
     u32x4 w[2][4];
 #pragma unroll
@@ -143,10 +177,10 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
             if (g >= sd.g) break;  // uniform
             if (MOMENTS) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) s_area[wave][64 * k + lane] = w[q][k];
+                for (int k = 0; k < 4; ++k) s_area[wave][tslot(64 * k + lane)] = w[q][k];
                 __builtin_amdgcn_wave_barrier();
                 group_moments(s_area[wave], lane, (uint64_t)kGroup * g + 32u * lane, sd.n,
-                              m1[q], m2[q], mn[q]);
+                              (uint64_t)kGroup * (g + 1) <= sd.n, m1[q], m2[q], mn[q]);
                 __builtin_amdgcn_wave_barrier();  // before the area is reused
             }
             uint32_t P[3];

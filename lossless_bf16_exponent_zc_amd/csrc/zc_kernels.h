@@ -18,6 +18,8 @@ struct EncodeArgs {
     uint32_t* gcnt;         // per group: its escape count
     uint32_t block_elems;   // moment block (16,384 values, or the chunk if smaller)
     uint32_t forced_L;      // nonzero: this window for every segment, no moments
+    uint32_t single;        // one segment: seg0 is it, items are (0, index)
+    SegDesc seg0;
 };
 
 struct WindowArgs {
@@ -37,6 +39,8 @@ struct PlaceArgs {
     const uint32_t* gcnt;
     uint32_t chunk_elems;
     uint32_t nchunks;
+    uint32_t single;        // one segment: seg0 is it, chunk i is (0, i)
+    SegDesc seg0;
 };
 
 struct DecodeArgs {
@@ -49,6 +53,8 @@ struct DecodeArgs {
     uint32_t ngroups;
     uint16_t* out;
     uint32_t* status;                // per group
+    uint32_t single;                 // one segment: seg0 is it, group i is (0, i)
+    SegDesc seg0;
 };
 
 __global__ void zc_window(WindowArgs a);

@@ -130,9 +130,9 @@ __device__ __forceinline__ void place_offsets(const WindowArgs& a, const SegDesc
 __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
     __shared__ MomentScratch s_mom;
     __shared__ uint32_t s_L, s_last;
-    const ItemDesc wi = a.items[blockIdx.x];
+    const ItemDesc wi = a.enc.single ? ItemDesc{0u, blockIdx.x} : a.items[blockIdx.x];
     const uint32_t seg = wi.seg, r = wi.local;
-    const SegDesc sd = a.enc.segs[seg];
+    const SegDesc sd = a.enc.single ? a.enc.seg0 : a.enc.segs[seg];
     uint8_t* st = a.enc.out + sd.out_off;
     const uint32_t forced = a.enc.forced_L;
     // workgroup 0 counts the chunks' escapes at once (loads beside the
