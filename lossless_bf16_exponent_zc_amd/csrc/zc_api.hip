@@ -85,6 +85,7 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     ea.part.esc = ws_ptr<uint32_t>(p, d_ws, p->ws.pesc);
     ea.pred = ws_ptr<uint32_t>(p, d_ws, p->ws.pred);
     ea.done = ws_ptr<uint32_t>(p, d_ws, p->ws.done);
+    ea.zero = ws_ptr<uint32_t>(p, d_ws, p->ws.zero);
     ea.staging = ws_ptr<uint8_t>(p, d_ws, p->ws.staging);
     ea.gcnt = ws_ptr<uint32_t>(p, d_ws, p->ws.gcnt);
     ea.block_elems = p->block;
@@ -206,6 +207,7 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
     p->ws.gcnt = o;     o += a256(4 * G);
     p->ws.pred = o;     o += a256(4ull * num_segments);
     p->ws.done = o;     o += a256(4ull * num_segments);
+    p->ws.zero = o;     o += 256;
     p->ws.staging = o;  o += a256((uint64_t)kGroup * G + 16);
     p->ws.total = o;
 

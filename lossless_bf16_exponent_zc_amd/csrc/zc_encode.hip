@@ -58,6 +58,7 @@ __global__ __launch_bounds__(256) void zc_encode(EncodeArgs a) {
     const ItemDesc first = a.single ? ItemDesc{0u, 4 * blockIdx.x} : a.pairs[blockIdx.x * 4];
     const uint32_t L = a.forced_L ? a.forced_L : predicted_L(a.stats[first.seg].L);
     encode_wg<MOMENTS>(a, blockIdx.x, L);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.zero = 0u;
     if (first.local == 0 && threadIdx.x == 0) {  // the segment's first item
         a.pred[first.seg] = L;
         a.done[first.seg] = 0;
@@ -87,6 +88,13 @@ __device__ __forceinline__ void place_chunk(const PlaceArgs& a, uint32_t ci) {
     const uint32_t* slot0 = reinterpret_cast<const uint32_t*>(a.staging) +
                             (uint64_t)(sd.group_base + gc0) * (kGroup / 4);
 
+    // the chunk's escape offset (chunk table, written from the group counts
+    // before this kernel runs) and the group counts go out first: the scan
+    // waits only for them, not for the staging loads behind them
+    const uint32_t l = cd.local;
+    const uint32_t prefix = reinterpret_cast<const uint32_t*>(st + kHeaderBytes)[l];
+    const uint32_t c_raw = a.gcnt[sd.group_base + gc0 + min(lane, ng - 1)];
+
     // source dwords of this wave's groups, loaded once (inside the slots); the
     // next dword of each comes from the next lane, lane 63's from the next
     // round or, for the last round, from one scalar load
@@ -101,20 +109,8 @@ __device__ __forceinline__ void place_chunk(const PlaceArgs& a, uint32_t ci) {
         for (int r = 0; r < R; ++r) lo[q][r] = s32[lane + 64 * r];
         past[q] = s32[64 * R];  // wave-uniform address
     }
-#pragma unroll
-    for (int q = 0; q < GPW; ++q)
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint32_t nxt = r + 1 < R ? readlane(lo[q][r + 1 < R ? r + 1 : r], 0) : past[q];
-            const uint32_t sh = dpp<kDppWaveShl1>(lo[q][r]);
-            hi[q][r] = lane == 63 ? nxt : sh;
-        }
-    // the chunk's escape offset comes from the chunk table (written from the
-    // group counts before this kernel runs)
-    const uint32_t l = cd.local;
-    const uint32_t prefix = reinterpret_cast<const uint32_t*>(st + kHeaderBytes)[l];
     if (wave == 0) {
-        const uint32_t c = lane < ng ? a.gcnt[sd.group_base + gc0 + lane] : 0u;
+        const uint32_t c = lane < ng ? c_raw : 0u;
         const uint32_t incl = wave_inclusive_scan(c);
         if (lane < ng) {
             reinterpret_cast<uint16_t*>(st + sd.gtab_off)[gc0 + lane] = (uint16_t)(incl - c);
@@ -130,6 +126,14 @@ __device__ __forceinline__ void place_chunk(const PlaceArgs& a, uint32_t ci) {
         }
     }
     lds_barrier();
+#pragma unroll
+    for (int q = 0; q < GPW; ++q)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t nxt = r + 1 < R ? readlane(lo[q][r + 1 < R ? r + 1 : r], 0) : past[q];
+            const uint32_t sh = dpp<kDppWaveShl1>(lo[q][r]);
+            hi[q][r] = lane == 63 ? nxt : sh;
+        }
     const uint32_t pre = s_prefix, t = s_t;
     if (pre == 0xFFFFFFFFu) {
         lds_barrier();  // s_* are rewritten by the next chunk

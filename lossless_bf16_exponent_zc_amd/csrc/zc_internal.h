@@ -80,6 +80,7 @@ struct WsLayout {
     uint64_t gcnt;      // u32 per group: escape count
     uint64_t pred;      // u32 per segment: the window of the first encoder pass
     uint64_t done;      // u32 per segment: window workgroups done re-coding
+    uint64_t zero;      // u32: zero (written by the encoder's first pass)
     uint64_t staging;   // 2048 bytes per group (+16): escape exponents before placement
     uint64_t total;
 };

@@ -14,6 +14,7 @@ struct EncodeArgs {
     Partials part;          // per block: escape count; with moments, the moments
     uint32_t* pred;         // per segment: the window the first pass used
     uint32_t* done;         // per segment: window workgroups done re-coding (first pass clears)
+    uint32_t* zero;         // one word the first pass sets to 0 (a target for masked loads)
     uint8_t* staging;       // 2048 bytes per group (+16): the group's escape exponents
     uint32_t* gcnt;         // per group: its escape count
     uint32_t block_elems;   // moment block (16,384 values, or the chunk if smaller)

@@ -156,65 +156,87 @@ __device__ __forceinline__ uint32_t leaf_slot(uint32_t b, LeafOrder o) {
 // leaves of 2048, and T*m = 4096 when there are several rounds) are joined
 // by a last pairwise tree.  Inputs at leaf slots (leaf_slot), so each load
 // instruction reads consecutive slots.  The result is valid in thread 0.
-// Contains __syncthreads: call from uniform control flow only.
-__device__ __forceinline__ void reduce_partials(const double* ps1, const double* ps2,
-                                                const uint32_t* pn, uint32_t B,
-                                                MomentScratch& sh, double& s1, double& s2,
-                                                uint64_t& n) {
+// The round's loads (load_round) can be issued ahead of other work;
+// finish_round and reduce_partials contain __syncthreads: call them from
+// uniform control flow only.
+struct ReduceShape {
+    LeafOrder o;
+    uint32_t T, m, rounds;
+};
+
+__device__ __forceinline__ ReduceShape reduce_shape(uint32_t B) {
+    ReduceShape r;
+    r.o = leaf_order(B);
+    r.T = 1u << r.o.lt;
+    r.m = 1u << r.o.lm;
+    r.rounds = (B <= 1 ? 1u : (1u << (32 - __builtin_clz(B - 1)))) >> (r.o.lt + r.o.lm);
+    return r;
+}
+
+struct RoundLoads {  // raw loads; leaves past B are masked when the round is finished
+    double v1[16], v2[16];
+    uint32_t n[16];
+};
+
+__device__ __forceinline__ void load_round(const double* ps1, const double* ps2, const uint32_t* pn,
+                                           uint32_t B, const ReduceShape& sh, uint32_t r,
+                                           RoundLoads& L) {
+    const uint32_t tid = threadIdx.x, T = sh.T, m = sh.m;
+#pragma unroll
+    for (uint32_t i = 0; i < 16; ++i) {  // loads only: nothing here waits for them
+        const uint32_t slot = (r * T * m) + (i < m ? i : 0u) * T + (tid < T ? tid : 0u);  // < P
+        L.v1[i] = ps1[slot];
+        L.v2[i] = ps2[slot];
+        L.n[i] = pn[slot];
+    }
+}
+
+__device__ __forceinline__ void finish_round(RoundLoads& L, uint32_t B, const ReduceShape& shp,
+                                             uint32_t r, MomentScratch& sh, uint64_t& nn) {
     const uint32_t tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     constexpr uint32_t nw = kReduceThreads / 64;
-    const LeafOrder o = leaf_order(B);
-    const uint32_t T = 1u << o.lt, m = 1u << o.lm;
-    const uint32_t rounds = (B <= 1 ? 1u : (1u << (32 - __builtin_clz(B - 1)))) >> (o.lt + o.lm);
-    uint64_t nn = 0;
-    for (uint32_t r = 0; r < rounds; ++r) {
-        double r1 = 0.0, r2 = 0.0;
-        uint32_t rn = 0;  // at most 16 * 16384 values per thread and round
-        if (tid < T) {
-            double v1[16], v2[16];
+    uint32_t rn = 0;  // at most 16 * 16384 values per thread and round
 #pragma unroll
-            for (uint32_t i = 0; i < 16; ++i) {  // all loads issued before use
-                const uint32_t leaf = (r * T + tid) * m + i;
-                const bool ok = i < m && leaf < B;
-                const uint32_t slot = (r * T * m) + (i < m ? i : 0u) * T + tid;  // < P
-                const double a1 = ps1[slot], a2 = ps2[slot];
-                const uint32_t an = pn[slot];
-                v1[i] = ok ? a1 : 0.0;
-                v2[i] = ok ? a2 : 0.0;
-                rn += ok ? an : 0u;
-            }
-#pragma unroll
-            for (uint32_t h = 1; h < 16; h <<= 1)
-#pragma unroll
-                for (uint32_t i = 0; i < 16; i += 2 * h) {
-                    v1[i] = v1[i] + v1[i + h];
-                    v2[i] = v2[i] + v2[i + h];
-                }
-            r1 = v1[0];
-            r2 = v2[0];
-        }
-        r1 = wave_tree(r1);
-        r2 = wave_tree(r2);
-        rn = wave_sum(rn);
-        if (lane == 0) {
-            sh.v1[wave] = r1;
-            sh.v2[wave] = r2;
-            sh.n[wave] = rn;
-        }
-        __syncthreads();
-        if (wave == 0) {  // lanes 0..15 join the waves' sums: a 16-leaf butterfly
-            double t1 = lane < nw ? sh.v1[lane] : 0.0, t2 = lane < nw ? sh.v2[lane] : 0.0;
-            t1 = row_tree(t1);
-            t2 = row_tree(t2);
-            if (lane == 0) {
-                sh.r1[r] = t1;
-                sh.r2[r] = t2;
-                for (uint32_t i = 0; i < nw; ++i) nn += sh.n[i];
-            }
-        }
-        __syncthreads();
+    for (uint32_t i = 0; i < 16; ++i) {
+        const uint32_t leaf = (r * shp.T + tid) * shp.m + i;
+        const bool ok = tid < shp.T && i < shp.m && leaf < B;
+        L.v1[i] = ok ? L.v1[i] : 0.0;
+        L.v2[i] = ok ? L.v2[i] : 0.0;
+        rn += ok ? L.n[i] : 0u;
     }
-    if (wave == 0) {  // the wave joins the rounds: lane l the 8 rounds 8l .. 8l+7, then the lanes
+#pragma unroll
+    for (uint32_t h = 1; h < 16; h <<= 1)
+#pragma unroll
+        for (uint32_t i = 0; i < 16; i += 2 * h) {
+            L.v1[i] = L.v1[i] + L.v1[i + h];
+            L.v2[i] = L.v2[i] + L.v2[i + h];
+        }
+    const double r1 = wave_tree(L.v1[0]), r2 = wave_tree(L.v2[0]);
+    rn = wave_sum(rn);
+    if (lane == 0) {
+        sh.v1[wave] = r1;
+        sh.v2[wave] = r2;
+        sh.n[wave] = rn;
+    }
+    __syncthreads();
+    if (wave == 0) {  // lanes 0..15 join the waves' sums: a 16-leaf butterfly
+        double t1 = lane < nw ? sh.v1[lane] : 0.0, t2 = lane < nw ? sh.v2[lane] : 0.0;
+        t1 = row_tree(t1);
+        t2 = row_tree(t2);
+        if (lane == 0) {
+            sh.r1[r] = t1;
+            sh.r2[r] = t2;
+            for (uint32_t i = 0; i < nw; ++i) nn += sh.n[i];
+        }
+    }
+    __syncthreads();
+}
+
+// The wave joins the rounds: lane l the 8 rounds 8l .. 8l+7, then the lanes.
+__device__ __forceinline__ void join_rounds(const MomentScratch& sh, uint32_t rounds, uint64_t nn,
+                                            double& s1, double& s2, uint64_t& n) {
+    const uint32_t lane = lane_id();
+    if (wave_id() == 0) {
         double t1[8], t2[8];
 #pragma unroll
         for (uint32_t i = 0; i < 8; ++i) {
@@ -229,6 +251,20 @@ __device__ __forceinline__ void reduce_partials(const double* ps1, const double*
             n = nn;
         }
     }
+}
+
+__device__ __forceinline__ void reduce_partials(const double* ps1, const double* ps2,
+                                                const uint32_t* pn, uint32_t B,
+                                                MomentScratch& sh, double& s1, double& s2,
+                                                uint64_t& n) {
+    const ReduceShape shape = reduce_shape(B);
+    uint64_t nn = 0;
+    for (uint32_t r = 0; r < shape.rounds; ++r) {
+        RoundLoads L;
+        load_round(ps1, ps2, pn, B, shape, r, L);
+        finish_round(L, B, shape, r, sh, nn);
+    }
+    join_rounds(sh, shape.rounds, nn, s1, s2, n);
 }
 
 // Population variance of the finite values from the moments: three

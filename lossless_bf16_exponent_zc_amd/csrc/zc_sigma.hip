@@ -23,11 +23,11 @@ namespace {
 
 // Chunk table, E, total size and stream size of segment sd from the moment
 // blocks' escape counts (BPC blocks per chunk), by the whole workgroup, each
-// thread a run of chunks.  chunk_counts leaves each chunk's count in its
-// table entry and returns the thread's run total; place_offsets scans the
-// runs' totals across the workgroup and replaces the counts by offsets.
-// Loads go out in batches of 32, unconditionally (indexes clamped, values
-// masked).
+// thread a run of chunks.  chunk_counts returns the thread's run total and,
+// for runs of up to 8 chunks, the chunks' counts in registers (longer runs
+// leave them in the table entries); place_offsets scans the runs' totals
+// across the workgroup and writes the offsets.  Loads go out in batches of
+// 32, unconditionally (indexes clamped, values masked).
 struct ChunkRun {
     uint32_t c0, c1;
 };
@@ -38,14 +38,43 @@ __device__ __forceinline__ ChunkRun chunk_run(const SegDesc& sd) {
     return ChunkRun{c0, min(K, c0 + per)};
 }
 
+struct ChunkCounts {
+    uint32_t c[8];
+    uint32_t run;
+    bool in_table;
+};
+
 template <uint32_t BPC>
-__device__ __forceinline__ uint32_t chunk_counts_t(const WindowArgs& a, const SegDesc& sd, uint8_t* st) {
+__device__ __forceinline__ void chunk_counts_t(const WindowArgs& a, const SegDesc& sd, uint8_t* st,
+                                               ChunkCounts& cc) {
     constexpr uint32_t U = 32 / BPC;  // chunks per batch
     const ChunkRun cr = chunk_run(sd);
     const uint32_t last = sd.nsb - 1;
     const uint32_t* pe = a.enc.part.esc + sd.sb_base;
+    cc.run = 0;
+    cc.in_table = (sd.k + blockDim.x - 1) / blockDim.x > 8;  // uniform
+    if (!cc.in_table) {
+        // entries outside the run read a word the encoder zeroed, so every
+        // load goes out unconditionally and nothing waits between them
+        uint32_t v[8][BPC];
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u)
+#pragma unroll
+            for (uint32_t j = 0; j < BPC; ++j) {
+                const uint32_t b = (cr.c0 + u) * BPC + j;
+                v[u][j] = *(cr.c0 + u < cr.c1 && b <= last ? pe + b : a.enc.zero);
+            }
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u) {
+            uint32_t t = 0;
+#pragma unroll
+            for (uint32_t j = 0; j < BPC; ++j) t += v[u][j];
+            cc.c[u] = t;
+            cc.run += t;
+        }
+        return;
+    }
     uint32_t* table = reinterpret_cast<uint32_t*>(st + kHeaderBytes);
-    uint32_t run = 0;
     for (uint32_t c = cr.c0; c < cr.c1; c += U) {
         uint32_t v[U][BPC];
 #pragma unroll
@@ -53,8 +82,7 @@ __device__ __forceinline__ uint32_t chunk_counts_t(const WindowArgs& a, const Se
 #pragma unroll
             for (uint32_t j = 0; j < BPC; ++j) {
                 const uint32_t b = (c + u) * BPC + j;
-                const uint32_t x = pe[min(b, last)];
-                v[u][j] = c + u < cr.c1 && b <= last ? x : 0u;
+                v[u][j] = *(c + u < cr.c1 && b <= last ? pe + b : a.enc.zero);
             }
 #pragma unroll
         for (uint32_t u = 0; u < U; ++u) {
@@ -62,29 +90,28 @@ __device__ __forceinline__ uint32_t chunk_counts_t(const WindowArgs& a, const Se
 #pragma unroll
             for (uint32_t j = 0; j < BPC; ++j) t += v[u][j];
             if (c + u < cr.c1) table[c + u] = t;
-            run += t;
+            cc.run += t;
         }
     }
-    return run;
 }
 
-__device__ __forceinline__ uint32_t chunk_counts(const WindowArgs& a, const SegDesc& sd,
-                                                 uint8_t* st) {
+__device__ __forceinline__ void chunk_counts(const WindowArgs& a, const SegDesc& sd, uint8_t* st,
+                                             ChunkCounts& cc) {
     switch (a.chunk_blocks) {
-        case 1: return chunk_counts_t<1>(a, sd, st);
-        case 2: return chunk_counts_t<2>(a, sd, st);
-        default: return chunk_counts_t<4>(a, sd, st);
+        case 1: chunk_counts_t<1>(a, sd, st, cc); break;
+        case 2: chunk_counts_t<2>(a, sd, st, cc); break;
+        default: chunk_counts_t<4>(a, sd, st, cc); break;
     }
 }
 
 // Contains __syncthreads.
-__device__ __forceinline__ void place_offsets(const WindowArgs& a, const SegDesc& sd, uint32_t seg, uint8_t* st,
-                              uint32_t run) {
+__device__ __forceinline__ void place_offsets(const WindowArgs& a, const SegDesc& sd, uint32_t seg,
+                                              uint8_t* st, const ChunkCounts& cc) {
     __shared__ uint32_t s_w[16], s_base;
     const uint32_t lane = lane_id(), wave = wave_id(), nw = blockDim.x >> 6;
     const ChunkRun cr = chunk_run(sd);
     uint32_t* table = reinterpret_cast<uint32_t*>(st + kHeaderBytes);
-    const uint32_t incl = wave_inclusive_scan(run);
+    const uint32_t incl = wave_inclusive_scan(cc.run);
     if (lane == 63) s_w[wave] = incl;
     __syncthreads();
     if (wave == 0) {
@@ -94,17 +121,26 @@ __device__ __forceinline__ void place_offsets(const WindowArgs& a, const SegDesc
         if (lane == 63) s_base = wi;  // E
     }
     __syncthreads();
-    uint32_t at = s_w[wave] + incl - run;
-    for (uint32_t c = cr.c0; c < cr.c1; c += 8) {
-        uint32_t t[8];
-#pragma unroll
-        for (uint32_t u = 0; u < 8; ++u) t[u] = table[min(c + u, cr.c1 - 1)];
+    uint32_t at = s_w[wave] + incl - cc.run;
+    if (!cc.in_table) {
 #pragma unroll
         for (uint32_t u = 0; u < 8; ++u)
-            if (c + u < cr.c1) {
-                table[c + u] = at;
-                at += t[u];
+            if (cr.c0 + u < cr.c1) {
+                table[cr.c0 + u] = at;
+                at += cc.c[u];
             }
+    } else {
+        for (uint32_t c = cr.c0; c < cr.c1; c += 8) {
+            uint32_t t[8];
+#pragma unroll
+            for (uint32_t u = 0; u < 8; ++u) t[u] = table[min(c + u, cr.c1 - 1)];
+#pragma unroll
+            for (uint32_t u = 0; u < 8; ++u)
+                if (c + u < cr.c1) {
+                    table[c + u] = at;
+                    at += t[u];
+                }
+        }
     }
     if (threadIdx.x == 0) {
         const uint64_t E = s_base;
@@ -135,14 +171,30 @@ __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
     const SegDesc sd = a.enc.single ? a.enc.seg0 : a.enc.segs[seg];
     uint8_t* st = a.enc.out + sd.out_off;
     const uint32_t forced = a.enc.forced_L;
-    // workgroup 0 counts the chunks' escapes at once (loads beside the
-    // moments'); the counts stand unless the prediction fails
-    const uint32_t run = r == 0 && sd.k ? chunk_counts(a, sd, st) : 0u;
+    // one round of loads: the moments' first round, and in workgroup 0 the
+    // chunks' escape counts (they stand unless the prediction fails)
+    const double* ps1 = a.enc.part.s1 + sd.sb_base;
+    const double* ps2 = a.enc.part.s2 + sd.sb_base;
+    const uint32_t* pn = a.enc.part.n + sd.sb_base;
+    const bool moments = !forced && sd.nsb;
+    const ReduceShape shape = reduce_shape(sd.nsb);
+    RoundLoads rl;
+    if (moments) load_round(ps1, ps2, pn, sd.nsb, shape, 0, rl);
+    ChunkCounts cc;
+    cc.run = 0;
+    cc.in_table = false;
+    if (r == 0 && sd.k) chunk_counts(a, sd, st, cc);
     double s1 = 0.0, s2 = 0.0;
     uint64_t n = 0;
-    if (!forced && sd.nsb)
-        reduce_partials(a.enc.part.s1 + sd.sb_base, a.enc.part.s2 + sd.sb_base,
-                        a.enc.part.n + sd.sb_base, sd.nsb, s_mom, s1, s2, n);
+    if (moments) {
+        uint64_t nn = 0;
+        finish_round(rl, sd.nsb, shape, 0, s_mom, nn);
+        for (uint32_t k = 1; k < shape.rounds; ++k) {
+            load_round(ps1, ps2, pn, sd.nsb, shape, k, rl);
+            finish_round(rl, sd.nsb, shape, k, s_mom, nn);
+        }
+        join_rounds(s_mom, shape.rounds, nn, s1, s2, n);
+    }
     if (threadIdx.x == 0) {
         const double var = forced ? 0.0 : variance(s1, s2, n);
         const uint32_t L = forced ? forced : window_from_variance(var);
@@ -171,7 +223,7 @@ __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
     const uint32_t L = s_L;
     if (sd.k == 0) return;
     if (L == a.enc.pred[seg]) {  // the prediction held (always, with a fixed window)
-        if (r == 0) place_offsets(a, sd, seg, st, run);
+        if (r == 0) place_offsets(a, sd, seg, st, cc);
         return;
     }
     for (uint32_t i = r; i < sd.nwg; i += sd.wr) encode_wg<false>(a.enc, sd.wg_base + i, L);
@@ -181,7 +233,9 @@ __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
     __syncthreads();
     if (s_last) {
         __threadfence();  // the others' reports, before their counts are read
-        place_offsets(a, sd, seg, st, chunk_counts(a, sd, st));
+        ChunkCounts c2;
+        chunk_counts(a, sd, st, c2);
+        place_offsets(a, sd, seg, st, c2);
     }
 }
 
