@@ -8,7 +8,8 @@ HBM.  Also timed: decompress-reduce of 8 shards of 33,554,432 values each.
 Prints one JSON line (see the keys below).  `value` is input GB/s of the
 round trip (2N bytes per step / step time); compress and decompress GB/s,
 their fraction of the 8 TB/s HBM peak by algorithmic bytes, and the ratio are
-extra keys.  Timed calls are cold: a 1 GiB read before each (outside the
+extra keys.  `roofline` is the encoder pass (the step's dominant kernel,
+timed by HIP events around it), `roofline_decode` the decode kernel.  Timed calls are cold: a 1 GiB read before each (outside the
 timed region) evicts the caches, so inputs come from HBM; warm times (no
 eviction) are reported beside them.  The oracle (plain C) is timed on a
 bounded sample on the host as `cpu_baseline`.
@@ -26,11 +27,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12  # bytes/s, MI355X
-# counter summary of the decode kernel on this workload (FETCH_SIZE and
-# WRITE_SIZE per dispatch, scaled by a plain copy's readings), valid while the
-# decoder's sources hash to the value recorded there
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "zc_decode_gradient64M_hbm_traffic.txt")
-DECODER_SOURCES = ["zc_decode.hip", "zc_internal.h", "zc_kernels.h"]
+# counter summary of the encoder pass and the decoder on this workload
+# (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by a plain copy's readings);
+# a kernel's figure is used while its sources hash to the value recorded there
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "zc_codec_gradient64M_hbm_traffic.txt")
+KERNEL_SOURCES = {
+    "zc_encode": ["zc_encode.hip", "zc_encoder.h", "zc_moments.h", "zc_internal.h", "zc_kernels.h"],
+    "zc_decode": ["zc_decode.hip", "zc_internal.h", "zc_kernels.h"],
+}
 
 
 def log(*a):
@@ -57,25 +61,27 @@ def timed(fn, steps, warmup, stream, flush=None):
     return [a.elapsed_time(b) * 1e-3 for a, b in evs]  # seconds
 
 
-def decoder_hash():
+def sources_hash(kernel):
     import hashlib
     h = hashlib.sha256()
-    for f in DECODER_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "lossless_bf16_exponent_zc_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed counter summary, or None
-    when the decoder has changed since it was taken."""
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (lines "traffic <kernel> <bytes> <sources sha256>"), or None when the
+    kernel's sources have changed since it was taken."""
     try:
-        kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
-        if kv.get("decoder_sources_sha256", "").strip() != decoder_hash():
-            return None
-        return int(kv["traffic_bytes_per_launch"].strip())
-    except (OSError, KeyError, ValueError):
-        return None
+        for line in open(TRAFFIC_FILE):
+            f = line.split()
+            if len(f) == 4 and f[0] == "traffic" and f[1] == kernel:
+                return int(f[2]) if f[3] == sources_hash(kernel) else None
+    except (OSError, ValueError):
+        pass
+    return None
 
 
 def cpu_baseline(x, chunk):
@@ -147,10 +153,30 @@ def main():
     tcw = timed(comp, args.steps, args.warmup, stream)
     tdw = timed(dec, args.steps, args.warmup, stream)
 
-    # algorithmic bytes: compress reads the input twice (sigma, encode) and
-    # writes the stream; decompress reads the stream and writes the values
+    # algorithmic bytes as the method is defined (a sigma pass and an encode
+    # pass each read the input, then the stream is written); this library's
+    # compress reads the input once (the moments come from the encoder's
+    # pass), so compress_hbm_frac_one_read gives the same time against
+    # input + stream.  Decompress reads the stream and writes the values.
     comp_bytes = 2 * N + 2 * N + stream_bytes
+    comp_bytes_one_read = 2 * N + stream_bytes
     dec_bytes = stream_bytes + 2 * N
+
+    # the encoder pass, timed on its own: HIP events on this stream around
+    # each kernel of a compress call (cold, like the calls above)
+    log("kernel times")
+    ku = []
+    for i in range(args.warmup + args.steps):
+        flush.sum()
+        us = plan.compress_timed(xd, out, sizes, ws)
+        if i >= args.warmup:
+            ku.append(us)
+    ku = np.median(np.array(ku), axis=0)
+    G = (N + 2047) // 2048
+    # the encoder pass moves the input in and the codes, sign+mantissa bytes
+    # and escape exponents out (the escape copy of the placement kernel is
+    # overhead)
+    enc_bytes = 2 * N + (768 + 2048) * G + E
     t_c, t_d, t_s, t_cw, t_dw = (float(np.median(v)) for v in (tc, td, ts, tcw, tdw))
     res = {
         "metric": "compress / decompress GB/s (BF16 input) + % of HBM peak; compression ratio",
@@ -173,6 +199,7 @@ def main():
         "compress_ms": round(t_c * 1e3, 4),
         "decompress_ms": round(t_d * 1e3, 4),
         "compress_hbm_frac": round(comp_bytes / t_c / HBM_PEAK, 4),
+        "compress_hbm_frac_one_read": round(comp_bytes_one_read / t_c / HBM_PEAK, 4),
         "decompress_hbm_frac": round(dec_bytes / t_d / HBM_PEAK, 4),
         "timing": "cold: caches filled by a 1 GiB read before every timed call; "
                   "medians of the timed calls",
@@ -182,16 +209,27 @@ def main():
         "decompress_ms_warm": round(t_dw * 1e3, 4),
         "ratio": round(2 * N / stream_bytes, 4),
         "escape_frac": round(E / N, 5),
+        "compress_kernels_us": {"encode": round(float(ku[0]), 2), "window": round(float(ku[1]), 2),
+                                "place_escapes": round(float(ku[2]), 2)},
+        # the dominant kernel of the step: the encoder pass (moments, codes,
+        # staged escapes), its time from HIP events around it (cold)
+        "roofline": {"bound": "hbm", "kernel": "zc_encode",
+                     "achieved": round(enc_bytes / (ku[0] * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(enc_bytes / (ku[0] * 1e-6) / HBM_PEAK, 4),
+                     # HBM bytes per launch (counters); algorithmic bytes beside it
+                     "traffic": measured_traffic("zc_encode"),
+                     "algorithmic_bytes": enc_bytes,
+                     "launch_us": round(float(ku[0]), 2)},
         # the decode kernel is the only launch of zc_decompress, so the event
         # time around the call is that kernel's launch duration
-        "roofline": {"bound": "hbm", "kernel": "zc_decode",
-                     "achieved": round(dec_bytes / t_d / 1e9, 1),
-                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(dec_bytes / t_d / HBM_PEAK, 4),
-                     # HBM bytes per launch (counters); algorithmic bytes beside it
-                     "traffic": measured_traffic(),
-                     "algorithmic_bytes": dec_bytes,
-                     "launch_us": round(t_d * 1e6, 2)},
+        "roofline_decode": {"bound": "hbm", "kernel": "zc_decode",
+                            "achieved": round(dec_bytes / t_d / 1e9, 1),
+                            "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                            "frac": round(dec_bytes / t_d / HBM_PEAK, 4),
+                            "traffic": measured_traffic("zc_decode"),
+                            "algorithmic_bytes": dec_bytes,
+                            "launch_us": round(t_d * 1e6, 2)},
     }
 
     if args.copy_ref:

@@ -113,17 +113,35 @@ uint64_t zc_plan_workspace_bytes(const zc_plan *plan);
  * The window of each segment comes from its standard deviation (fp64
  * moments by a pairwise tree, population variance of the finite values,
  * the 7-binade window of largest Gaussian mass).
+ * One pass over the input: it is coded with the window the workspace
+ * recorded for the segment on the previous call (any value on a fresh
+ * workspace) while the moments are taken; a segment whose window turns out
+ * different is coded again in the same call.  The streams are the same
+ * either way; a call after a change of window only takes longer.  Calls
+ * that share a workspace must not overlap.
  */
 zc_status zc_compress(const zc_plan *plan, const void *d_in, void *d_out,
                       uint64_t out_capacity, uint64_t *d_stream_bytes,
                       void *d_ws, uint64_t ws_bytes, hipStream_t stream);
 
 /* As zc_compress, but every segment uses the window L (1..248) given here
- * instead of one derived from its standard deviation (skips that pass). */
+ * instead of one derived from its standard deviation (no moments). */
 zc_status zc_compress_window(const zc_plan *plan, const void *d_in, void *d_out,
                              uint64_t out_capacity, uint64_t *d_stream_bytes,
                              uint32_t window_L, void *d_ws, uint64_t ws_bytes,
                              hipStream_t stream);
+
+/*
+ * For profiling: zc_compress with HIP events recorded on `stream` before,
+ * between and after its kernels; waits for the call to finish and writes
+ * the kernels' times in microseconds to us[0] (encoder pass: moments, codes,
+ * staged escapes), us[1] (window, check of the prediction, chunk table) and
+ * us[2] (escape placement).  Same output as zc_compress.
+ */
+zc_status zc_compress_timed(const zc_plan *plan, const void *d_in, void *d_out,
+                            uint64_t out_capacity, uint64_t *d_stream_bytes,
+                            void *d_ws, uint64_t ws_bytes, hipStream_t stream,
+                            float *us);
 
 /*
  * Decode every segment's stream (at d_in + zc_plan_stream_offset(s); the

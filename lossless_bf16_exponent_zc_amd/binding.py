@@ -23,7 +23,7 @@ EXPORTS = (
     "zc_plan_num_segments", "zc_plan_chunk_elems", "zc_plan_input_offset",
     "zc_plan_input_elems", "zc_plan_stream_offset", "zc_plan_max_stream_bytes",
     "zc_plan_out_bytes", "zc_plan_workspace_bytes", "zc_compress",
-    "zc_compress_window", "zc_decompress", "zc_decompress_reduce",
+    "zc_compress_window", "zc_compress_timed", "zc_decompress", "zc_decompress_reduce",
     "zc_read_status", "zc_read_sigma",
 )
 
@@ -67,13 +67,14 @@ def lib() -> ctypes.CDLL:
         f.restype = u64
     L.zc_compress.argtypes = [vp, vp, vp, u64, vp, vp, u64, vp]
     L.zc_compress_window.argtypes = [vp, vp, vp, u64, vp, u32, vp, u64, vp]
+    L.zc_compress_timed.argtypes = [vp, vp, vp, u64, vp, vp, u64, vp, P(ctypes.c_float)]
     L.zc_decompress.argtypes = [vp, vp, u64, vp, vp, u64, vp]
     L.zc_decompress_reduce.argtypes = [vp, P(vp), u32, u64, vp, vp, u64, vp]
     L.zc_read_status.argtypes = [vp, vp, vp, P(u32)]
     L.zc_read_sigma.argtypes = [vp, vp, u32, vp, P(ctypes.c_double),
                                 P(ctypes.c_double), P(u64), P(ctypes.c_double),
                                 P(u32)]
-    for name in ("zc_plan_create", "zc_compress", "zc_compress_window",
+    for name in ("zc_plan_create", "zc_compress", "zc_compress_window", "zc_compress_timed",
                  "zc_decompress", "zc_decompress_reduce", "zc_read_status",
                  "zc_read_sigma"):
         getattr(L, name).restype = ctypes.c_int
@@ -184,6 +185,17 @@ class Plan:
                                           _ptr(stream_bytes), int(window), _ptr(ws),
                                           _nbytes(ws), _stream(stream))
             _check(rc, "zc_compress_window")
+
+    def compress_timed(self, x, out, stream_bytes, ws, stream=None):
+        """Compress as compress() and wait for it; returns the three kernels'
+        times in microseconds (encoder pass, window, escape placement), from
+        HIP events recorded on the stream between them."""
+        us = (ctypes.c_float * 3)()
+        rc = lib().zc_compress_timed(self._h, _ptr(x), _ptr(out), _nbytes(out),
+                                     _ptr(stream_bytes), _ptr(ws), _nbytes(ws),
+                                     _stream(stream), us)
+        _check(rc, "zc_compress_timed")
+        return [float(v) for v in us]
 
     def decompress(self, comp, out, ws, capacity: int | None = None, stream=None):
         """Enqueue decoding of the packed streams in comp into out."""

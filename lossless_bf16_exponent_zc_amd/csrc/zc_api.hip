@@ -62,9 +62,10 @@ T* ws_ptr(const zc_plan* p, void* d_ws, uint64_t off) {
     return reinterpret_cast<T*>(static_cast<uint8_t*>(d_ws) + off);
 }
 
+// ev: null, or four events recorded on the stream around the three kernels
 zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
                         uint64_t* d_stream_bytes, uint32_t forced_L, void* d_ws, uint64_t ws_bytes,
-                        hipStream_t stream) {
+                        hipStream_t stream, hipEvent_t* ev = nullptr) {
     if (!p) return ZC_ERR_INVALID_ARG;
     if (p->input_elems && (!d_in || !aligned(d_in, 16))) return ZC_ERR_INVALID_ARG;
     if (!d_out || !aligned(d_out, 256) || !d_stream_bytes || !aligned(d_stream_bytes, 8))
@@ -92,13 +93,16 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     ea.forced_L = forced_L;
     ea.single = p->nseg == 1;
     ea.seg0 = p->segs[0];
+    if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return ZC_ERR_HIP;
     if (nwg) {
         if (forced_L) hipLaunchKernelGGL((zc_encode<false>), dim3(nwg), dim3(256), 0, stream, ea);
         else hipLaunchKernelGGL((zc_encode<true>), dim3(nwg), dim3(256), 0, stream, ea);
     }
+    if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return ZC_ERR_HIP;
     WindowArgs wa{ea, p->d_witems, ws_ptr<SegStat>(p, d_ws, p->ws.stats), d_stream_bytes,
                   p->chunk, p->chunk / p->block};
     hipLaunchKernelGGL(zc_window, dim3((uint32_t)p->witems.size()), dim3(256), 0, stream, wa);
+    if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return ZC_ERR_HIP;
     uint8_t* out = static_cast<uint8_t*>(d_out);
     uint8_t* staging = ea.staging;
     uint32_t* gcnt = ea.gcnt;
@@ -117,6 +121,7 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
             default: hipLaunchKernelGGL((zc_place_escapes<8>), pgrid, pblock, 0, stream, pa); break;
         }
     }
+    if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return ZC_ERR_HIP;
     return launch_status();
 }
 
@@ -261,6 +266,27 @@ uint64_t zc_plan_workspace_bytes(const zc_plan* p) { return p ? p->ws.total : 0;
 zc_status zc_compress(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
                       uint64_t* d_stream_bytes, void* d_ws, uint64_t ws_bytes, hipStream_t stream) {
     return compress_impl(p, d_in, d_out, out_capacity, d_stream_bytes, 0, d_ws, ws_bytes, stream);
+}
+
+zc_status zc_compress_timed(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
+                            uint64_t* d_stream_bytes, void* d_ws, uint64_t ws_bytes,
+                            hipStream_t stream, float* us) {
+    if (!us) return ZC_ERR_INVALID_ARG;
+    hipEvent_t ev[4] = {};
+    zc_status st = ZC_OK;
+    for (auto& e : ev)
+        if (hipEventCreate(&e) != hipSuccess) st = ZC_ERR_HIP;
+    if (st == ZC_OK)
+        st = compress_impl(p, d_in, d_out, out_capacity, d_stream_bytes, 0, d_ws, ws_bytes, stream, ev);
+    if (st == ZC_OK && hipEventSynchronize(ev[3]) != hipSuccess) st = ZC_ERR_HIP;
+    for (int k = 0; st == ZC_OK && k < 3; ++k) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, ev[k], ev[k + 1]) != hipSuccess) st = ZC_ERR_HIP;
+        us[k] = 1000.f * ms;
+    }
+    for (auto& e : ev)
+        if (e) (void)hipEventDestroy(e);
+    return st;
 }
 
 zc_status zc_compress_window(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,

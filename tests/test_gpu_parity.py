@@ -171,3 +171,17 @@ def test_rejection_set_matches_oracle():
         assert (obits == 0) == (gbits == 0), i
         if obits == 0:
             assert np.array_equal(dec[0], oracle.decompress(m, N, 2048))
+
+
+def test_timed_compress_same_streams():
+    from lossless_bf16_exponent_zc_amd import Plan
+    from gpu_util import pack_inputs
+    x = W.gradient(3 * 65536 + 999, seed=12)
+    plan = Plan([x.size])
+    xd = pack_inputs(plan, [x])
+    out, sizes, ws = plan.empty_output(), plan.empty_sizes(), plan.empty_workspace()
+    for _ in range(2):  # a fresh workspace (prediction may fail), then a settled one
+        us = plan.compress_timed(xd, out, sizes, ws)
+        assert len(us) == 3 and all(t > 0 for t in us), us
+        n = int(sizes.cpu()[0])
+        assert out[:n].cpu().numpy().tobytes() == oracle.compress(x)
