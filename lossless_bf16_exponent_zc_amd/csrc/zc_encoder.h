@@ -69,21 +69,20 @@ __device__ __forceinline__ uint32_t tslot(uint32_t u) { return u ^ ((u >> 2) & 1
 // or not: the tree8 sums of v and v^2, with the first level of the squares
 // as one fused multiply-add (v^2 of a BF16 value is exact in fp64, so
 // fma(b, b, a*a) rounds a^2 + b^2 once, as the add of the two squares does).
+__device__ __forceinline__ void moments4_half(uint32_t w0, uint32_t w1, double& a01, double& q01) {
+    const double v0 = bf16_lo(w0), v1 = bf16_hi(w0), v2 = bf16_lo(w1), v3 = bf16_hi(w1);
+    a01 = (v0 + v1) + (v2 + v3);
+    q01 = __builtin_fma(v1, v1, v0 * v0) + __builtin_fma(v3, v3, v2 * v2);
+}
+
 __device__ __forceinline__ void moments8_full(const u32x4 w, double& s1, double& s2) {
-    double v[8];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        v[2 * m] = bf16_lo(w[m]);
-        v[2 * m + 1] = bf16_hi(w[m]);
-    }
-    double a[4], q[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        a[i] = v[2 * i] + v[2 * i + 1];
-        q[i] = __builtin_fma(v[2 * i + 1], v[2 * i + 1], v[2 * i] * v[2 * i]);
-    }
-    s1 = (a[0] + a[1]) + (a[2] + a[3]);
-    s2 = (q[0] + q[1]) + (q[2] + q[3]);
+    // two halves one after the other: only four values' fp64 temporaries live
+    double a0, q0, a1, q1;
+    moments4_half(w[0], w[1], a0, q0);
+    __builtin_amdgcn_sched_barrier(0);
+    moments4_half(w[2], w[3], a1, q1);
+    s1 = a0 + a1;
+    s2 = q0 + q1;
 }
 
 // Moments of one group (the wave's LDS area holds its 2048 values in index
@@ -176,11 +175,16 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
             const uint64_t g = g0 + q;
             if (g >= sd.g) break;  // uniform
             if (MOMENTS) {
+                // the group's words go to LDS and come back after the moments,
+                // so they hold no registers while the fp64 sums run
 #pragma unroll
                 for (int k = 0; k < 4; ++k) s_area[wave][tslot(64 * k + lane)] = w[q][k];
                 __builtin_amdgcn_wave_barrier();
                 group_moments(s_area[wave], lane, (uint64_t)kGroup * g + 32u * lane, sd.n,
                               (uint64_t)kGroup * (g + 1) <= sd.n, m1[q], m2[q], mn[q]);
+                asm volatile("" ::: "memory");  // reload below: no forwarding of the stored words
+#pragma unroll
+                for (int k = 0; k < 4; ++k) w[q][k] = s_area[wave][tslot(64 * k + lane)];
                 __builtin_amdgcn_wave_barrier();  // before the area is reused
             }
             uint32_t P[3];
