@@ -65,10 +65,11 @@ __device__ __forceinline__ void exponent_bytes(const u32x4 (&w)[4], uint32_t (&Q
 // reads (lane l: units 4l + t) free of LDS bank conflicts.
 __device__ __forceinline__ uint32_t tslot(uint32_t u) { return u ^ ((u >> 2) & 15u); }
 
-// Moments of 8 consecutive values, all of them real (index < n) and finite
-// or not: the tree8 sums of v and v^2, with the first level of the squares
-// as one fused multiply-add (v^2 of a BF16 value is exact in fp64, so
-// fma(b, b, a*a) rounds a^2 + b^2 once, as the add of the two squares does).
+// Moments of 8 consecutive values, all of them real (index < n) and finite:
+// the 8-leaf pairwise trees of v and v^2, with the first level of the
+// squares as one fused multiply-add (v^2 of a BF16 value is exact in fp64,
+// so fma(b, b, a*a) rounds a^2 + b^2 once, as the add of the two squares
+// does).
 __device__ __forceinline__ void moments4_half(uint32_t w0, uint32_t w1, double& a01, double& q01) {
     const double v0 = bf16_lo(w0), v1 = bf16_hi(w0), v2 = bf16_lo(w1), v3 = bf16_hi(w1);
     a01 = (v0 + v1) + (v2 + v3);
@@ -85,21 +86,60 @@ __device__ __forceinline__ void moments8_full(const u32x4 w, double& s1, double&
     s2 = q0 + q1;
 }
 
+// The same sums with values at or past n and Inf/NaN values taken as +0.0,
+// and the count of the others; values base + 4h .. base + 4h + 3.
+__device__ __forceinline__ uint32_t moments4_careful(uint32_t w0, uint32_t w1, uint64_t base,
+                                                     uint64_t n, double& a01, double& q01) {
+    const uint32_t wd[2] = {w0, w1};
+    double v[4];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t d = wd[i >> 1];
+        const float f = __uint_as_float((i & 1) ? (d & 0xFFFF0000u) : (d << 16));
+        const bool ok = __builtin_isfinite(f) && base + i < n;
+        v[i] = ok ? (double)f : 0.0;
+        cnt += ok ? 1u : 0u;
+    }
+    a01 = (v[0] + v[1]) + (v[2] + v[3]);
+    q01 = __builtin_fma(v[1], v[1], v[0] * v[0]) + __builtin_fma(v[3], v[3], v[2] * v[2]);
+    return cnt;
+}
+
+__device__ __forceinline__ uint32_t moments8_careful(const u32x4 w, uint64_t base, uint64_t n,
+                                                     double& s1, double& s2) {
+    double a0, q0, a1, q1;
+    uint32_t c = moments4_careful(w[0], w[1], base, n, a0, q0);
+    __builtin_amdgcn_sched_barrier(0);
+    c += moments4_careful(w[2], w[3], base + 4, n, a1, q1);
+    s1 = a0 + a1;
+    s2 = q0 + q1;
+    return c;
+}
+
 // Moments of one group (the wave's LDS area holds its 2048 values in index
 // order at tslot units; lane l takes values 32l .. 32l + 31): per lane the
 // 8-value trees of its four runs joined as (r0 + r1) + (r2 + r3), then the
-// lane butterfly.  The runs are taken one after the other (scheduling
-// barriers between them keep only one run's fp64 temporaries live).  A full
-// group (all values < n) with only finite values needs no count; otherwise
-// moments8 takes the run again, with values past n and non-finite ones
-// left out.
+// lane butterfly.  The runs are taken one after the other, each in two
+// halves (scheduling barriers between them keep only four values' fp64
+// temporaries live).  A full group (all values < n) with only finite values
+// needs no count; otherwise the careful sums leave values past n and
+// non-finite ones out (as +0.0) and count the others.
 __device__ __forceinline__ void run_moments(const u32x4* area, uint32_t lane, uint32_t t,
                                             uint64_t base, uint64_t n, bool full, double& r1,
                                             double& r2, uint32_t& cnt) {
     const u32x4 w = area[tslot(4 * lane + t)];
+    // an Inf or NaN among the 8 values (exponent field 255: adding 0x80 to a
+    // half's masked exponent bits carries into its top bit only then) or a
+    // partial group takes the careful path; the two paths share nothing
+    uint32_t top = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) top |= (w[m] & 0x7F807F80u) + 0x00800080u;
     uint32_t c = 8;
-    moments8_full(w, r1, r2);
-    if (!full || !__builtin_isfinite(r2)) moments8(w, base + 8 * t, n, r1, r2, c);
+    if (full && (top & 0x80008000u) == 0)
+        moments8_full(w, r1, r2);
+    else
+        c = moments8_careful(w, base + 8 * t, n, r1, r2);
     cnt += c;
     __builtin_amdgcn_sched_barrier(0);
 }

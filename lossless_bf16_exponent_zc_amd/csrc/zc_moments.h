@@ -27,38 +27,6 @@ __device__ __forceinline__ double bf16_lo(uint32_t w) {
     return (double)__uint_as_float(w << 16);
 }
 
-// Moments of 8 consecutive values (one 16-byte word).  Values at or past n
-// are zero; an Inf or NaN among them is replaced by +0.0 and not counted.
-__device__ __forceinline__ void moments8(const u32x4 w, uint64_t base, uint64_t n, double& s1,
-                                         double& s2, uint32_t& cnt) {
-    double v[8], q[8];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        v[2 * m] = bf16_lo(w[m]);
-        v[2 * m + 1] = bf16_hi(w[m]);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = v[i] * v[i];
-    s1 = tree8(v);
-    s2 = tree8(q);
-    cnt = base >= n ? 0u : (n - base >= 8 ? 8u : (uint32_t)(n - base));
-    if (!__builtin_isfinite(s2)) {  // rare: redo without the non-finite values
-        cnt = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t d = w[i >> 1];
-            const float f = __uint_as_float((i & 1) ? (d & 0xFFFF0000u) : (d << 16));
-            const bool ok = __builtin_isfinite(f) && base + i < n;
-            v[i] = ok ? (double)f : 0.0;
-            q[i] = v[i] * v[i];
-            cnt += ok ? 1u : 0u;
-        }
-        s1 = tree8(v);
-        s2 = tree8(q);
-    }
-}
-
-
 __device__ __forceinline__ double make_f64(uint32_t lo, uint32_t hi) {
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
