@@ -9,7 +9,8 @@
 //                      fields known before encoding; where the prediction
 //                      failed, the segment's codes again; chunk table, sizes
 //   zc_place_escapes   group table, escapes to their place
-// Decompress: zc_decode.  Decompress-reduce: zc_decode_reduce.
+// Decompress: zc_decode.  Decompress-reduce: zc_decode_reduce_wide (one wave
+// per shard, up to 8 shards), else zc_decode_reduce (shards in turn).
 // Every call enqueues on the caller's stream and returns; nothing here reads
 // device memory except the two zc_read_* helpers, which synchronise.
 #include <stdlib.h>
@@ -341,7 +342,10 @@ zc_status zc_decompress_reduce(const zc_plan* p, const void* const* d_streams, u
     a.ngroups = ngroups(p);
     a.out = static_cast<uint16_t*>(d_out);
     a.status = ws_ptr<uint32_t>(p, d_ws, p->ws.status);
-    hipLaunchKernelGGL(zc_decode_reduce, dim3(group_grid(p)), dim3(256), 0, stream, a);
+    if (nstreams <= 8)  // one wave per shard, one workgroup per group
+        hipLaunchKernelGGL(zc_decode_reduce_wide, dim3(ngroups(p)), dim3(64 * nstreams), 0, stream, a);
+    else
+        hipLaunchKernelGGL(zc_decode_reduce, dim3(group_grid(p)), dim3(256), 0, stream, a);
     return launch_status();
 }
 

@@ -339,6 +339,105 @@ __device__ __forceinline__ void decode_kernel(const DecodeArgs& a) {
     if (lane == 0) a.status[gg] = bad;
 }
 
+// One stream's group for the one-wave-per-shard reduce: decode into o (the
+// lane's four words: tile k at word 64k + lane), returns the rejection bits.
+template <bool TAIL>
+__device__ __forceinline__ uint32_t decode_one(const uint8_t* st, uint64_t cap, const SegDesc& sd,
+                                               uint32_t C, uint32_t g, uint32_t lane,
+                                               uint32_t* esc_lds, u32x4* row, u32x4 (&o)[4]) {
+    GroupData d;
+    fetch<true>(st, cap, sd, C, g, lane, d);
+    uint32_t first = 0;
+    if (!d.bad) first = fetch_escapes(st, cap, sd.esc_off + d.t0 + d.rel, d.span, lane, esc_lds);
+    uint32_t bad = d.bad;
+    if (bad) return bad;
+    if (TAIL) {
+        const uint32_t valid = (uint32_t)(sd.n - (uint64_t)kGroup * g);
+        const uint32_t V = valid_bits(lane, valid);
+        bool padbad = ((d.P[0] | d.P[1] | d.P[2]) & ~V) != 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            padbad |= (__builtin_bit_cast(uint64_t, d.sm[k]) & sm_pad_mask(lane, valid, k)) != 0;
+        if (__ballot(padbad)) bad |= kBadPad;
+    }
+    const uint32_t M = d.P[0] & d.P[1] & d.P[2];
+    const uint32_t cnt = __builtin_popcount(M);
+    const uint32_t incl = wave_inclusive_scan(cnt);
+    if (readlane(incl, 63) != d.span) bad |= kBadCount;
+    if (!bad) rebuild(d, M, first + incl - cnt, reinterpret_cast<const uint8_t*>(esc_lds), row, o);
+    return bad;
+}
+
+// Output word i (values 512 (i / 64) + 8 (i % 64) .. + 7 of group g).
+template <bool TAIL>
+__device__ __forceinline__ void store_word(uint16_t* __restrict__ out, uint64_t n, uint64_t g,
+                                           uint32_t i, const u32x4 w) {
+    const uint64_t b = (uint64_t)kGroup * g + 512u * (i >> 6) + 8u * (i & 63u);
+    if (!TAIL || b + 8 <= n) {
+        *reinterpret_cast<u32x4*>(out + b) = w;
+        return;
+    }
+    for (uint32_t j = 0; j < 8; ++j)
+        if (b + j < n) out[b + j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+}
+
+// Decompress-reduce with one wave per shard (up to 8 shards): wave s decodes
+// shard s's group into its LDS area (the area first holds its exponent rows
+// and escape bytes), then the workgroup sums the shards' values word by
+// word in shard order, in fp32, and rounds to BF16.  Every shard's loads are
+// in flight at once; a group costs two memory round trips.
+template <bool TAIL>
+__device__ __forceinline__ void reduce_group_wide(const DecodeArgs& a, const SegDesc& sd, uint32_t g,
+                                                  uint32_t gg, u32x4 (*s_area)[258], uint32_t* s_bad) {
+    const uint32_t lane = lane_id(), wave = wave_id(), S = a.nstreams;
+    u32x4* area = s_area[wave];
+    u32x4 o[4];
+    const uint32_t bad = decode_one<TAIL>(a.in[wave], a.capacity, sd, a.chunk_elems, g, lane,
+                                          reinterpret_cast<uint32_t*>(area + 128), area + 2 * lane, o);
+    if (!bad) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) area[64 * k + lane] = o[k];
+    }
+    if (lane == 0) s_bad[wave] = bad;
+    __syncthreads();
+    uint32_t bad_all = 0;
+    for (uint32_t s = 0; s < S; ++s) bad_all |= s_bad[s];
+    if (bad_all == 0) {
+        for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) {
+            float acc[8];
+#pragma unroll
+            for (uint32_t s = 0; s < 8; ++s) {
+                if (s >= S) break;  // uniform
+                const u32x4 v = s_area[s][i];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float lo = __uint_as_float(v[m] << 16), hi = __uint_as_float(v[m] & 0xFFFF0000u);
+                    acc[2 * m] = s == 0 ? lo : acc[2 * m] + lo;
+                    acc[2 * m + 1] = s == 0 ? hi : acc[2 * m + 1] + hi;
+                }
+            }
+            u32x4 w;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) w[m] = to_bf16(acc[2 * m]) | (to_bf16(acc[2 * m + 1]) << 16);
+            store_word<TAIL>(a.out + sd.in_off, sd.n, g, i, w);
+        }
+    }
+    if (threadIdx.x == 0) a.status[gg] = bad_all;
+}
+
+__global__ __launch_bounds__(512) void zc_decode_reduce_wide(DecodeArgs a) {
+    __shared__ u32x4 s_area[8][258];  // per wave: rows (2048 B) + escapes (2080 B); then values
+    __shared__ uint32_t s_bad[8];
+    const uint32_t gg = blockIdx.x;
+    const ItemDesc gd = a.single ? ItemDesc{0u, gg} : a.groups[gg];
+    const SegDesc sd = a.single ? a.seg0 : a.segs[gd.seg];
+    const uint32_t g = gd.local;
+    if ((uint64_t)kGroup * (g + 1) > sd.n)
+        reduce_group_wide<true>(a, sd, g, gg, s_area, s_bad);
+    else
+        reduce_group_wide<false>(a, sd, g, gg, s_area, s_bad);
+}
+
 // Eight waves per SIMD for the plain decoder (it fits in 64 VGPRs).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void zc_decode(DecodeArgs a) {
     decode_kernel<false>(a);

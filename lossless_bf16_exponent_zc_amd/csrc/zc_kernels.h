@@ -65,5 +65,6 @@ template <int GPW>
 __global__ void zc_place_escapes(PlaceArgs a);
 __global__ void zc_decode(DecodeArgs a);
 __global__ void zc_decode_reduce(DecodeArgs a);
+__global__ void zc_decode_reduce_wide(DecodeArgs a);
 
 }  // namespace zc

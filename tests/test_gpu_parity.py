@@ -185,3 +185,15 @@ def test_timed_compress_same_streams():
         assert len(us) == 3 and all(t > 0 for t in us), us
         n = int(sizes.cpu()[0])
         assert out[:n].cpu().numpy().tobytes() == oracle.compress(x)
+
+
+def test_decompress_reduce_more_than_eight_shards():
+    # 9..16 shards take the kernel that walks the shards in turn
+    n = 70000 + 17
+    sh = W.shards(n=n, nshards=16)
+    streams = [oracle.compress(s) for s in sh]
+    for S in (9, 16):
+        say(f"  reduce over {S} shards")
+        bits, got = gpu_reduce(streams[:S], n)
+        assert bits == 0
+        assert np.array_equal(got, oracle.decompress_reduce(streams[:S], n))
