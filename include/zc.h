@@ -97,6 +97,11 @@ uint64_t zc_plan_input_elems(const zc_plan *plan);
 /* Byte offset (multiple of 256) and worst-case size of segment s's stream. */
 uint64_t zc_plan_stream_offset(const zc_plan *plan, uint32_t s);
 uint64_t zc_plan_max_stream_bytes(const zc_plan *plan, uint32_t s);
+/* Offsets, from the start of segment s's stream, of its code planes and of
+ * its escape region; [code offset, escape offset) holds the code planes and
+ * the sign+mantissa bytes (sizes fixed by the plan). */
+uint64_t zc_plan_code_offset(const zc_plan *plan, uint32_t s);
+uint64_t zc_plan_escape_offset(const zc_plan *plan, uint32_t s);
 /* Bytes the compressed buffer must hold for every segment's worst case. */
 uint64_t zc_plan_out_bytes(const zc_plan *plan);
 /* Workspace bytes needed by any call with this plan: about one byte per
@@ -130,6 +135,21 @@ zc_status zc_compress_window(const zc_plan *plan, const void *d_in, void *d_out,
                              uint64_t out_capacity, uint64_t *d_stream_bytes,
                              uint32_t window_L, void *d_ws, uint64_t ws_bytes,
                              hipStream_t stream);
+
+/*
+ * zc_compress that also records `fixed_ready` (a HIP event the caller
+ * created) on `stream` as soon as, for every segment, the bytes before the
+ * group table (header and chunk table), the bytes [code offset, escape
+ * offset) and d_stream_bytes are final; the group table and the escape
+ * region are final when the call's work completes.  A caller can wait on the
+ * event from another stream and start the size exchange and the sending of
+ * those regions while the escapes are still being placed (ZipCCL's
+ * static/dynamic split, Fig. 5).
+ */
+zc_status zc_compress_split(const zc_plan *plan, const void *d_in, void *d_out,
+                            uint64_t out_capacity, uint64_t *d_stream_bytes,
+                            void *d_ws, uint64_t ws_bytes, hipStream_t stream,
+                            hipEvent_t fixed_ready);
 
 /*
  * For profiling: zc_compress with HIP events recorded on `stream` before,

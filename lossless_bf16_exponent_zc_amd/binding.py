@@ -22,8 +22,10 @@ EXPORTS = (
     "zc_version", "zc_status_string", "zc_plan_create", "zc_plan_destroy",
     "zc_plan_num_segments", "zc_plan_chunk_elems", "zc_plan_input_offset",
     "zc_plan_input_elems", "zc_plan_stream_offset", "zc_plan_max_stream_bytes",
+    "zc_plan_code_offset", "zc_plan_escape_offset",
     "zc_plan_out_bytes", "zc_plan_workspace_bytes", "zc_compress",
-    "zc_compress_window", "zc_compress_timed", "zc_decompress", "zc_decompress_reduce",
+    "zc_compress_window", "zc_compress_split", "zc_compress_timed", "zc_decompress",
+    "zc_decompress_reduce",
     "zc_read_status", "zc_read_sigma",
 )
 
@@ -61,13 +63,14 @@ def lib() -> ctypes.CDLL:
         f.argtypes = [vp]
         f.restype = rt
     for name in ("zc_plan_input_offset", "zc_plan_stream_offset",
-                 "zc_plan_max_stream_bytes"):
+                 "zc_plan_max_stream_bytes", "zc_plan_code_offset", "zc_plan_escape_offset"):
         f = getattr(L, name)
         f.argtypes = [vp, u32]
         f.restype = u64
     L.zc_compress.argtypes = [vp, vp, vp, u64, vp, vp, u64, vp]
     L.zc_compress_window.argtypes = [vp, vp, vp, u64, vp, u32, vp, u64, vp]
     L.zc_compress_timed.argtypes = [vp, vp, vp, u64, vp, vp, u64, vp, P(ctypes.c_float)]
+    L.zc_compress_split.argtypes = [vp, vp, vp, u64, vp, vp, u64, vp, vp]
     L.zc_decompress.argtypes = [vp, vp, u64, vp, vp, u64, vp]
     L.zc_decompress_reduce.argtypes = [vp, P(vp), u32, u64, vp, vp, u64, vp]
     L.zc_read_status.argtypes = [vp, vp, vp, P(u32)]
@@ -75,6 +78,7 @@ def lib() -> ctypes.CDLL:
                                 P(ctypes.c_double), P(u64), P(ctypes.c_double),
                                 P(u32)]
     for name in ("zc_plan_create", "zc_compress", "zc_compress_window", "zc_compress_timed",
+                 "zc_compress_split",
                  "zc_decompress", "zc_decompress_reduce", "zc_read_status",
                  "zc_read_sigma"):
         getattr(L, name).restype = ctypes.c_int
@@ -155,6 +159,14 @@ class Plan:
     def max_stream_bytes(self, s: int) -> int:
         return lib().zc_plan_max_stream_bytes(self._h, s)
 
+    def code_offset(self, s: int) -> int:
+        """Offset of segment s's code planes from its stream start."""
+        return lib().zc_plan_code_offset(self._h, s)
+
+    def escape_offset(self, s: int) -> int:
+        """Offset of segment s's escape region from its stream start."""
+        return lib().zc_plan_escape_offset(self._h, s)
+
     # buffers (torch allocation only) -------------------------------------
     def empty_input(self, device="cuda"):
         import torch
@@ -185,6 +197,15 @@ class Plan:
                                           _ptr(stream_bytes), int(window), _ptr(ws),
                                           _nbytes(ws), _stream(stream))
             _check(rc, "zc_compress_window")
+
+    def compress_split(self, x, out, stream_bytes, ws, fixed_ready, stream=None):
+        """Enqueue compress() and record fixed_ready (a torch.cuda.Event that
+        has been recorded once, so it exists) as soon as the headers, chunk
+        tables, code planes, sign+mantissa bytes and sizes are final."""
+        rc = lib().zc_compress_split(self._h, _ptr(x), _ptr(out), _nbytes(out),
+                                     _ptr(stream_bytes), _ptr(ws), _nbytes(ws),
+                                     _stream(stream), ctypes.c_void_p(fixed_ready.cuda_event))
+        _check(rc, "zc_compress_split")
 
     def compress_timed(self, x, out, stream_bytes, ws, stream=None):
         """Compress as compress() and wait for it; returns the three kernels'

@@ -63,10 +63,11 @@ T* ws_ptr(const zc_plan* p, void* d_ws, uint64_t off) {
     return reinterpret_cast<T*>(static_cast<uint8_t*>(d_ws) + off);
 }
 
-// ev: null, or four events recorded on the stream around the three kernels
+// ev: null, or four events recorded on the stream around the three kernels;
+// fixed: null, or an event recorded once the fixed-size regions are final
 zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
                         uint64_t* d_stream_bytes, uint32_t forced_L, void* d_ws, uint64_t ws_bytes,
-                        hipStream_t stream, hipEvent_t* ev = nullptr) {
+                        hipStream_t stream, hipEvent_t* ev = nullptr, hipEvent_t fixed = nullptr) {
     if (!p) return ZC_ERR_INVALID_ARG;
     if (p->input_elems && (!d_in || !aligned(d_in, 16))) return ZC_ERR_INVALID_ARG;
     if (!d_out || !aligned(d_out, 256) || !d_stream_bytes || !aligned(d_stream_bytes, 8))
@@ -104,6 +105,9 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
                   p->chunk, p->chunk / p->block};
     hipLaunchKernelGGL(zc_window, dim3((uint32_t)p->witems.size()), dim3(256), 0, stream, wa);
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return ZC_ERR_HIP;
+    // after the window kernel: codes and sm bytes (coded again there when
+    // the prediction failed), header, chunk table and sizes are final
+    if (fixed && hipEventRecord(fixed, stream) != hipSuccess) return ZC_ERR_HIP;
     uint8_t* out = static_cast<uint8_t*>(d_out);
     uint8_t* staging = ea.staging;
     uint32_t* gcnt = ea.gcnt;
@@ -258,6 +262,12 @@ uint64_t zc_plan_input_elems(const zc_plan* p) { return p ? p->input_elems : 0; 
 uint64_t zc_plan_stream_offset(const zc_plan* p, uint32_t s) {
     return p && s < p->nseg ? p->segs[s].out_off : 0;
 }
+uint64_t zc_plan_code_offset(const zc_plan* p, uint32_t s) {
+    return p && s < p->nseg ? p->segs[s].code_off : 0;
+}
+uint64_t zc_plan_escape_offset(const zc_plan* p, uint32_t s) {
+    return p && s < p->nseg ? p->segs[s].esc_off : 0;
+}
 uint64_t zc_plan_max_stream_bytes(const zc_plan* p, uint32_t s) {
     return p && s < p->nseg ? p->segs[s].max_bytes : 0;
 }
@@ -267,6 +277,14 @@ uint64_t zc_plan_workspace_bytes(const zc_plan* p) { return p ? p->ws.total : 0;
 zc_status zc_compress(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
                       uint64_t* d_stream_bytes, void* d_ws, uint64_t ws_bytes, hipStream_t stream) {
     return compress_impl(p, d_in, d_out, out_capacity, d_stream_bytes, 0, d_ws, ws_bytes, stream);
+}
+
+zc_status zc_compress_split(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
+                            uint64_t* d_stream_bytes, void* d_ws, uint64_t ws_bytes,
+                            hipStream_t stream, hipEvent_t fixed_ready) {
+    if (!fixed_ready) return ZC_ERR_INVALID_ARG;
+    return compress_impl(p, d_in, d_out, out_capacity, d_stream_bytes, 0, d_ws, ws_bytes, stream,
+                         nullptr, fixed_ready);
 }
 
 zc_status zc_compress_timed(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,

@@ -94,3 +94,43 @@ def test_fixed_window_between_derived_calls():
     check([x], plan, ws)
     check([x], plan, ws, window=oracle.sigma(x)[4])
     check([x], plan, ws)
+
+
+def test_split_event_fixed_regions_final():
+    # copies taken on another stream right after the split event must equal
+    # the finished streams: headers, chunk tables, code planes, sm bytes and
+    # sizes are final at the event (first call mispredicted: the window kernel
+    # codes again before the event)
+    import torch
+    segs = [W.gradient(200000 + 777 * i, seed=40 + i) for i in range(3)]
+    plan = Plan([s.size for s in segs])
+    from gpu_util import pack_inputs
+    x = pack_inputs(plan, segs)
+    out, sizes, ws = plan.empty_output(), plan.empty_sizes(), plan.empty_workspace()
+    ws.zero_()
+    side = torch.cuda.Stream()
+    for call in range(3):
+        out.fill_(0xA5)
+        torch.cuda.synchronize()
+        ev = torch.cuda.Event()
+        ev.record()
+        plan.compress_split(x, out, sizes, ws, ev)
+        early = []
+        with torch.cuda.stream(side):
+            side.wait_event(ev)
+            early_sizes = sizes.clone()
+            for s in range(len(segs)):
+                so = plan.stream_offset(s)
+                k = -(-segs[s].size // plan.chunk_elems)
+                head = 64 + 4 * (k + 1)  # header and chunk table
+                early.append((out[so:so + head].clone(),
+                              out[so + plan.code_offset(s):so + plan.escape_offset(s)].clone()))
+        torch.cuda.synchronize()
+        assert torch.equal(early_sizes, sizes), call
+        for s, seg in enumerate(segs):
+            so = plan.stream_offset(s)
+            ref = oracle.compress(seg)
+            assert out[so:so + int(sizes[s])].cpu().numpy().tobytes() == ref, (call, s)
+            h, f = early[s]
+            assert torch.equal(h, out[so:so + h.numel()]), (call, s, "header/table")
+            assert torch.equal(f, out[so + plan.code_offset(s):so + plan.escape_offset(s)]), (call, s)
