@@ -103,6 +103,53 @@ def cpu_baseline(x, chunk):
                       f"workload, {reps} rep(s), {el:.1f} s, single-threaded C"}
 
 
+def time_config(name, segs, chunk, args, stream):
+    """Cold compress and decompress of a list of segments (one plan)."""
+    import lossless_bf16_exponent_zc_amd as zc
+    plan = zc.Plan([x.size for x in segs], chunk)
+    xd = plan.empty_input()
+    for s, x in enumerate(segs):
+        off = plan.input_offset(s)
+        xd[off:off + x.size] = torch.from_numpy(x.view(np.int16)).cuda()
+    out, sizes, ws = plan.empty_output(), plan.empty_sizes(), plan.empty_workspace()
+    y = plan.empty_input()
+    comp = lambda: plan.compress(xd, out, sizes, ws)
+    dec = lambda: plan.decompress(out, y, ws)
+    comp()
+    dec()
+    torch.cuda.synchronize()
+    assert plan.read_status(ws) == 0
+    n = sum(x.size for x in segs)
+    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    tc = float(np.median(timed(comp, args.steps, args.warmup, stream, flush)))
+    td = float(np.median(timed(dec, args.steps, args.warmup, stream, flush)))
+    sb = int(sizes.sum().item())
+    r = {"workload": name, "elements": n, "segments": len(segs), "chunk_elems": chunk,
+         "compress_ms": round(tc * 1e3, 4), "decompress_ms": round(td * 1e3, 4),
+         "compress_GBps": round(2 * n / tc / 1e9, 2), "decompress_GBps": round(2 * n / td / 1e9, 2),
+         "compress_hbm_frac": round((4 * n + sb) / tc / HBM_PEAK, 4),
+         "compress_hbm_frac_one_read": round((2 * n + sb) / tc / HBM_PEAK, 4),
+         "decompress_hbm_frac": round((2 * n + sb) / td / HBM_PEAK, 4),
+         "ratio": round(2 * n / sb, 4)}
+    del plan, xd, out, sizes, ws, y, flush
+    torch.cuda.empty_cache()
+    return r
+
+
+def other_configs(args, stream):
+    from lossless_bf16_exponent_zc_amd import workloads as W
+    log("Llama3-8B MLP matrices")
+    res = [time_config("Llama3-8B MLP layer: 3 BF16 matrices (4096x14336, 14336x4096, "
+                       "4096x14336), one segment each", W.llama_mlp(), 65536, args, stream)]
+    log("MoE 256 experts")
+    bits, counts = W.moe(device="cuda")
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    segs = [bits[offs[i]:offs[i + 1]] for i in range(len(counts))]
+    res.append(time_config("MoE all-to-all: 256 expert segments, 65,536 tokens x 7168", segs,
+                           65536, args, stream))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +157,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reduce", action="store_true")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="also time compress / decompress of the Llama3-8B MLP matrices "
+                         "(3 segments) and the 256-expert MoE batch (extra keys)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also time a plain 128 MiB device-to-device copy (bandwidth "
                          "reference and counter calibration)")
@@ -172,6 +222,23 @@ def main():
         if i >= args.warmup:
             ku.append(us)
     ku = np.median(np.array(ku), axis=0)
+
+    # the static/dynamic split: when the fixed-size regions (headers, chunk
+    # tables, codes, sign+mantissa bytes) and the sizes are final, measured
+    # from the call's start (cold calls, events on this stream)
+    log("split event")
+    sp = []
+    for i in range(args.warmup + args.steps):
+        flush.sum()
+        e0, ef, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        ef.record(stream)
+        e0.record(stream)
+        plan.compress_split(xd, out, sizes, ws, ef)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            sp.append((e0.elapsed_time(ef) * 1e3, e0.elapsed_time(e1) * 1e3))
+    sp = np.median(np.array(sp), axis=0)
     G = (N + 2047) // 2048
     # the encoder pass moves the input in and the codes, sign+mantissa bytes
     # and escape exponents out (the escape copy of the placement kernel is
@@ -211,6 +278,9 @@ def main():
         "escape_frac": round(E / N, 5),
         "compress_kernels_us": {"encode": round(float(ku[0]), 2), "window": round(float(ku[1]), 2),
                                 "place_escapes": round(float(ku[2]), 2)},
+        # zc_compress_split: fixed-size regions and sizes final / whole call done
+        "split_fixed_ready_us": round(float(sp[0]), 2),
+        "split_call_us": round(float(sp[1]), 2),
         # the dominant kernel of the step: the encoder pass (moments, codes,
         # staged escapes), its time from HIP events around it (cold)
         "roofline": {"bound": "hbm", "kernel": "zc_encode",
@@ -264,6 +334,9 @@ def main():
         res["reduce_ms"] = round(tr * 1e3, 4)
         res["reduce_hbm_frac"] = round((tot + 2 * n) / tr / HBM_PEAK, 4)
         res["reduce_out_GBps"] = round(2 * n / tr / 1e9, 2)
+
+    if args.all_configs:
+        res["other_configs"] = other_configs(args, stream)
 
     if not args.no_cpu_baseline:
         log("cpu baseline")
