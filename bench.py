@@ -275,6 +275,10 @@ def main():
         "compress_ms_warm": round(t_cw * 1e3, 4),
         "decompress_ms_warm": round(t_dw * 1e3, 4),
         "ratio": round(2 * N / stream_bytes, 4),
+        # the compressed/raw switch: links slower than this favour sending
+        # the compressed stream (cold compress + decompress of this tensor)
+        "break_even_link_GBps": round(zc.prefer_compressed(2 * N, stream_bytes, t_c * 1e6,
+                                                           t_d * 1e6, 1.0)[1], 1),
         "escape_frac": round(E / N, 5),
         "compress_kernels_us": {"encode": round(float(ku[0]), 2), "window": round(float(ku[1]), 2),
                                 "place_escapes": round(float(ku[2]), 2)},

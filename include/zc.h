@@ -205,6 +205,22 @@ zc_status zc_read_sigma(const zc_plan *plan, const void *d_ws, uint32_t s,
                         hipStream_t stream, double *S1, double *S2,
                         uint64_t *n, double *var, uint32_t *L);
 
+/*
+ * Host-side switch between sending a tensor compressed and sending it raw
+ * over a link of link_GBps (GB/s, > 0): returns 1 when
+ *   compress_us + compressed_bytes / link + decompress_us < raw_bytes / link
+ * (ZipCCL, "Key idea and contribution", technique 3: the reduce-scatter path
+ * switches to the native collective when compression does not pay; for a
+ * reduce-scatter, decompress_us is the fused decompress-reduce's time minus
+ * the native reduce's).  Times are measured ones (microseconds).  When
+ * break_even_GBps is not NULL it receives the link bandwidth below which
+ * compression pays, (raw - compressed) / (compress_us + decompress_us), or 0
+ * when the compressed form is not smaller.  Returns 0 for invalid arguments
+ * (link_GBps <= 0, negative times).
+ */
+int zc_prefer_compressed(uint64_t raw_bytes, uint64_t compressed_bytes, double compress_us,
+                         double decompress_us, double link_GBps, double *break_even_GBps);
+
 #ifdef __cplusplus
 }
 #endif

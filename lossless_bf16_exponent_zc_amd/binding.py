@@ -26,7 +26,7 @@ EXPORTS = (
     "zc_plan_out_bytes", "zc_plan_workspace_bytes", "zc_compress",
     "zc_compress_window", "zc_compress_split", "zc_compress_timed", "zc_decompress",
     "zc_decompress_reduce",
-    "zc_read_status", "zc_read_sigma",
+    "zc_read_status", "zc_read_sigma", "zc_prefer_compressed",
 )
 
 
@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
     L.zc_decompress.argtypes = [vp, vp, u64, vp, vp, u64, vp]
     L.zc_decompress_reduce.argtypes = [vp, P(vp), u32, u64, vp, vp, u64, vp]
     L.zc_read_status.argtypes = [vp, vp, vp, P(u32)]
+    L.zc_prefer_compressed.argtypes = [u64, u64, ctypes.c_double, ctypes.c_double,
+                                       ctypes.c_double, P(ctypes.c_double)]
+    L.zc_prefer_compressed.restype = ctypes.c_int
     L.zc_read_sigma.argtypes = [vp, vp, u32, vp, P(ctypes.c_double),
                                 P(ctypes.c_double), P(u64), P(ctypes.c_double),
                                 P(u32)]
@@ -88,6 +91,15 @@ def lib() -> ctypes.CDLL:
 
 def status_string(code: int) -> str:
     return lib().zc_status_string(code).decode()
+
+
+def prefer_compressed(raw_bytes: int, compressed_bytes: int, compress_us: float,
+                      decompress_us: float, link_GBps: float):
+    """(send compressed?, break-even link GB/s) from measured sizes and times."""
+    be = ctypes.c_double()
+    r = lib().zc_prefer_compressed(int(raw_bytes), int(compressed_bytes), float(compress_us),
+                                   float(decompress_us), float(link_GBps), ctypes.byref(be))
+    return bool(r), be.value
 
 
 def _check(rc: int, what: str):

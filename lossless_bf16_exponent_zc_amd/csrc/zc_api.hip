@@ -13,6 +13,7 @@
 // per shard, up to 8 shards), else zc_decode_reduce (shards in turn).
 // Every call enqueues on the caller's stream and returns; nothing here reads
 // device memory except the two zc_read_* helpers, which synchronise.
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -397,6 +398,18 @@ zc_status zc_read_sigma(const zc_plan* p, const void* d_ws, uint32_t s, hipStrea
     if (var) *var = st.var;
     if (L) *L = st.L;
     return ZC_OK;
+}
+
+int zc_prefer_compressed(uint64_t raw_bytes, uint64_t compressed_bytes, double compress_us,
+                         double decompress_us, double link_GBps, double* break_even_GBps) {
+    if (break_even_GBps) *break_even_GBps = 0.0;
+    if (!(link_GBps > 0.0) || !(compress_us >= 0.0) || !(decompress_us >= 0.0)) return 0;
+    const double saved = (double)raw_bytes - (double)compressed_bytes;  // bytes
+    const double cost_us = compress_us + decompress_us;
+    if (break_even_GBps && saved > 0.0)
+        *break_even_GBps = cost_us > 0.0 ? saved / (cost_us * 1e3) : INFINITY;  // bytes/us -> GB/s
+    // compare the link time saved (us) with the codec's time
+    return saved > 0.0 && saved / (link_GBps * 1e3) > cost_us ? 1 : 0;
 }
 
 }  // extern "C"

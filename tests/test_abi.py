@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     assert sorted(binding.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -58,3 +58,23 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "libzc.so"))
     with pytest.raises(ImportError):
         binding.lib()
+
+
+def test_prefer_compressed_cost_model(lib):
+    # 64M BF16 values (134,217,728 raw bytes) at ratio ~1.27, 73 us to
+    # compress and 47 us to decompress: compression pays below
+    # (raw - compressed) / 120 us
+    raw, comp = 134217728, 105900000
+    ok, be = binding.prefer_compressed(raw, comp, 73.0, 47.0, 50.0)
+    assert ok and abs(be - (raw - comp) / 120e3) < 1e-9
+    assert binding.prefer_compressed(raw, comp, 73.0, 47.0, be * 1.01)[0] is False
+    assert binding.prefer_compressed(raw, comp, 73.0, 47.0, be * 0.99)[0] is True
+    # no saving: never compressed, break-even 0
+    assert binding.prefer_compressed(raw, raw, 1.0, 1.0, 0.001) == (False, 0.0)
+    assert binding.prefer_compressed(raw, raw + 5, 0.0, 0.0, 1.0) == (False, 0.0)
+    # free codec: any saving pays on any link
+    ok, be = binding.prefer_compressed(raw, comp, 0.0, 0.0, 1e6)
+    assert ok and be == float("inf")
+    # invalid arguments
+    assert binding.prefer_compressed(raw, comp, 1.0, 1.0, 0.0)[0] is False
+    assert binding.prefer_compressed(raw, comp, -1.0, 1.0, 10.0)[0] is False
