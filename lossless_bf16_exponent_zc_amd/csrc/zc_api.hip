@@ -60,7 +60,7 @@ zc_status check_ws(const zc_plan* p, const void* d_ws, uint64_t ws_bytes) {
 }
 
 template <typename T>
-T* ws_ptr(const zc_plan* p, void* d_ws, uint64_t off) {
+T* ws_ptr(const zc_plan*, void* d_ws, uint64_t off) {
     return reinterpret_cast<T*>(static_cast<uint8_t*>(d_ws) + off);
 }
 

@@ -86,8 +86,10 @@ __device__ __forceinline__ void moments8_full(const u32x4 w, double& s1, double&
     s2 = q0 + q1;
 }
 
-// The same sums with values at or past n and Inf/NaN values taken as +0.0,
-// and the count of the others; values base + 4h .. base + 4h + 3.
+// The same sums with Inf/NaN values taken as +0.0 and positions at or past
+// n as -0.0 (the sum's identity: beyond the data the tree has no leaves;
+// the window kernel restores the +0.0 padding's one effect, the sign of a
+// zero sum), and the count of the finite values; values base .. base + 3.
 __device__ __forceinline__ uint32_t moments4_careful(uint32_t w0, uint32_t w1, uint64_t base,
                                                      uint64_t n, double& a01, double& q01) {
     const uint32_t wd[2] = {w0, w1};
@@ -97,8 +99,8 @@ __device__ __forceinline__ uint32_t moments4_careful(uint32_t w0, uint32_t w1, u
     for (int i = 0; i < 4; ++i) {
         const uint32_t d = wd[i >> 1];
         const float f = __uint_as_float((i & 1) ? (d & 0xFFFF0000u) : (d << 16));
-        const bool ok = __builtin_isfinite(f) && base + i < n;
-        v[i] = ok ? (double)f : 0.0;
+        const bool in = base + i < n, ok = in && __builtin_isfinite(f);
+        v[i] = ok ? (double)f : (in ? 0.0 : -0.0);
         cnt += ok ? 1u : 0u;
     }
     a01 = (v[0] + v[1]) + (v[2] + v[3]);
@@ -205,7 +207,8 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
             for (int k = 0; k < 4; ++k) w[q][k] = u32x4{0, 0, 0, 0};
         }
     }
-    double m1[2] = {0.0, 0.0}, m2[2] = {0.0, 0.0};  // group moments (wave-uniform)
+    // group moments (wave-uniform); groups past the data are -0.0 (identity)
+    double m1[2] = {-0.0, -0.0}, m2[2] = {-0.0, -0.0};
     uint32_t mn[2] = {0, 0}, ec[2] = {0, 0};       // values, escapes
     if (live) {
         uint8_t* __restrict__ st = a.out + sd.out_off;

@@ -116,17 +116,17 @@ __device__ __forceinline__ uint32_t leaf_slot(uint32_t b, LeafOrder o) {
     return ((b >> lr) << lr) | ((w & ((1u << o.lm) - 1u)) << o.lt) | (w >> o.lm);
 }
 
-// Pairwise sums over B leaf partials (padded with +0.0 to P = 2^ceil(log2 B)),
-// by a workgroup of kReduceThreads threads.  A round covers an aligned run
-// of T*m leaves: thread t sums m <= 16 of them pairwise (a shorter run
-// padded with +0.0), a wave butterfly and a tree over the waves join the
-// threads.  Rounds (at most 512: a segment has fewer than 2^32 values, 2^21
+// Pairwise sums over B leaf partials (positions past B and past the rounds
+// taken as -0.0, the identity, so the result is the tree over the leaves
+// alone), by a workgroup of kReduceThreads threads.  A round covers an
+// aligned run of T*m leaves: thread t sums m <= 16 of them pairwise, a wave
+// butterfly and a tree over the waves join the threads.  Rounds (at most 512: a segment has fewer than 2^32 values, 2^21
 // leaves of 2048, and T*m = 4096 when there are several rounds) are joined
 // by a last pairwise tree.  Inputs at leaf slots (leaf_slot), so each load
 // instruction reads consecutive slots.  The result is valid in thread 0.
-// The round's loads (load_round) can be issued ahead of other work;
-// finish_round and reduce_partials contain __syncthreads: call them from
-// uniform control flow only.
+// The round's loads (load_round) can be issued ahead of other work (the
+// masks are applied by finish_round); finish_round contains __syncthreads:
+// call it from uniform control flow only.
 struct ReduceShape {
     LeafOrder o;
     uint32_t T, m, rounds;
@@ -147,8 +147,7 @@ struct RoundLoads {  // raw loads; leaves past B are masked when the round is fi
 };
 
 __device__ __forceinline__ void load_round(const double* ps1, const double* ps2, const uint32_t* pn,
-                                           uint32_t B, const ReduceShape& sh, uint32_t r,
-                                           RoundLoads& L) {
+                                           const ReduceShape& sh, uint32_t r, RoundLoads& L) {
     const uint32_t tid = threadIdx.x, T = sh.T, m = sh.m;
 #pragma unroll
     for (uint32_t i = 0; i < 16; ++i) {  // loads only: nothing here waits for them
@@ -168,8 +167,8 @@ __device__ __forceinline__ void finish_round(RoundLoads& L, uint32_t B, const Re
     for (uint32_t i = 0; i < 16; ++i) {
         const uint32_t leaf = (r * shp.T + tid) * shp.m + i;
         const bool ok = tid < shp.T && i < shp.m && leaf < B;
-        L.v1[i] = ok ? L.v1[i] : 0.0;
-        L.v2[i] = ok ? L.v2[i] : 0.0;
+        L.v1[i] = ok ? L.v1[i] : -0.0;  // no leaf: the identity
+        L.v2[i] = ok ? L.v2[i] : -0.0;
         rn += ok ? L.n[i] : 0u;
     }
 #pragma unroll
@@ -188,7 +187,7 @@ __device__ __forceinline__ void finish_round(RoundLoads& L, uint32_t B, const Re
     }
     __syncthreads();
     if (wave == 0) {  // lanes 0..15 join the waves' sums: a 16-leaf butterfly
-        double t1 = lane < nw ? sh.v1[lane] : 0.0, t2 = lane < nw ? sh.v2[lane] : 0.0;
+        double t1 = lane < nw ? sh.v1[lane] : -0.0, t2 = lane < nw ? sh.v2[lane] : -0.0;
         t1 = row_tree(t1);
         t2 = row_tree(t2);
         if (lane == 0) {
@@ -209,8 +208,8 @@ __device__ __forceinline__ void join_rounds(const MomentScratch& sh, uint32_t ro
 #pragma unroll
         for (uint32_t i = 0; i < 8; ++i) {
             const uint32_t j = 8 * lane + i;
-            t1[i] = j < rounds ? sh.r1[j] : 0.0;
-            t2[i] = j < rounds ? sh.r2[j] : 0.0;
+            t1[i] = j < rounds ? sh.r1[j] : -0.0;
+            t2[i] = j < rounds ? sh.r2[j] : -0.0;
         }
         const double u1 = wave_tree(tree8(t1)), u2 = wave_tree(tree8(t2));
         if (lane == 0) {
@@ -219,20 +218,6 @@ __device__ __forceinline__ void join_rounds(const MomentScratch& sh, uint32_t ro
             n = nn;
         }
     }
-}
-
-__device__ __forceinline__ void reduce_partials(const double* ps1, const double* ps2,
-                                                const uint32_t* pn, uint32_t B,
-                                                MomentScratch& sh, double& s1, double& s2,
-                                                uint64_t& n) {
-    const ReduceShape shape = reduce_shape(B);
-    uint64_t nn = 0;
-    for (uint32_t r = 0; r < shape.rounds; ++r) {
-        RoundLoads L;
-        load_round(ps1, ps2, pn, B, shape, r, L);
-        finish_round(L, B, shape, r, sh, nn);
-    }
-    join_rounds(sh, shape.rounds, nn, s1, s2, n);
 }
 
 // Population variance of the finite values from the moments: three

@@ -5,9 +5,11 @@
 // online histogram and no sort.  Here the statistic is the population
 // variance of the finite values, from fp64 sums S1 = sum v and S2 = sum v^2
 // taken by a pairwise tree over the segment (padded to a power of two with
-// +0.0).  The tree's shape depends only on indices, so the result is the
-// same bit pattern on any device.  The encoder's first pass computes the
-// tree up to moment blocks of 16,384 values (or the chunk, if smaller); the
+// +0.0; the kernels take positions past the data as -0.0, the identity, and
+// restore the padding's effect on the sign of a zero sum at the end).  The
+// tree's shape depends only on indices, so the result is the same bit
+// pattern on any device.  The encoder's first pass computes the tree up to
+// moment blocks of 16,384 values (or the chunk, if smaller); the
 // window kernel here joins the moment blocks of each segment.
 //
 // Window: the 7 exponents [L, L+6] holding the most N(0, var) mass, i.e.
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
     const bool moments = !forced && sd.nsb;
     const ReduceShape shape = reduce_shape(sd.nsb);
     RoundLoads rl;
-    if (moments) load_round(ps1, ps2, pn, sd.nsb, shape, 0, rl);
+    if (moments) load_round(ps1, ps2, pn, shape, 0, rl);
     ChunkCounts cc;
     cc.run = 0;
     cc.in_table = false;
@@ -190,12 +192,19 @@ __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
         uint64_t nn = 0;
         finish_round(rl, sd.nsb, shape, 0, s_mom, nn);
         for (uint32_t k = 1; k < shape.rounds; ++k) {
-            load_round(ps1, ps2, pn, sd.nsb, shape, k, rl);
+            load_round(ps1, ps2, pn, shape, k, rl);
             finish_round(rl, sd.nsb, shape, k, s_mom, nn);
         }
         join_rounds(s_mom, shape.rounds, nn, s1, s2, n);
     }
     if (threadIdx.x == 0) {
+        // the tree above had no leaves past the data; the segment's tree pads
+        // it with +0.0 to a power of two, which changes nothing but the sign
+        // of a zero sum: -0.0 becomes +0.0 when any padding leaf exists
+        if ((sd.n & (sd.n - 1)) != 0) {
+            s1 = s1 == 0.0 ? 0.0 : s1;
+            s2 = s2 == 0.0 ? 0.0 : s2;
+        }
         const double var = forced ? 0.0 : variance(s1, s2, n);
         const uint32_t L = forced ? forced : window_from_variance(var);
         s_L = L;

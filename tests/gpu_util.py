@@ -12,6 +12,14 @@ def say(*a):
     sys.stdout.flush()
 
 
+def stat_bits(stats):
+    """(S1, S2, n, var, L) with the floats as their IEEE bit patterns, so
+    that a comparison also tells +0.0 from -0.0."""
+    S1, S2, n, var, L = stats
+    f = lambda v: int(np.float64(v).view(np.uint64))
+    return (f(S1), f(S2), int(n), f(var), int(L))
+
+
 def to_device(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
 
