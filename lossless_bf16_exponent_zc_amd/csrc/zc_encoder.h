@@ -87,11 +87,12 @@ __device__ __forceinline__ void moments8_full(const u32x4 w, double& s1, double&
 }
 
 // The same sums with Inf/NaN values taken as +0.0 and positions at or past
-// n as -0.0 (the sum's identity: beyond the data the tree has no leaves;
-// the window kernel restores the +0.0 padding's one effect, the sign of a
-// zero sum), and the count of the finite values; values base .. base + 3.
-__device__ __forceinline__ uint32_t moments4_careful(uint32_t w0, uint32_t w1, uint64_t base,
-                                                     uint64_t n, double& a01, double& q01) {
+// the data's end as -0.0 (the sum's identity: beyond the data the tree has
+// no leaves; the window kernel restores the +0.0 padding's one effect, the
+// sign of a zero sum), and the count of the finite values.  rem: how many of
+// the four values lie before the end (0..4 or more).
+__device__ __forceinline__ uint32_t moments4_careful(uint32_t w0, uint32_t w1, uint32_t rem,
+                                                     double& a01, double& q01) {
     const uint32_t wd[2] = {w0, w1};
     double v[4];
     uint32_t cnt = 0;
@@ -99,7 +100,7 @@ __device__ __forceinline__ uint32_t moments4_careful(uint32_t w0, uint32_t w1, u
     for (int i = 0; i < 4; ++i) {
         const uint32_t d = wd[i >> 1];
         const float f = __uint_as_float((i & 1) ? (d & 0xFFFF0000u) : (d << 16));
-        const bool in = base + i < n, ok = in && __builtin_isfinite(f);
+        const bool in = (uint32_t)i < rem, ok = in && __builtin_isfinite(f);
         v[i] = ok ? (double)f : (in ? 0.0 : -0.0);
         cnt += ok ? 1u : 0u;
     }
@@ -108,12 +109,13 @@ __device__ __forceinline__ uint32_t moments4_careful(uint32_t w0, uint32_t w1, u
     return cnt;
 }
 
-__device__ __forceinline__ uint32_t moments8_careful(const u32x4 w, uint64_t base, uint64_t n,
-                                                     double& s1, double& s2) {
+// rem: values of the 8 before the data's end (32-bit group-local arithmetic).
+__device__ __forceinline__ uint32_t moments8_careful(const u32x4 w, uint32_t rem, double& s1,
+                                                     double& s2) {
     double a0, q0, a1, q1;
-    uint32_t c = moments4_careful(w[0], w[1], base, n, a0, q0);
+    uint32_t c = moments4_careful(w[0], w[1], rem, a0, q0);
     __builtin_amdgcn_sched_barrier(0);
-    c += moments4_careful(w[2], w[3], base + 4, n, a1, q1);
+    c += moments4_careful(w[2], w[3], rem > 4 ? rem - 4 : 0u, a1, q1);
     s1 = a0 + a1;
     s2 = q0 + q1;
     return c;
@@ -128,8 +130,7 @@ __device__ __forceinline__ uint32_t moments8_careful(const u32x4 w, uint64_t bas
 // needs no count; otherwise the careful sums leave values past n and
 // non-finite ones out (as +0.0) and count the others.
 __device__ __forceinline__ void run_moments(const u32x4* area, uint32_t lane, uint32_t t,
-                                            uint64_t base, uint64_t n, bool full, double& r1,
-                                            double& r2, uint32_t& cnt) {
+                                            uint32_t valid, double& r1, double& r2, uint32_t& cnt) {
     const u32x4 w = area[tslot(4 * lane + t)];
     // an Inf or NaN among the 8 values (exponent field 255: adding 0x80 to a
     // half's masked exponent bits carries into its top bit only then) or a
@@ -138,24 +139,26 @@ __device__ __forceinline__ void run_moments(const u32x4* area, uint32_t lane, ui
 #pragma unroll
     for (int m = 0; m < 4; ++m) top |= (w[m] & 0x7F807F80u) + 0x00800080u;
     uint32_t c = 8;
-    if (full && (top & 0x80008000u) == 0)
+    if (valid == kGroup && (top & 0x80008000u) == 0) {
         moments8_full(w, r1, r2);
-    else
-        c = moments8_careful(w, base + 8 * t, n, r1, r2);
+    } else {
+        const uint32_t start = 32u * lane + 8u * t;  // the run's first value in the group
+        c = moments8_careful(w, valid > start ? valid - start : 0u, r1, r2);
+    }
     cnt += c;
     __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ void group_moments(const u32x4* area, uint32_t lane, uint64_t base,
-                                              uint64_t n, bool full, double& g1, double& g2,
-                                              uint32_t& gn) {
+// valid: the group's values before the data's end (2048 for a full group).
+__device__ __forceinline__ void group_moments(const u32x4* area, uint32_t lane, uint32_t valid,
+                                              double& g1, double& g2, uint32_t& gn) {
     uint32_t cnt = 0;
     double a1, a2, b1, b2;
-    run_moments(area, lane, 0, base, n, full, a1, a2, cnt);
-    run_moments(area, lane, 1, base, n, full, b1, b2, cnt);
+    run_moments(area, lane, 0, valid, a1, a2, cnt);
+    run_moments(area, lane, 1, valid, b1, b2, cnt);
     const double h1 = a1 + b1, h2 = a2 + b2;
-    run_moments(area, lane, 2, base, n, full, a1, a2, cnt);
-    run_moments(area, lane, 3, base, n, full, b1, b2, cnt);
+    run_moments(area, lane, 2, valid, a1, a2, cnt);
+    run_moments(area, lane, 3, valid, b1, b2, cnt);
     g1 = wave_tree(h1 + (a1 + b1));
     g2 = wave_tree(h2 + (a2 + b2));
     gn = wave_sum(cnt);
@@ -223,8 +226,9 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
 #pragma unroll
                 for (int k = 0; k < 4; ++k) s_area[wave][tslot(64 * k + lane)] = w[q][k];
                 __builtin_amdgcn_wave_barrier();
-                group_moments(s_area[wave], lane, (uint64_t)kGroup * g + 32u * lane, sd.n,
-                              (uint64_t)kGroup * (g + 1) <= sd.n, m1[q], m2[q], mn[q]);
+                const uint64_t left = sd.n - (uint64_t)kGroup * g;
+                group_moments(s_area[wave], lane, left < kGroup ? (uint32_t)left : kGroup,
+                              m1[q], m2[q], mn[q]);
                 asm volatile("" ::: "memory");  // reload below: no forwarding of the stored words
 #pragma unroll
                 for (int k = 0; k < 4; ++k) w[q][k] = s_area[wave][tslot(64 * k + lane)];
