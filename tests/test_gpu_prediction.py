@@ -134,3 +134,16 @@ def test_split_event_fixed_regions_final():
             h, f = early[s]
             assert torch.equal(h, out[so:so + h.numel()]), (call, s, "header/table")
             assert torch.equal(f, out[so + plan.code_offset(s):so + plan.escape_offset(s)]), (call, s)
+
+
+def test_many_small_chunks():
+    # 2048-value chunks over 32M values: 16,385 chunks (the chunk table goes
+    # through its table-resident path, 64+ chunks per thread) and 16,385
+    # moment blocks (8 rounds in the window kernel's reduction); fresh
+    # workspace (the window kernel codes again), then the predicted path
+    x = W.gradient((1 << 25) + 555, seed=25)
+    plan = Plan([x.size], 2048)
+    ws = plan.empty_workspace()
+    ws.zero_()
+    for _ in range(2):
+        check([x], plan, ws, chunk=2048)
