@@ -25,6 +25,8 @@ MAGIC = 0x3142435A
 GROUP = 2048
 FMT_MAGIC, FMT_WINDOW, FMT_SHAPE, FMT_SIZE = 0x01, 0x02, 0x04, 0x08
 FMT_TABLE, FMT_COUNT, FMT_PAD = 0x10, 0x20, 0x40
+FLAG_RAW = 0x01          # header flags: a raw stream
+OPT_RAW_FALLBACK = 0x01  # compress option: raw when the coded stream is longer
 
 
 def lib():
@@ -55,6 +57,10 @@ def lib():
         L.zco_compress.argtypes = [u16p, ctypes.c_uint64, ctypes.c_uint32,
                                    ctypes.c_int, u8p, ctypes.c_uint64, u64p]
         L.zco_compress.restype = ctypes.c_int
+        L.zco_compress_ex.argtypes = [u16p, ctypes.c_uint64, ctypes.c_uint32,
+                                      ctypes.c_int, ctypes.c_uint32, u8p,
+                                      ctypes.c_uint64, u64p]
+        L.zco_compress_ex.restype = ctypes.c_int
         L.zco_decompress.argtypes = [u8p, ctypes.c_uint64, ctypes.c_uint64,
                                      ctypes.c_uint32, u16p]
         L.zco_decompress.restype = ctypes.c_uint32
@@ -126,15 +132,18 @@ def max_stream_bytes(N, C=65536):
     return lib().zco_max_stream_bytes(N, C)
 
 
-def compress(x, C=65536, L=None) -> bytes:
-    """Compress one tensor of BF16 bits; L forces the window (1..248)."""
+def compress(x, C=65536, L=None, raw_fallback=False) -> bytes:
+    """Compress one tensor of BF16 bits; L forces the window (1..248);
+    raw_fallback stores the words as they are when coding would not shrink
+    them."""
     x = _u16(x)
-    cap = max_stream_bytes(x.size, C)
+    cap = max(max_stream_bytes(x.size, C), 64 + 2 * x.size)
     out = np.zeros(cap, dtype=np.uint8)
     n = ctypes.c_uint64()
-    rc = lib().zco_compress(_ptr(x, ctypes.c_uint16), x.size, C,
-                            -1 if L is None else int(L),
-                            _ptr(out, ctypes.c_uint8), cap, ctypes.byref(n))
+    rc = lib().zco_compress_ex(_ptr(x, ctypes.c_uint16), x.size, C,
+                               -1 if L is None else int(L),
+                               OPT_RAW_FALLBACK if raw_fallback else 0,
+                               _ptr(out, ctypes.c_uint8), cap, ctypes.byref(n))
     if rc != 0:
         raise ValueError(f"zco_compress failed with {rc}")
     return out[: n.value].tobytes()

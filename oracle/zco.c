@@ -269,11 +269,46 @@ static uint64_t get_u64(const uint8_t *b)
     return v;
 }
 
+/* ------------------------------------------------------------------ */
+/* Raw streams.  The ZipCCL notes ("Key idea and contribution", third   */
+/* technique) switch between the compressed and the native path by the  */
+/* compression benefit.  Per stream this reads as: when the coded stream */
+/* would be longer than the values themselves, send them as they are.   */
+/* A raw stream is the 64-byte header with flags = 1, L = 0, E = 0,      */
+/* total = 64 + 2N and the three region offsets 0, followed by the N    */
+/* BF16 words, little-endian, from byte 64.  Compression picks it only  */
+/* when asked to (ZCO_OPT_RAW_FALLBACK) and only when the coded total is */
+/* strictly larger; decoders always accept both kinds.                 */
+/* ------------------------------------------------------------------ */
+static uint64_t raw_total(uint64_t N) { return ZCO_HEADER_BYTES + 2u * N; }
+
+static void write_raw(const uint16_t *x, uint64_t N, uint32_t C, uint8_t *out)
+{
+    memset(out, 0, ZCO_HEADER_BYTES);
+    put_u32(out + 0, ZCO_MAGIC);
+    put_u16(out + 4, ZCO_VERSION);
+    out[6] = 0;
+    out[7] = ZCO_FLAG_RAW;
+    put_u64(out + 8, N);
+    put_u32(out + 16, C);
+    put_u32(out + 20, (uint32_t)ceil_div(N, C));
+    put_u64(out + 24, 0);
+    put_u64(out + 32, raw_total(N));
+    for (uint64_t i = 0; i < N; ++i)
+        put_u16(out + ZCO_HEADER_BYTES + 2u * i, x[i]);
+}
+
 int zco_compress(const uint16_t *x, uint64_t N, uint32_t C, int forced_L,
                  uint8_t *out, uint64_t cap, uint64_t *out_len)
 {
+    return zco_compress_ex(x, N, C, forced_L, 0u, out, cap, out_len);
+}
+
+int zco_compress_ex(const uint16_t *x, uint64_t N, uint32_t C, int forced_L,
+                    uint32_t options, uint8_t *out, uint64_t cap, uint64_t *out_len)
+{
     if (!chunk_ok(C) || (forced_L >= 0 && (forced_L < 1 || forced_L > 248)) ||
-        N >= ((uint64_t)1 << 32))
+        N >= ((uint64_t)1 << 32) || (options & ~ZCO_OPT_RAW_FALLBACK) != 0)
         return -1;
 
     /* 1. window from the standard deviation, or the forced one */
@@ -294,6 +329,14 @@ int zco_compress(const uint16_t *x, uint64_t N, uint32_t C, int forced_L,
     uint64_t K = ceil_div(N, C), G = ceil_div(N, ZCO_GROUP);
     uint64_t code_off = zco_code_off(N, C), sm_off = zco_sm_off(N, C);
     uint64_t esc_off = zco_esc_off(N, C), total = esc_off + E;
+    if ((options & ZCO_OPT_RAW_FALLBACK) && total > raw_total(N)) {
+        if (out_len)
+            *out_len = raw_total(N);
+        if (raw_total(N) > cap)
+            return -2;
+        write_raw(x, N, C, out);
+        return 0;
+    }
     if (out_len)
         *out_len = total;
     if (total > cap)
@@ -358,6 +401,28 @@ static unsigned code_at(const uint8_t *s, uint64_t code_off, uint64_t i)
     return c;
 }
 
+/* A raw stream: header fields as write_raw sets them, then the words. */
+static uint32_t decompress_raw(const uint8_t *s, uint64_t len, uint64_t N, uint32_t C,
+                               uint16_t *out)
+{
+    uint32_t bad = 0;
+    if (get_u32(s) != ZCO_MAGIC || get_u16(s + 4) != ZCO_VERSION)
+        bad |= ZCO_FMT_MAGIC;
+    if (s[6] != 0)
+        bad |= ZCO_FMT_WINDOW;
+    if (!chunk_ok(C) || get_u64(s + 8) != N || get_u32(s + 16) != C ||
+        get_u32(s + 20) != ceil_div(N, C) || get_u64(s + 40) != 0 ||
+        get_u64(s + 48) != 0 || get_u64(s + 56) != 0)
+        bad |= ZCO_FMT_SHAPE;
+    if (get_u64(s + 24) != 0 || get_u64(s + 32) != raw_total(N) || raw_total(N) > len)
+        bad |= ZCO_FMT_SIZE;
+    if (bad)
+        return bad;
+    for (uint64_t i = 0; i < N; ++i)
+        out[i] = get_u16(s + ZCO_HEADER_BYTES + 2u * i);
+    return 0;
+}
+
 uint32_t zco_decompress(const uint8_t *s, uint64_t len, uint64_t N, uint32_t C,
                         uint16_t *out)
 {
@@ -366,6 +431,8 @@ uint32_t zco_decompress(const uint8_t *s, uint64_t len, uint64_t N, uint32_t C,
 
     /* header checks */
     uint32_t bad = 0;
+    if (s[7] == ZCO_FLAG_RAW)
+        return decompress_raw(s, len, N, C, out);
     if (get_u32(s) != ZCO_MAGIC || get_u16(s + 4) != ZCO_VERSION || s[7] != 0)
         bad |= ZCO_FMT_MAGIC;
     unsigned L = s[6];

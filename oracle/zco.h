@@ -33,6 +33,10 @@ extern "C" {
 #define ZCO_HEADER_BYTES 64u
 #define ZCO_GROUP        2048u       /* values per code group */
 #define ZCO_ESC          7u          /* the escape code */
+#define ZCO_FLAG_RAW     1u          /* header flags: the values stored as they are */
+
+/* Compression options (zco_compress_ex). */
+#define ZCO_OPT_RAW_FALLBACK 1u /* a raw stream when the coded one is longer */
 
 /* Decoder rejection bits (zco_decompress return value; 0 = accepted). */
 #define ZCO_FMT_MAGIC    0x01u  /* magic, version or flags wrong            */
@@ -74,6 +78,12 @@ uint64_t zco_max_stream_bytes(uint64_t N, uint32_t C);
  * Returns 0 on success, -1 on a bad argument, -2 if cap is too small. */
 int zco_compress(const uint16_t *x, uint64_t N, uint32_t C, int forced_L,
                  uint8_t *out, uint64_t cap, uint64_t *out_len);
+
+/* As zco_compress, with options (ZCO_OPT_*): with ZCO_OPT_RAW_FALLBACK a
+ * tensor whose coded stream would exceed 64 + 2N bytes is stored as a raw
+ * stream (header flags = 1, the N words after the header). */
+int zco_compress_ex(const uint16_t *x, uint64_t N, uint32_t C, int forced_L,
+                    uint32_t options, uint8_t *out, uint64_t cap, uint64_t *out_len);
 
 /* Decode one stream of `len` readable bytes that must hold N values coded
  * with chunk size C.  Returns 0 and fills out[0..N) when the stream is

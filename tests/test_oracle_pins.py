@@ -378,7 +378,10 @@ def _mutations(s, N):
     out = []
     b = bytearray(s); b[0] ^= 1; out.append(("magic", bytes(b), oracle.FMT_MAGIC))
     b = bytearray(s); b[4] = 2; out.append(("version", bytes(b), oracle.FMT_MAGIC))
-    b = bytearray(s); b[7] = 1; out.append(("flags", bytes(b), oracle.FMT_MAGIC))
+    b = bytearray(s); b[7] = 2; out.append(("flags", bytes(b), oracle.FMT_MAGIC))
+    # flags = 1 declares a raw stream: a coded header fails its checks
+    b = bytearray(s); b[7] = 1
+    out.append(("raw flag", bytes(b), oracle.FMT_WINDOW | oracle.FMT_SHAPE | oracle.FMT_SIZE))
     b = bytearray(s); b[6] = 0; out.append(("L=0", bytes(b), oracle.FMT_WINDOW))
     b = bytearray(s); b[6] = 249; out.append(("L=249", bytes(b), oracle.FMT_WINDOW))
     b = bytearray(s); b[8] ^= 1; out.append(("N", bytes(b), oracle.FMT_SHAPE))
@@ -435,3 +438,112 @@ def test_gaussian_escape_band():
     assert 0.0212 <= rate <= 0.0303 + 0.001  # Gaussian model: 2.13%..3.03%
     assert h["L"] == 116
     assert 1.42 < 2 * x.size / h["total"] < 16 / 11
+
+
+# --------------------------------------------------------------------------
+# Raw streams: the compressed/native switch of the ZipCCL notes ("Key idea
+# and contribution", third technique) taken per stream: with the raw
+# fallback, a tensor whose coded stream would be longer than 64 + 2N bytes
+# is stored as a 64-byte header (flags 1, L 0, E 0, offsets 0) and its words.
+# --------------------------------------------------------------------------
+def _raw_by_hand(x, C):
+    N = x.size
+    head = struct.pack("<IHBBQIIQQQQQ", oracle.MAGIC, 1, 0, 1, N, C, -(-N // C), 0,
+                       64 + 2 * N, 0, 0, 0)
+    assert len(head) == 64
+    return head + x.astype("<u2").tobytes()
+
+
+def _coded_size(x, C, L):
+    N = x.size
+    e = (x.astype(np.int64) >> 7) & 0xFF
+    E = int(((e < L) | (e > L + 6)).sum())
+    K, G = -(-N // C), -(-N // 2048)
+    return _a256(64 + 4 * (K + 1) + 2 * G) + 2816 * G + E
+
+
+def test_raw_stream_layout_by_hand():
+    # all zeros: var 0 -> L 1, and every zero escapes (exponent 0)
+    for N, C in [(0, 2048), (1, 2048), (5000, 2048), (70001, 65536)]:
+        x = np.zeros(N, dtype=np.uint16)
+        s = oracle.compress(x, C=C, raw_fallback=True)
+        assert s == _raw_by_hand(x, C), N
+        assert np.array_equal(oracle.decompress(s, N, C), x)
+        # without the fallback the same tensor keeps the coded form
+        assert oracle.parse_header(oracle.compress(x, C=C))["flags"] == 0
+
+
+@pytest.mark.parametrize("extra", [0, 1])
+def test_raw_switch_at_the_break_even_size(extra):
+    # forced window 127: 1.0 (exponent 127) codes, 0x0001 (exponent 0) escapes.
+    # N = 8192, C = 8192: fixed part 256 + 4 * 2816 = 11520 bytes, raw 16448,
+    # so E = 4928 ties (stays coded) and one escape more goes raw.
+    N, C, L = 8192, 8192, 127
+    E = 16448 - 11520 + extra
+    x = np.full(N, 0x3F80, dtype=np.uint16)
+    x[np.random.default_rng(3).permutation(N)[:E]] = 0x0001
+    assert _coded_size(x, C, L) == 16448 + extra
+    s = oracle.compress(x, C=C, L=L, raw_fallback=True)
+    assert len(s) == 16448
+    if extra:
+        assert s == _raw_by_hand(x, C)
+    else:
+        assert s == oracle.compress(x, C=C, L=L)
+    assert np.array_equal(oracle.decompress(s, N, C), x)
+
+
+@pytest.mark.parametrize("N", [0, 1, 7, 1000, 1500, 2047, 2048, 2049, 4096, 3 * 2048 + 5, 65536])
+def test_raw_fallback_picks_the_shorter(N):
+    x = W.small(N, seed=40 + N) if N else np.zeros(0, dtype=np.uint16)
+    for C in (2048, 65536):
+        L = oracle.parse_header(oracle.compress(x, C=C))["L"]
+        coded = _coded_size(x, C, L)
+        s = oracle.compress(x, C=C, raw_fallback=True)
+        assert len(s) == min(coded, 64 + 2 * N), (N, C)
+        assert oracle.parse_header(s)["flags"] == (1 if coded > 64 + 2 * N else 0)
+        assert np.array_equal(oracle.decompress(s, N, C), x)
+
+
+def test_raw_round_trip_every_pattern():
+    # uniform bit patterns: 7 exponents of 256 code, the rest escape -> raw
+    allp = np.arange(65536, dtype=np.uint16)
+    for x in (allp, np.random.default_rng(9).permutation(allp)):
+        s = oracle.compress(x, C=8192, raw_fallback=True)
+        assert s == _raw_by_hand(x, 8192)
+        assert np.array_equal(oracle.decompress(s, x.size, 8192), x)
+
+
+def test_raw_header_rejections():
+    N, C = 3000, 2048
+    x = np.random.default_rng(5).integers(0, 65536, N, dtype=np.uint16)
+    s = oracle.compress(x, C=C, raw_fallback=True)
+    assert oracle.parse_header(s)["flags"] == 1
+    cases = [(0, 0x01, oracle.FMT_MAGIC), (4, 0x02, oracle.FMT_MAGIC),
+             (6, 0x05, oracle.FMT_WINDOW), (8, 0x01, oracle.FMT_SHAPE),
+             (16, 0x01, oracle.FMT_SHAPE), (20, 0x01, oracle.FMT_SHAPE),
+             (40, 0x01, oracle.FMT_SHAPE), (48, 0x10, oracle.FMT_SHAPE),
+             (56, 0x01, oracle.FMT_SHAPE), (24, 0x01, oracle.FMT_SIZE),
+             (32, 0x01, oracle.FMT_SIZE)]
+    for off, xor, bit in cases:
+        b = bytearray(s)
+        b[off] ^= xor
+        bad, _ = oracle.decompress_status(bytes(b), N, C)
+        assert bad == bit, (off, bad)
+    assert oracle.decompress_status(s[:-1], N, C)[0] == oracle.FMT_SIZE
+    # unknown flags: rejected as a coded header with a bad flags byte
+    b = bytearray(s); b[7] = 2
+    assert oracle.decompress_status(bytes(b), N, C)[0] & oracle.FMT_MAGIC
+
+
+def test_reduce_over_raw_and_coded_shards():
+    sh = W.shards(n=10000, nshards=4)
+    sh[1] = np.random.default_rng(11).integers(0, 65536, 10000, dtype=np.uint16)
+    sh[1][(sh[1] & 0x7F80) == 0x7F80] = 0  # no Inf/NaN in the uniform shard
+    streams = [oracle.compress(s, C=8192, raw_fallback=True) for s in sh]
+    flags = [oracle.parse_header(t)["flags"] for t in streams]
+    assert flags == [0, 1, 0, 0]
+    got = oracle.decompress_reduce(streams, 10000, C=8192)
+    acc = (sh[0].astype(np.uint32) << 16).view(np.float32).copy()
+    for s in sh[1:]:
+        acc = acc + (s.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(got, _round_torch(acc))
