@@ -23,6 +23,15 @@
  *   u64 N @8, u32 C @16, u32 K @20, u64 E @24, u64 total @32,
  *   u64 code_off @40, u64 sm_off @48, u64 esc_off @56.
  *
+ * A raw stream (only from plans made with ZC_PLAN_RAW_FALLBACK) has flags 1,
+ * L 0, E 0, total 64 + 2N and the three offsets 0, and holds the N BF16
+ * words as they are from byte 64.  It is written when the coded stream
+ * would be longer (ties stay coded): mostly zeros, near-uniform bit
+ * patterns, tensors of a few thousand values.  This is the notes' switch
+ * between the compressed and the native path by compression benefit
+ * (technique 3 of the same section), taken per stream.  Decoders accept
+ * both kinds whatever their plan's flags.
+ *
  * Conventions for every call below:
  *  - "d_" pointers are device memory owned by the caller; the library never
  *    frees, keeps or reallocates them.  Host pointers are read during the
@@ -87,10 +96,24 @@ const char *zc_status_string(zc_status s);
  */
 zc_status zc_plan_create(uint32_t num_segments, const uint64_t *segment_elems,
                          uint32_t chunk_elems, zc_plan **out_plan);
+
+/* Plan flags. */
+#define ZC_PLAN_RAW_FALLBACK 0x1u /* compress writes a raw stream for a segment
+                                     whose coded stream would exceed 64 + 2N
+                                     bytes (see the format above) */
+
+/* zc_plan_create with flags (0 or ZC_PLAN_RAW_FALLBACK; other bits:
+ * ZC_ERR_INVALID_ARG).  The raw copy happens in the escape-placement
+ * kernel, after the header is written, so the compress call's work stays
+ * the same three kernels; a raw segment costs one more pass over its
+ * values. */
+zc_status zc_plan_create_ex(uint32_t num_segments, const uint64_t *segment_elems,
+                            uint32_t chunk_elems, uint32_t flags, zc_plan **out_plan);
 void zc_plan_destroy(zc_plan *plan);
 
 uint32_t zc_plan_num_segments(const zc_plan *plan);
 uint32_t zc_plan_chunk_elems(const zc_plan *plan);
+uint32_t zc_plan_flags(const zc_plan *plan);
 /* BF16 element offset of segment s (a multiple of 8) and total elements. */
 uint64_t zc_plan_input_offset(const zc_plan *plan, uint32_t s);
 uint64_t zc_plan_input_elems(const zc_plan *plan);
@@ -144,7 +167,9 @@ zc_status zc_compress_window(const zc_plan *plan, const void *d_in, void *d_out,
  * region are final when the call's work completes.  A caller can wait on the
  * event from another stream and start the size exchange and the sending of
  * those regions while the escapes are still being placed (ZipCCL's
- * static/dynamic split, Fig. 5).
+ * static/dynamic split, Fig. 5).  Plans with ZC_PLAN_RAW_FALLBACK are
+ * refused (ZC_ERR_INVALID_ARG): a raw stream's bytes are written after the
+ * event.
  */
 zc_status zc_compress_split(const zc_plan *plan, const void *d_in, void *d_out,
                             uint64_t out_capacity, uint64_t *d_stream_bytes,

@@ -19,8 +19,9 @@ FMT_BITS = {0x01: "magic", 0x02: "window", 0x04: "shape", 0x08: "size",
 
 # Every symbol include/zc.h declares.
 EXPORTS = (
-    "zc_version", "zc_status_string", "zc_plan_create", "zc_plan_destroy",
-    "zc_plan_num_segments", "zc_plan_chunk_elems", "zc_plan_input_offset",
+    "zc_version", "zc_status_string", "zc_plan_create", "zc_plan_create_ex",
+    "zc_plan_destroy", "zc_plan_num_segments", "zc_plan_chunk_elems", "zc_plan_flags",
+    "zc_plan_input_offset",
     "zc_plan_input_elems", "zc_plan_stream_offset", "zc_plan_max_stream_bytes",
     "zc_plan_code_offset", "zc_plan_escape_offset",
     "zc_plan_out_bytes", "zc_plan_workspace_bytes", "zc_compress",
@@ -54,9 +55,11 @@ def lib() -> ctypes.CDLL:
     L.zc_status_string.argtypes = [ctypes.c_int]
     L.zc_status_string.restype = ctypes.c_char_p
     L.zc_plan_create.argtypes = [u32, P(u64), u32, P(vp)]
+    L.zc_plan_create_ex.argtypes = [u32, P(u64), u32, u32, P(vp)]
     L.zc_plan_destroy.argtypes = [vp]
     L.zc_plan_destroy.restype = None
     for name, rt in (("zc_plan_num_segments", u32), ("zc_plan_chunk_elems", u32),
+                     ("zc_plan_flags", u32),
                      ("zc_plan_input_elems", u64), ("zc_plan_out_bytes", u64),
                      ("zc_plan_workspace_bytes", u64)):
         f = getattr(L, name)
@@ -80,7 +83,7 @@ def lib() -> ctypes.CDLL:
     L.zc_read_sigma.argtypes = [vp, vp, u32, vp, P(ctypes.c_double),
                                 P(ctypes.c_double), P(u64), P(ctypes.c_double),
                                 P(u32)]
-    for name in ("zc_plan_create", "zc_compress", "zc_compress_window", "zc_compress_timed",
+    for name in ("zc_plan_create", "zc_plan_create_ex", "zc_compress", "zc_compress_window", "zc_compress_timed",
                  "zc_compress_split",
                  "zc_decompress", "zc_decompress_reduce", "zc_read_status",
                  "zc_read_sigma"):
@@ -121,18 +124,25 @@ def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
 
-class Plan:
-    """A codec plan: segment sizes and chunk size, plus its device tables."""
+PLAN_RAW_FALLBACK = 0x1  # ZC_PLAN_RAW_FALLBACK
 
-    def __init__(self, segment_elems, chunk_elems: int = 65536):
+
+class Plan:
+    """A codec plan: segment sizes and chunk size, plus its device tables.
+    raw_fallback: compress stores a segment as a raw stream (its words after
+    the header) when the coded stream would be longer."""
+
+    def __init__(self, segment_elems, chunk_elems: int = 65536, raw_fallback: bool = False):
         sizes = [int(n) for n in segment_elems]
         arr = (ctypes.c_uint64 * len(sizes))(*sizes)
         h = ctypes.c_void_p()
-        _check(lib().zc_plan_create(len(sizes), arr, chunk_elems, ctypes.byref(h)),
-               "zc_plan_create")
+        flags = PLAN_RAW_FALLBACK if raw_fallback else 0
+        _check(lib().zc_plan_create_ex(len(sizes), arr, chunk_elems, flags, ctypes.byref(h)),
+               "zc_plan_create_ex")
         self._h = h
         self.segment_elems = sizes
         self.chunk_elems = lib().zc_plan_chunk_elems(h)
+        self.flags = lib().zc_plan_flags(h)
 
     def close(self):
         if getattr(self, "_h", None):

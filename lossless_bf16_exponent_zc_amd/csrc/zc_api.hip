@@ -27,7 +27,7 @@
 using namespace zc;
 
 struct zc_plan {
-    uint32_t nseg = 0, chunk = 0, block = 0;
+    uint32_t nseg = 0, chunk = 0, block = 0, flags = 0;
     std::vector<SegDesc> segs;
     std::vector<ItemDesc> chunks, groups, pairs, witems;  // pairs: encoder waves; witems: window workgroups
     uint64_t input_elems = 0, out_bytes = 0;
@@ -103,7 +103,7 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     }
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return ZC_ERR_HIP;
     WindowArgs wa{ea, p->d_witems, ws_ptr<SegStat>(p, d_ws, p->ws.stats), d_stream_bytes,
-                  p->chunk, p->chunk / p->block};
+                  p->chunk, p->chunk / p->block, (p->flags & ZC_PLAN_RAW_FALLBACK) ? 1u : 0u};
     hipLaunchKernelGGL(zc_window, dim3((uint32_t)p->witems.size()), dim3(256), 0, stream, wa);
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return ZC_ERR_HIP;
     // after the window kernel: codes and sm bytes (coded again there when
@@ -113,7 +113,7 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     uint8_t* staging = ea.staging;
     uint32_t* gcnt = ea.gcnt;
     if (nchunks(p)) {
-        PlaceArgs pa{p->d_segs, p->d_chunks, out, staging, gcnt, p->chunk, nchunks(p),
+        PlaceArgs pa{p->d_segs, p->d_chunks, out, staging, gcnt, ea.in, p->chunk, nchunks(p),
                      p->nseg == 1, p->segs[0]};
         const uint32_t gpc = p->chunk / kGroup;
         // placement: up to 4 waves, each with gpc / waves groups
@@ -151,8 +151,14 @@ const char* zc_status_string(zc_status s) {
 
 zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, uint32_t chunk_elems,
                          zc_plan** out_plan) {
+    return zc_plan_create_ex(num_segments, segment_elems, chunk_elems, 0u, out_plan);
+}
+
+zc_status zc_plan_create_ex(uint32_t num_segments, const uint64_t* segment_elems, uint32_t chunk_elems,
+                            uint32_t flags, zc_plan** out_plan) {
     if (!out_plan || num_segments == 0 || !segment_elems) return ZC_ERR_INVALID_ARG;
     *out_plan = nullptr;
+    if (flags & ~ZC_PLAN_RAW_FALLBACK) return ZC_ERR_INVALID_ARG;
     const uint32_t C = chunk_elems ? chunk_elems : 65536u;
     if (C < kGroup || C > 65536u || (C & (C - 1))) return ZC_ERR_UNSUPPORTED;
 
@@ -160,6 +166,7 @@ zc_status zc_plan_create(uint32_t num_segments, const uint64_t* segment_elems, u
     if (!p) return ZC_ERR_HIP;
     p->nseg = num_segments;
     p->chunk = C;
+    p->flags = flags;
     p->block = C < kSigmaBlock ? C : kSigmaBlock;
     uint64_t in_off = 0, out_off = 0, sb = 0;
     for (uint32_t s = 0; s < num_segments; ++s) {
@@ -256,6 +263,7 @@ void zc_plan_destroy(zc_plan* p) {
 
 uint32_t zc_plan_num_segments(const zc_plan* p) { return p ? p->nseg : 0; }
 uint32_t zc_plan_chunk_elems(const zc_plan* p) { return p ? p->chunk : 0; }
+uint32_t zc_plan_flags(const zc_plan* p) { return p ? p->flags : 0; }
 uint64_t zc_plan_input_offset(const zc_plan* p, uint32_t s) {
     return p && s < p->nseg ? p->segs[s].in_off : 0;
 }
@@ -283,7 +291,8 @@ zc_status zc_compress(const zc_plan* p, const void* d_in, void* d_out, uint64_t 
 zc_status zc_compress_split(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
                             uint64_t* d_stream_bytes, void* d_ws, uint64_t ws_bytes,
                             hipStream_t stream, hipEvent_t fixed_ready) {
-    if (!fixed_ready) return ZC_ERR_INVALID_ARG;
+    // a raw stream rewrites its fixed regions after the event: no split then
+    if (!fixed_ready || !p || (p->flags & ZC_PLAN_RAW_FALLBACK)) return ZC_ERR_INVALID_ARG;
     return compress_impl(p, d_in, d_out, out_capacity, d_stream_bytes, 0, d_ws, ws_bytes, stream,
                          nullptr, fixed_ready);
 }

@@ -25,17 +25,36 @@ namespace {
 
 constexpr uint32_t kBadMagic = 0x01, kBadWindow = 0x02, kBadShape = 0x04, kBadSize = 0x08,
                    kBadTable = 0x10, kBadCount = 0x20, kBadPad = 0x40;
+// check_header's answer for a valid raw stream (no rejection bit: never stored)
+constexpr uint32_t kRawStream = 0x100;
 
 template <typename T>
 __device__ __forceinline__ T ld(const uint8_t* p) {
     return *reinterpret_cast<const T*>(p);
 }
 
+// A raw stream's header (flags 1): L 0, E 0, total 64 + 2N, offsets 0.
+__device__ __forceinline__ uint32_t check_raw_header(const uint8_t* st, uint64_t cap, const SegDesc& sd,
+                                                     uint32_t C, uint32_t w1) {
+    uint32_t bad = 0;
+    if (ld<uint32_t>(st) != kMagic || (w1 & 0xFFFFu) != kVersion) bad |= kBadMagic;
+    if (((w1 >> 16) & 0xFFu) != 0) bad |= kBadWindow;
+    if (ld<uint64_t>(st + 8) != sd.n || ld<uint32_t>(st + 16) != C || ld<uint32_t>(st + 20) != sd.k ||
+        (ld<uint64_t>(st + 40) | ld<uint64_t>(st + 48) | ld<uint64_t>(st + 56)) != 0)
+        bad |= kBadShape;
+    const uint64_t total = kHeaderBytes + 2ull * sd.n;
+    if (ld<uint64_t>(st + 24) != 0 || ld<uint64_t>(st + 32) != total || total > cap) bad |= kBadSize;
+    return bad ? bad : kRawStream;
+}
+
+// 0 for a valid coded header, kRawStream for a valid raw one, else the
+// rejection bits.
 __device__ __forceinline__ uint32_t check_header(const uint8_t* st, uint64_t cap, const SegDesc& sd,
                                                  uint32_t C) {
     if (cap < kHeaderBytes) return kBadSize;
     uint32_t bad = 0;
     const uint32_t w1 = ld<uint32_t>(st + 4);
+    if ((w1 >> 24) == kFlagRaw) return check_raw_header(st, cap, sd, C, w1);
     const uint32_t L = (w1 >> 16) & 0xFFu;
     if (ld<uint32_t>(st) != kMagic || (w1 & 0xFFFFu) != kVersion || (w1 >> 24) != 0) bad |= kBadMagic;
     if (L < 1 || L > 248) bad |= kBadWindow;
@@ -122,6 +141,27 @@ __device__ __forceinline__ void store_values(uint16_t* __restrict__ out, uint64_
         } else {
             for (uint32_t j = 0; j < 8; ++j)
                 if (b + j < n) out[b + j] = (uint16_t)(o[k][j >> 1] >> (16 * (j & 1)));
+        }
+    }
+}
+
+// The lane's four 8-value words of group g of a raw stream (the values
+// after the header, 64 + 2N bytes checked to be in the buffer); word k holds
+// values 2048 g + 512 k + 8 lane .. + 7, zeros past N.
+template <bool TAIL>
+__device__ __forceinline__ void raw_words(const uint8_t* st, uint64_t n, uint64_t g, uint32_t lane,
+                                          u32x4 (&o)[4]) {
+    const uint8_t* src = st + kHeaderBytes + 2ull * ((uint64_t)kGroup * g + 8u * lane);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint64_t b = (uint64_t)kGroup * g + 512u * k + 8u * lane;
+        if (!TAIL || b + 8 <= n) {
+            o[k] = ld<u32x4>(src + 1024 * k);
+        } else {
+            o[k] = u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (uint32_t j = 0; j < 8; ++j)
+                if (b + j < n) o[k][j >> 1] |= (uint32_t)ld<uint16_t>(src + 1024 * k + 2 * j) << (16 * (j & 1));
         }
     }
 }
@@ -264,8 +304,35 @@ __device__ __forceinline__ uint32_t decode_group_all(const DecodeArgs& a, const 
             fetch<!REDUCE>(nst, ncap, sd, a.chunk_elems, g, lane, nxt);
         }
 
+        // the group's values: summed in shard order, or stored
+        auto take = [&](const u32x4 (&o)[4]) {
+            if (REDUCE) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int mm = 0; mm < 4; ++mm) {
+                        const float lo = __uint_as_float(o[k][mm] << 16);
+                        const float hi = __uint_as_float(o[k][mm] & 0xFFFF0000u);
+                        float& a0 = acc[REDUCE ? 8 * k + 2 * mm : 0];
+                        float& a1 = acc[REDUCE ? 8 * k + 2 * mm + 1 : 0];
+                        a0 = s == 0 ? lo : a0 + lo;
+                        a1 = s == 0 ? hi : a1 + hi;
+                    }
+            } else {
+                store_values<TAIL>(a.out + sd.in_off, sd.n, g, lane, o);
+            }
+        };
+        // (the sum takes both kinds of stream at one join; the plain decoder
+        // stores on each path, which keeps it within its registers)
         uint32_t bad = cur.bad;
-        if (!bad) {
+        u32x4 o[4];
+        bool have = false;
+        if (bad == kRawStream) {  // uniform: a raw stream
+            bad = 0;
+            raw_words<TAIL>(st, sd.n, g, lane, o);
+            if (REDUCE) have = true;
+            else take(o);
+        } else if (!bad) {
             if (TAIL) {
                 const uint32_t V = valid_bits(lane, valid);
                 bool padbad = ((cur.P[0] | cur.P[1] | cur.P[2]) & ~V) != 0;
@@ -279,25 +346,12 @@ __device__ __forceinline__ uint32_t decode_group_all(const DecodeArgs& a, const 
             const uint32_t incl = wave_inclusive_scan(cnt);
             if (readlane(incl, 63) != cur.span) bad |= kBadCount;
             if (!bad) {
-                u32x4 o[4];
                 rebuild(cur, M, first + incl - cnt, escb, row, o);
-                if (REDUCE) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-#pragma unroll
-                        for (int mm = 0; mm < 4; ++mm) {
-                            const float lo = __uint_as_float(o[k][mm] << 16);
-                            const float hi = __uint_as_float(o[k][mm] & 0xFFFF0000u);
-                            float& a0 = acc[REDUCE ? 8 * k + 2 * mm : 0];
-                            float& a1 = acc[REDUCE ? 8 * k + 2 * mm + 1 : 0];
-                            a0 = s == 0 ? lo : a0 + lo;
-                            a1 = s == 0 ? hi : a1 + hi;
-                        }
-                } else {
-                    store_values<TAIL>(a.out + sd.in_off, sd.n, g, lane, o);
-                }
+                if (REDUCE) have = true;
+                else take(o);
             }
         }
+        if (REDUCE && have) take(o);
         bad_all |= bad;
         if (REDUCE && s + 1 < a.nstreams) {
             cur = nxt;
@@ -347,6 +401,10 @@ __device__ __forceinline__ uint32_t decode_one(const uint8_t* st, uint64_t cap, 
                                                uint32_t* esc_lds, u32x4* row, u32x4 (&o)[4]) {
     GroupData d;
     fetch<true>(st, cap, sd, C, g, lane, d);
+    if (d.bad == kRawStream) {  // uniform
+        raw_words<TAIL>(st, sd.n, g, lane, o);
+        return 0;
+    }
     uint32_t first = 0;
     if (!d.bad) first = fetch_escapes(st, cap, sd.esc_off + d.t0 + d.rel, d.span, lane, esc_lds);
     uint32_t bad = d.bad;

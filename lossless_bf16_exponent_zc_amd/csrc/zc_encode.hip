@@ -68,6 +68,28 @@ __global__ __launch_bounds__(256) void zc_encode(EncodeArgs a) {
 template __global__ void zc_encode<true>(EncodeArgs);
 template __global__ void zc_encode<false>(EncodeArgs);
 
+// Values [v0, min(n, v0 + C)) of a segment into its raw stream (after the
+// 64-byte header), 16-byte words, four in flight per thread.
+__device__ __forceinline__ void copy_raw_chunk(const uint16_t* __restrict__ in, uint8_t* st, uint64_t n,
+                                               uint64_t v0, uint32_t C) {
+    const uint32_t m = (uint32_t)min((uint64_t)C, n - v0), words = m / 8u;
+    const u32x4* src = reinterpret_cast<const u32x4*>(in + v0);
+    u32x4* dst = reinterpret_cast<u32x4*>(st + kHeaderBytes + 2ull * v0);
+    const uint32_t step = blockDim.x;
+    uint32_t i = threadIdx.x;
+    for (; i + 3 * step < words; i += 4 * step) {
+        u32x4 w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = src[i + u * step];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dst[i + u * step] = w[u];
+    }
+    for (; i < words; i += step) dst[i] = src[i];
+    const uint32_t j = 8u * words + threadIdx.x;  // the last partial word, value by value
+    if (threadIdx.x < 8 && j < m)
+        reinterpret_cast<uint16_t*>(st + kHeaderBytes)[v0 + j] = in[v0 + j];
+}
+
 // One workgroup of up to 4 waves per chunk; wave w owns the chunk's groups
 // w, w + nw, ... (GPW = groups per wave).  The chunk's escape run is
 // gathered in LDS at its final alignment modulo 16 and leaves in 16-byte
@@ -93,6 +115,9 @@ __device__ __forceinline__ void place_chunk(const PlaceArgs& a, uint32_t ci) {
     // waits only for them, not for the staging loads behind them
     const uint32_t l = cd.local;
     const uint32_t prefix = reinterpret_cast<const uint32_t*>(st + kHeaderBytes)[l];
+    // a raw stream (flags byte 1, set by the window kernel) takes the values
+    // as they are: no group table, no escapes (checked once the loads are in)
+    const bool raw = (reinterpret_cast<const uint32_t*>(st)[1] >> 24) == kFlagRaw;
     const uint32_t c_raw = a.gcnt[sd.group_base + gc0 + min(lane, ng - 1)];
 
     // source dwords of this wave's groups, loaded once (inside the slots); the
@@ -113,7 +138,7 @@ __device__ __forceinline__ void place_chunk(const PlaceArgs& a, uint32_t ci) {
         const uint32_t c = lane < ng ? c_raw : 0u;
         const uint32_t incl = wave_inclusive_scan(c);
         if (lane < ng) {
-            reinterpret_cast<uint16_t*>(st + sd.gtab_off)[gc0 + lane] = (uint16_t)(incl - c);
+            if (!raw) reinterpret_cast<uint16_t*>(st + sd.gtab_off)[gc0 + lane] = (uint16_t)(incl - c);
             s_gb[lane] = incl - c;
             s_gn[lane] = min(c, kGroup);
         }
@@ -134,6 +159,11 @@ __device__ __forceinline__ void place_chunk(const PlaceArgs& a, uint32_t ci) {
             const uint32_t sh = dpp<kDppWaveShl1>(lo[q][r]);
             hi[q][r] = lane == 63 ? nxt : sh;
         }
+    if (raw) {
+        copy_raw_chunk(a.in + sd.in_off, st, sd.n, (uint64_t)l * a.chunk_elems, a.chunk_elems);
+        lds_barrier();  // s_* are rewritten by the next chunk
+        return;
+    }
     const uint32_t pre = s_prefix, t = s_t;
     if (pre == 0xFFFFFFFFu) {
         lds_barrier();  // s_* are rewritten by the next chunk

@@ -25,6 +25,7 @@ constexpr uint32_t kGroup = 2048;
 constexpr uint32_t kHeaderBytes = 64;
 constexpr uint32_t kMagic = 0x3142435Au;  // "ZCB1"
 constexpr uint32_t kVersion = 1;
+constexpr uint32_t kFlagRaw = 1;  // header flags byte: the values stored as they are
 constexpr uint32_t kMaxStreams = 16;
 constexpr uint32_t kSigmaBlock = 16384;  // values per moment partial (or the chunk, if smaller)
 

@@ -30,6 +30,7 @@ struct WindowArgs {
     uint64_t* stream_bytes;
     uint32_t chunk_elems;
     uint32_t chunk_blocks;    // moment blocks per chunk: 1, 2 or 4
+    uint32_t raw_fallback;    // a raw stream when the coded one would be longer
 };
 
 struct PlaceArgs {
@@ -38,6 +39,7 @@ struct PlaceArgs {
     uint8_t* out;
     const uint8_t* staging;
     const uint32_t* gcnt;
+    const uint16_t* in;     // the values, copied into raw streams
     uint32_t chunk_elems;
     uint32_t nchunks;
     uint32_t single;        // one segment: seg0 is it, chunk i is (0, i)

@@ -245,4 +245,22 @@ __device__ __forceinline__ void write_static_header(uint8_t* st, const SegDesc& 
     *reinterpret_cast<uint64_t*>(st + 56) = sd.esc_off;
 }
 
+// Header of a raw stream (the values follow it as they are): flags 1, L 0,
+// E 0, total 64 + 2N, region offsets 0.  Written in place of the coded
+// header when coding would not shrink the tensor, the ZipCCL notes' switch
+// between the compressed and the native path by compression benefit
+// ("Key idea and contribution", third technique), taken per stream.
+__device__ __forceinline__ void write_raw_header(uint8_t* st, const SegDesc& sd, uint32_t C) {
+    *reinterpret_cast<uint32_t*>(st + 0) = kMagic;
+    *reinterpret_cast<uint32_t*>(st + 4) = kVersion | (kFlagRaw << 24);  // L byte = 0
+    *reinterpret_cast<uint64_t*>(st + 8) = sd.n;
+    *reinterpret_cast<uint32_t*>(st + 16) = C;
+    *reinterpret_cast<uint32_t*>(st + 20) = sd.k;
+    *reinterpret_cast<uint64_t*>(st + 24) = 0;
+    *reinterpret_cast<uint64_t*>(st + 32) = kHeaderBytes + 2ull * sd.n;
+    *reinterpret_cast<uint64_t*>(st + 40) = 0;
+    *reinterpret_cast<uint64_t*>(st + 48) = 0;
+    *reinterpret_cast<uint64_t*>(st + 56) = 0;
+}
+
 }  // namespace zc

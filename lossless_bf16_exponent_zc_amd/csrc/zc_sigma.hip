@@ -147,6 +147,11 @@ __device__ __forceinline__ void place_offsets(const WindowArgs& a, const SegDesc
     if (threadIdx.x == 0) {
         const uint64_t E = s_base;
         table[sd.k] = (uint32_t)E;
+        if (a.raw_fallback && sd.esc_off + E > kHeaderBytes + 2ull * sd.n) {
+            write_raw_header(st, sd, a.chunk_elems);  // the placement kernel copies the values
+            a.stream_bytes[seg] = kHeaderBytes + 2ull * sd.n;
+            return;
+        }
         *reinterpret_cast<uint64_t*>(st + 24) = E;
         *reinterpret_cast<uint64_t*>(st + 32) = sd.esc_off + E;
         a.stream_bytes[seg] = sd.esc_off + E;
@@ -217,7 +222,10 @@ __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
             ss.L = L;
             a.stats[seg] = ss;
             write_static_header(st, sd, a.chunk_elems, L);
-            if (sd.k == 0) {  // empty: chunk table entry 0 = E = 0
+            if (sd.k == 0 && a.raw_fallback) {  // empty: the header alone is shorter
+                write_raw_header(st, sd, a.chunk_elems);
+                a.stream_bytes[seg] = kHeaderBytes;
+            } else if (sd.k == 0) {  // empty: chunk table entry 0 = E = 0
                 *reinterpret_cast<uint32_t*>(st + kHeaderBytes) = 0;
                 *reinterpret_cast<uint64_t*>(st + 24) = 0;
                 *reinterpret_cast<uint64_t*>(st + 32) = sd.esc_off;

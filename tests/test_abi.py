@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 25
     assert sorted(binding.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -49,6 +49,10 @@ def test_plan_argument_errors_need_no_gpu(lib):
     assert lib.zc_plan_create(0, sizes, 0, ctypes.byref(h)) == binding.ZC_ERR_INVALID_ARG
     big = (ctypes.c_uint64 * 1)(1 << 32)
     assert lib.zc_plan_create(1, big, 0, ctypes.byref(h)) == binding.ZC_ERR_UNSUPPORTED
+    # plan flags: only the raw fallback is defined
+    assert lib.zc_plan_create_ex(2, sizes, 0, 0x2, ctypes.byref(h)) == binding.ZC_ERR_INVALID_ARG
+    assert lib.zc_plan_create_ex(2, sizes, 1000, 0x1, ctypes.byref(h)) == binding.ZC_ERR_UNSUPPORTED
+    assert lib.zc_plan_flags(None) == 0
     assert lib.zc_compress(None, None, None, 0, None, None, 0, None) == binding.ZC_ERR_INVALID_ARG
     assert lib.zc_decompress(None, None, 0, None, None, 0, None) == binding.ZC_ERR_INVALID_ARG
 
