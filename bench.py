@@ -150,6 +150,26 @@ def other_configs(args, stream):
     return res
 
 
+def raw_fallback(zc, N, chunk, args, stream, flush, res):
+    """Raw fallback (a plan flag): a tensor of zeros, which every window
+    escapes, is stored as its header plus its words; the speculative coding
+    pass still runs before the window kernel picks raw."""
+    log("raw fallback")
+    zplan = zc.Plan([N], chunk, raw_fallback=True)
+    zx = zplan.empty_input().zero_()
+    zout, zsz, zws, zy = zplan.empty_output(), zplan.empty_sizes(), zplan.empty_workspace(), zplan.empty_input()
+    zcomp = lambda: zplan.compress(zx, zout, zsz, zws)
+    zdec = lambda: zplan.decompress(zout, zy, zws)
+    zcomp(); zdec(); torch.cuda.synchronize()
+    assert zplan.read_status(zws) == 0 and torch.equal(zy[:N], zx[:N])
+    assert int(zsz.cpu()[0]) == 64 + 2 * N
+    res["raw_fallback"] = {
+        "input": f"{N:,} zeros, plan with the raw fallback",
+        "stream_bytes": 64 + 2 * N,
+        "compress_ms": round(float(np.median(timed(zcomp, args.steps, args.warmup, stream, flush))) * 1e3, 4),
+        "decompress_ms": round(float(np.median(timed(zdec, args.steps, args.warmup, stream, flush))) * 1e3, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +177,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reduce", action="store_true")
+    ap.add_argument("--no-raw", action="store_true", help="skip the raw-fallback measurement")
     ap.add_argument("--all-configs", action="store_true",
                     help="also time compress / decompress of the Llama3-8B MLP matrices "
                          "(3 segments) and the 256-expert MoE batch (extra keys)")
@@ -313,6 +334,9 @@ def main():
         res["copy_128MiB_ms"] = round(tcp * 1e3, 4)
         res["copy_GBps"] = round(2 * src.numel() * 2 / tcp / 1e9, 1)  # read + write
         del src, dst
+
+    if not args.no_raw:
+        raw_fallback(zc, N, chunk, args, stream, flush, res)
 
     if not args.no_reduce:
         log("decompress-reduce workload")

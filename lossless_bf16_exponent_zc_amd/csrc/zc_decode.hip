@@ -292,6 +292,12 @@ __device__ __forceinline__ uint32_t decode_group_all(const DecodeArgs& a, const 
     const uint8_t* st = stream_of(0, cap);
     GroupData cur;
     fetch<!REDUCE>(st, cap, sd, a.chunk_elems, g, lane, cur);
+    if (!REDUCE && cur.bad == kRawStream) {  // uniform: a raw stream, its words as they are
+        u32x4 o[4];
+        raw_words<TAIL>(st, sd.n, g, lane, o);
+        store_values<TAIL>(a.out + sd.in_off, sd.n, g, lane, o);
+        return 0;
+    }
     for (uint32_t s = 0; s < a.nstreams; ++s) {
         // escape bytes of this stream, then the next stream's loads
         uint32_t first = 0;
@@ -304,34 +310,14 @@ __device__ __forceinline__ uint32_t decode_group_all(const DecodeArgs& a, const 
             fetch<!REDUCE>(nst, ncap, sd, a.chunk_elems, g, lane, nxt);
         }
 
-        // the group's values: summed in shard order, or stored
-        auto take = [&](const u32x4 (&o)[4]) {
-            if (REDUCE) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-#pragma unroll
-                    for (int mm = 0; mm < 4; ++mm) {
-                        const float lo = __uint_as_float(o[k][mm] << 16);
-                        const float hi = __uint_as_float(o[k][mm] & 0xFFFF0000u);
-                        float& a0 = acc[REDUCE ? 8 * k + 2 * mm : 0];
-                        float& a1 = acc[REDUCE ? 8 * k + 2 * mm + 1 : 0];
-                        a0 = s == 0 ? lo : a0 + lo;
-                        a1 = s == 0 ? hi : a1 + hi;
-                    }
-            } else {
-                store_values<TAIL>(a.out + sd.in_off, sd.n, g, lane, o);
-            }
-        };
-        // (the sum takes both kinds of stream at one join; the plain decoder
-        // stores on each path, which keeps it within its registers)
+        // (raw shards of the sum join the decoded ones before the adds)
         uint32_t bad = cur.bad;
         u32x4 o[4];
         bool have = false;
-        if (bad == kRawStream) {  // uniform: a raw stream
+        if (REDUCE && bad == kRawStream) {  // uniform
             bad = 0;
             raw_words<TAIL>(st, sd.n, g, lane, o);
-            if (REDUCE) have = true;
-            else take(o);
+            have = true;
         } else if (!bad) {
             if (TAIL) {
                 const uint32_t V = valid_bits(lane, valid);
@@ -348,10 +334,22 @@ __device__ __forceinline__ uint32_t decode_group_all(const DecodeArgs& a, const 
             if (!bad) {
                 rebuild(cur, M, first + incl - cnt, escb, row, o);
                 if (REDUCE) have = true;
-                else take(o);
+                else store_values<TAIL>(a.out + sd.in_off, sd.n, g, lane, o);
             }
         }
-        if (REDUCE && have) take(o);
+        if (REDUCE && have) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    const float lo = __uint_as_float(o[k][mm] << 16);
+                    const float hi = __uint_as_float(o[k][mm] & 0xFFFF0000u);
+                    float& a0 = acc[REDUCE ? 8 * k + 2 * mm : 0];
+                    float& a1 = acc[REDUCE ? 8 * k + 2 * mm + 1 : 0];
+                    a0 = s == 0 ? lo : a0 + lo;
+                    a1 = s == 0 ? hi : a1 + hi;
+                }
+        }
         bad_all |= bad;
         if (REDUCE && s + 1 < a.nstreams) {
             cur = nxt;

@@ -69,8 +69,9 @@ template __global__ void zc_encode<true>(EncodeArgs);
 template __global__ void zc_encode<false>(EncodeArgs);
 
 // Values [v0, min(n, v0 + C)) of a segment into its raw stream (after the
-// 64-byte header), 16-byte words, four in flight per thread.
-__device__ __forceinline__ void copy_raw_chunk(const uint16_t* __restrict__ in, uint8_t* st, uint64_t n,
+// 64-byte header), 16-byte words, four in flight per thread.  Not inlined:
+// its registers stay out of the placement path's allocation.
+__device__ __noinline__ void copy_raw_chunk(const uint16_t* __restrict__ in, uint8_t* st, uint64_t n,
                                                uint64_t v0, uint32_t C) {
     const uint32_t m = (uint32_t)min((uint64_t)C, n - v0), words = m / 8u;
     const u32x4* src = reinterpret_cast<const u32x4*>(in + v0);
@@ -138,7 +139,6 @@ __device__ __forceinline__ void place_chunk(const PlaceArgs& a, uint32_t ci) {
         const uint32_t c = lane < ng ? c_raw : 0u;
         const uint32_t incl = wave_inclusive_scan(c);
         if (lane < ng) {
-            if (!raw) reinterpret_cast<uint16_t*>(st + sd.gtab_off)[gc0 + lane] = (uint16_t)(incl - c);
             s_gb[lane] = incl - c;
             s_gn[lane] = min(c, kGroup);
         }
@@ -164,6 +164,7 @@ __device__ __forceinline__ void place_chunk(const PlaceArgs& a, uint32_t ci) {
         lds_barrier();  // s_* are rewritten by the next chunk
         return;
     }
+    if (wave == 0 && lane < ng) reinterpret_cast<uint16_t*>(st + sd.gtab_off)[gc0 + lane] = (uint16_t)s_gb[lane];
     const uint32_t pre = s_prefix, t = s_t;
     if (pre == 0xFFFFFFFFu) {
         lds_barrier();  // s_* are rewritten by the next chunk
