@@ -104,7 +104,8 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return ZC_ERR_HIP;
     WindowArgs wa{ea, p->d_witems, ws_ptr<SegStat>(p, d_ws, p->ws.stats), d_stream_bytes,
                   p->chunk, p->chunk / p->block, (p->flags & ZC_PLAN_RAW_FALLBACK) ? 1u : 0u};
-    hipLaunchKernelGGL(zc_window, dim3((uint32_t)p->witems.size()), dim3(256), 0, stream, wa);
+    if (ea.single) hipLaunchKernelGGL(zc_window<true>, dim3((uint32_t)p->witems.size()), dim3(256), 0, stream, wa);
+    else hipLaunchKernelGGL(zc_window<false>, dim3((uint32_t)p->witems.size()), dim3(256), 0, stream, wa);
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return ZC_ERR_HIP;
     // after the window kernel: codes and sm bytes (coded again there when
     // the prediction failed), header, chunk table and sizes are final
@@ -344,7 +345,8 @@ zc_status zc_decompress(const zc_plan* p, const void* d_in, uint64_t in_capacity
     a.ngroups = ngroups(p);
     a.out = static_cast<uint16_t*>(d_out);
     a.status = ws_ptr<uint32_t>(p, d_ws, p->ws.status);
-    hipLaunchKernelGGL(zc_decode, dim3(group_grid(p)), dim3(256), 0, stream, a);
+    if (a.single) hipLaunchKernelGGL(zc_decode<true>, dim3(group_grid(p)), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(zc_decode<false>, dim3(group_grid(p)), dim3(256), 0, stream, a);
     return launch_status();
 }
 

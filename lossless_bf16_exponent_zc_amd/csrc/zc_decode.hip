@@ -33,37 +33,46 @@ __device__ __forceinline__ T ld(const uint8_t* p) {
     return *reinterpret_cast<const T*>(p);
 }
 
-// A raw stream's header (flags 1): L 0, E 0, total 64 + 2N, offsets 0.
-__device__ __forceinline__ uint32_t check_raw_header(const uint8_t* st, uint64_t cap, const SegDesc& sd,
-                                                     uint32_t C, uint32_t w1) {
-    uint32_t bad = 0;
-    if (ld<uint32_t>(st) != kMagic || (w1 & 0xFFFFu) != kVersion) bad |= kBadMagic;
-    if (((w1 >> 16) & 0xFFu) != 0) bad |= kBadWindow;
-    if (ld<uint64_t>(st + 8) != sd.n || ld<uint32_t>(st + 16) != C || ld<uint32_t>(st + 20) != sd.k ||
-        (ld<uint64_t>(st + 40) | ld<uint64_t>(st + 48) | ld<uint64_t>(st + 56)) != 0)
-        bad |= kBadShape;
-    const uint64_t total = kHeaderBytes + 2ull * sd.n;
-    if (ld<uint64_t>(st + 24) != 0 || ld<uint64_t>(st + 32) != total || total > cap) bad |= kBadSize;
-    return bad ? bad : kRawStream;
+// The 64-byte header, read as one block (one scalar load: every field
+// arrives in one round trip) and checked with bitwise ORs, so no check waits
+// for another.
+struct HeaderWords {
+    uint32_t w[16];
+};
+
+__device__ __forceinline__ uint64_t hword64(const HeaderWords& h, int i) {
+    return (uint64_t)h.w[i] | ((uint64_t)h.w[i + 1] << 32);
 }
 
-// 0 for a valid coded header, kRawStream for a valid raw one, else the
-// rejection bits.
+// 0 for a valid coded header, kRawStream for a valid raw one (flags 1: L 0,
+// E 0, total 64 + 2N, offsets 0), else the rejection bits.
+// E and L receive the header's escape count and window (when cap holds it).
 __device__ __forceinline__ uint32_t check_header(const uint8_t* st, uint64_t cap, const SegDesc& sd,
-                                                 uint32_t C) {
+                                                 uint32_t C, uint64_t& E, uint32_t& L) {
+    E = 0;
+    L = 0;
     if (cap < kHeaderBytes) return kBadSize;
+    const HeaderWords h = *reinterpret_cast<const HeaderWords*>(st);
+    const uint32_t w1 = h.w[1], flags = w1 >> 24;
+    L = (w1 >> 16) & 0xFFu;
+    E = hword64(h, 6);
+    const uint64_t N = hword64(h, 2), total = hword64(h, 8);
+    const uint64_t o40 = hword64(h, 10), o48 = hword64(h, 12), o56 = hword64(h, 14);
+    const bool id_ok = (h.w[0] == kMagic) & ((w1 & 0xFFFFu) == kVersion);
+    const bool dims_ok = (N == sd.n) & (h.w[4] == C) & (h.w[5] == sd.k);
     uint32_t bad = 0;
-    const uint32_t w1 = ld<uint32_t>(st + 4);
-    if ((w1 >> 24) == kFlagRaw) return check_raw_header(st, cap, sd, C, w1);
-    const uint32_t L = (w1 >> 16) & 0xFFu;
-    if (ld<uint32_t>(st) != kMagic || (w1 & 0xFFFFu) != kVersion || (w1 >> 24) != 0) bad |= kBadMagic;
-    if (L < 1 || L > 248) bad |= kBadWindow;
-    if (ld<uint64_t>(st + 8) != sd.n || ld<uint32_t>(st + 16) != C || ld<uint32_t>(st + 20) != sd.k ||
-        ld<uint64_t>(st + 40) != sd.code_off || ld<uint64_t>(st + 48) != sd.sm_off ||
-        ld<uint64_t>(st + 56) != sd.esc_off)
-        bad |= kBadShape;
-    const uint64_t E = ld<uint64_t>(st + 24), total = ld<uint64_t>(st + 32);
-    if (E > sd.n || total != sd.esc_off + E || total > cap) bad |= kBadSize;
+    if (flags == kFlagRaw) {
+        const uint64_t raw_total = kHeaderBytes + 2ull * sd.n;
+        bad |= id_ok ? 0u : kBadMagic;
+        bad |= L != 0 ? kBadWindow : 0u;
+        bad |= (dims_ok & ((o40 | o48 | o56) == 0)) ? 0u : kBadShape;
+        bad |= ((E == 0) & (total == raw_total) & (raw_total <= cap)) ? 0u : kBadSize;
+        return bad ? bad : kRawStream;
+    }
+    bad |= (id_ok & (flags == 0)) ? 0u : kBadMagic;
+    bad |= ((L >= 1) & (L <= 248)) ? 0u : kBadWindow;
+    bad |= (dims_ok & (o40 == sd.code_off) & (o48 == sd.sm_off) & (o56 == sd.esc_off)) ? 0u : kBadShape;
+    bad |= ((E <= sd.n) & (total == sd.esc_off + E) & (total <= cap)) ? 0u : kBadSize;
     return bad;
 }
 
@@ -191,10 +200,11 @@ __device__ __forceinline__ void fetch(const uint8_t* st, uint64_t cap, const Seg
 
     // header and table words, loaded with the fixed regions (every offset
     // here lies before esc_off, inside the buffer when fixed_ok), checked after
-    const uint32_t gpc = C / kGroup, k = g / gpc;
+    // C is a power of two >= 2048: chunk k = g >> (log2 C - 11)
+    const uint32_t gpc = C / kGroup, k = g >> (__builtin_ctz(C) - 11);
     const uint32_t* table = reinterpret_cast<const uint32_t*>(st + kHeaderBytes);
     const uint16_t* gtab = reinterpret_cast<const uint16_t*>(st + sd.gtab_off);
-    const bool last_in_chunk = (g + 1) % gpc == 0 || g + 1 == sd.g;
+    const bool last_in_chunk = ((g + 1) & (gpc - 1)) == 0 || g + 1 == sd.g;
     uint32_t t0 = 0, t1 = 0, rel = 0, rel1 = 0;
     if (EARLY && fixed_ok) {
         t0 = table[k];
@@ -202,7 +212,9 @@ __device__ __forceinline__ void fetch(const uint8_t* st, uint64_t cap, const Seg
         rel = gtab[g];
         rel1 = gtab[last_in_chunk ? g : g + 1];
     }
-    d.bad = check_header(st, cap, sd, C);
+    uint64_t E;
+    uint32_t L;
+    d.bad = check_header(st, cap, sd, C, E, L);
     d.L = d.t0 = d.rel = d.span = 0;
     if (!d.bad) {
         if (!EARLY) {
@@ -211,13 +223,12 @@ __device__ __forceinline__ void fetch(const uint8_t* st, uint64_t cap, const Seg
             rel = gtab[g];
             rel1 = gtab[last_in_chunk ? g : g + 1];
         }
-        const uint64_t E = ld<uint64_t>(st + 24);
-        d.L = st[6];
+        d.L = L;
         d.t0 = t0;
         d.rel = rel;
         const uint32_t next = last_in_chunk ? t1 - t0 : rel1;
         if (t0 > t1 || t1 > E || (k == 0 && t0 != 0) || (k + 1 == sd.k && t1 != E) ||
-            (g % gpc == 0 && rel != 0))
+            ((g & (gpc - 1)) == 0 && rel != 0))
             d.bad |= kBadTable;
         else if (rel > next || next > t1 - t0)
             d.bad |= kBadCount;
@@ -371,7 +382,7 @@ __device__ __forceinline__ uint32_t decode_group_all(const DecodeArgs& a, const 
     return bad_all;
 }
 
-template <bool REDUCE>
+template <bool REDUCE, bool SINGLE>
 __device__ __forceinline__ void decode_kernel(const DecodeArgs& a) {
     __shared__ u32x4 s_row[4][64][2];   // per wave and lane: 32 exponent bytes
     __shared__ uint32_t s_esc[4][520];  // the group's escape bytes per wave (whole dwords)
@@ -381,9 +392,10 @@ __device__ __forceinline__ void decode_kernel(const DecodeArgs& a) {
     if (gg >= a.ngroups) return;
     // (the fused reduce takes the descriptor from memory: the argument copy
     // costs it registers it does not have)
-    const bool single = !REDUCE && a.single;
-    const ItemDesc gd = single ? ItemDesc{0u, gg} : a.groups[gg];
-    const SegDesc sd = single ? a.seg0 : a.segs[gd.seg];
+    // (a compile-time choice: selecting between the argument copy and the
+    // table at run time would read the descriptor through vector loads)
+    const ItemDesc gd = SINGLE ? ItemDesc{0u, gg} : a.groups[gg];
+    const SegDesc sd = SINGLE ? a.seg0 : a.segs[gd.seg];
     const uint32_t g = gd.local;
     const uint32_t bad = (uint64_t)kGroup * (g + 1) > sd.n
                              ? decode_group_all<REDUCE, true>(a, sd, g, lane, s_esc[wave], s_row[wave][lane])
@@ -485,9 +497,8 @@ __global__ __launch_bounds__(512) void zc_decode_reduce_wide(DecodeArgs a) {
     __shared__ u32x4 s_area[8][258];  // per wave: rows (2048 B) + escapes (2080 B); then values
     __shared__ uint32_t s_bad[8];
     const uint32_t gg = blockIdx.x;
-    const ItemDesc gd = a.single ? ItemDesc{0u, gg} : a.groups[gg];
-    const SegDesc sd = a.single ? a.seg0 : a.segs[gd.seg];
-    const uint32_t g = gd.local;
+    const SegDesc& sd = a.seg0;  // a reduce plan has one segment
+    const uint32_t g = gg;
     if ((uint64_t)kGroup * (g + 1) > sd.n)
         reduce_group_wide<true>(a, sd, g, gg, s_area, s_bad);
     else
@@ -495,14 +506,18 @@ __global__ __launch_bounds__(512) void zc_decode_reduce_wide(DecodeArgs a) {
 }
 
 // Eight waves per SIMD for the plain decoder (it fits in 64 VGPRs).
+template <bool SINGLE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void zc_decode(DecodeArgs a) {
-    decode_kernel<false>(a);
+    decode_kernel<false, SINGLE>(a);
 }
+
+template __global__ void zc_decode<true>(DecodeArgs);
+template __global__ void zc_decode<false>(DecodeArgs);
 
 // Four waves per SIMD for the fused reduce (32 accumulators per lane).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void zc_decode_reduce(
     DecodeArgs a) {
-    decode_kernel<true>(a);
+    decode_kernel<true, false>(a);
 }
 
 }  // namespace zc

@@ -60,11 +60,13 @@ struct DecodeArgs {
     SegDesc seg0;
 };
 
+template <bool SINGLE>
 __global__ void zc_window(WindowArgs a);
 template <bool MOMENTS>
 __global__ void zc_encode(EncodeArgs a);
 template <int GPW>
 __global__ void zc_place_escapes(PlaceArgs a);
+template <bool SINGLE>
 __global__ void zc_decode(DecodeArgs a);
 __global__ void zc_decode_reduce(DecodeArgs a);
 __global__ void zc_decode_reduce_wide(DecodeArgs a);

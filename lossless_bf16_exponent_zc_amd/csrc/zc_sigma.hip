@@ -170,12 +170,16 @@ __device__ __forceinline__ void place_offsets(const WindowArgs& a, const SegDesc
 // codes are final and workgroup 0 writes the chunk table and sizes.  If not,
 // the segment's workgroups code its items again (workgroup r takes items
 // r, r + wr, ...), and the last of them to finish writes the tables.
+template <bool SINGLE>
 __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
     __shared__ MomentScratch s_mom;
     __shared__ uint32_t s_L, s_last;
-    const ItemDesc wi = a.enc.single ? ItemDesc{0u, blockIdx.x} : a.items[blockIdx.x];
+    // (SINGLE, one segment: the descriptor from the arguments; a choice made
+    // at run time would read it through vector loads before anything else)
+    const ItemDesc wi = SINGLE ? ItemDesc{0u, blockIdx.x} : a.items[blockIdx.x];
     const uint32_t seg = wi.seg, r = wi.local;
-    const SegDesc sd = a.enc.single ? a.enc.seg0 : a.enc.segs[seg];
+    const SegDesc sd_mem = SINGLE ? SegDesc{} : a.enc.segs[seg];  // read before any store
+    const SegDesc& sd = SINGLE ? a.enc.seg0 : sd_mem;
     uint8_t* st = a.enc.out + sd.out_off;
     const uint32_t forced = a.enc.forced_L;
     // one round of loads: the moments' first round, and in workgroup 0 the
@@ -255,5 +259,8 @@ __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
         place_offsets(a, sd, seg, st, c2);
     }
 }
+
+template __global__ void zc_window<true>(WindowArgs);
+template __global__ void zc_window<false>(WindowArgs);
 
 }  // namespace zc
