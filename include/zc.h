@@ -191,9 +191,9 @@ zc_status zc_compress_timed(const zc_plan *plan, const void *d_in, void *d_out,
 /*
  * Decode every segment's stream (at d_in + zc_plan_stream_offset(s); the
  * buffer holds in_capacity readable bytes) into d_out (BF16, laid out as
- * d_in of zc_compress).  Streams are validated on the device; a rejected
- * chunk writes no output and is reported by zc_read_status.  Reads never
- * leave [d_in, d_in + in_capacity).
+ * d_in of zc_compress).  Streams are validated on the device; a group of
+ * 2048 values whose checks fail writes no output and is reported by
+ * zc_read_status.  Reads never leave [d_in, d_in + in_capacity).
  */
 zc_status zc_decompress(const zc_plan *plan, const void *d_in,
                         uint64_t in_capacity, void *d_out, void *d_ws,
@@ -205,7 +205,8 @@ zc_status zc_decompress(const zc_plan *plan, const void *d_in,
  * stream of N values with stream_capacity readable bytes.  Writes
  * d_out[i] = bf16_rne(((x0[i] + x1[i]) + x2[i]) + ...) with the sum in fp32
  * in the given stream order; any NaN sum gives 0x7FC0.  A rejected stream
- * makes the affected chunks write no output (see zc_read_status).
+ * makes the affected 2048-value groups write no output (see
+ * zc_read_status).
  */
 zc_status zc_decompress_reduce(const zc_plan *plan, const void *const *d_streams,
                                uint32_t nstreams, uint64_t stream_capacity,
