@@ -436,16 +436,18 @@ __device__ __forceinline__ uint32_t decode_one(const uint8_t* st, uint64_t cap, 
     return bad;
 }
 
-// Output word i (values 512 (i / 64) + 8 (i % 64) .. + 7 of group g).
+// Output half-word i (values 512 (i / 128) + 8 ((i / 2) % 64) + 4 (i % 2)
+// .. + 3 of group g: the half of area word i / 2).
 template <bool TAIL>
-__device__ __forceinline__ void store_word(uint16_t* __restrict__ out, uint64_t n, uint64_t g,
-                                           uint32_t i, const u32x4 w) {
-    const uint64_t b = (uint64_t)kGroup * g + 512u * (i >> 6) + 8u * (i & 63u);
-    if (!TAIL || b + 8 <= n) {
-        *reinterpret_cast<u32x4*>(out + b) = w;
+__device__ __forceinline__ void store_half_word(uint16_t* __restrict__ out, uint64_t n, uint64_t g,
+                                                uint32_t i, const u32x2 w) {
+    const uint32_t wd = i >> 1;
+    const uint64_t b = (uint64_t)kGroup * g + 512u * (wd >> 6) + 8u * (wd & 63u) + 4u * (i & 1u);
+    if (!TAIL || b + 4 <= n) {
+        *reinterpret_cast<u32x2*>(out + b) = w;
         return;
     }
-    for (uint32_t j = 0; j < 8; ++j)
+    for (uint32_t j = 0; j < 4; ++j)
         if (b + j < n) out[b + j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
 }
 
@@ -471,23 +473,25 @@ __device__ __forceinline__ void reduce_group_wide(const DecodeArgs& a, const Seg
     uint32_t bad_all = 0;
     for (uint32_t s = 0; s < S; ++s) bad_all |= s_bad[s];
     if (bad_all == 0) {
-        for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) {
-            float acc[8];
+        // every thread takes 4 values (half an area word), so all S waves
+        // share the sum
+        for (uint32_t i = threadIdx.x; i < 512; i += blockDim.x) {
+            float acc[4];
 #pragma unroll
             for (uint32_t s = 0; s < 8; ++s) {
                 if (s >= S) break;  // uniform
-                const u32x4 v = s_area[s][i];
+                const u32x2 v = reinterpret_cast<const u32x2*>(s_area[s])[i];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
+                for (int m = 0; m < 2; ++m) {
                     const float lo = __uint_as_float(v[m] << 16), hi = __uint_as_float(v[m] & 0xFFFF0000u);
                     acc[2 * m] = s == 0 ? lo : acc[2 * m] + lo;
                     acc[2 * m + 1] = s == 0 ? hi : acc[2 * m + 1] + hi;
                 }
             }
-            u32x4 w;
+            u32x2 w;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) w[m] = to_bf16(acc[2 * m]) | (to_bf16(acc[2 * m + 1]) << 16);
-            store_word<TAIL>(a.out + sd.in_off, sd.n, g, i, w);
+            for (int m = 0; m < 2; ++m) w[m] = to_bf16(acc[2 * m]) | (to_bf16(acc[2 * m + 1]) << 16);
+            store_half_word<TAIL>(a.out + sd.in_off, sd.n, g, i, w);
         }
     }
     if (threadIdx.x == 0) a.status[gg] = bad_all;
