@@ -55,12 +55,11 @@ __device__ __forceinline__ void store_run(uint8_t* dst, const uint32_t* src, uin
 
 template <bool MOMENTS>
 __global__ __launch_bounds__(256) void zc_encode(EncodeArgs a) {
-    const ItemDesc first = a.single ? ItemDesc{0u, 4 * blockIdx.x} : a.pairs[blockIdx.x * 4];
-    const uint32_t L = a.forced_L ? a.forced_L : predicted_L(a.stats[first.seg].L);
-    encode_wg<MOMENTS>(a, blockIdx.x, L);
+    encode_wg<MOMENTS>(a, blockIdx.x, a.forced_L);  // 0: the predicted window
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.zero = 0u;
+    const ItemDesc first = a.single ? ItemDesc{0u, 4 * blockIdx.x} : a.pairs[blockIdx.x * 4];
     if (first.local == 0 && threadIdx.x == 0) {  // the segment's first item
-        a.pred[first.seg] = L;
+        a.pred[first.seg] = a.forced_L ? a.forced_L : predicted_L(a.stats[first.seg].L);
         a.done[first.seg] = 0;
     }
 }

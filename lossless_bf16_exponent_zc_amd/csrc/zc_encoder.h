@@ -183,6 +183,8 @@ __device__ __forceinline__ uint32_t predicted_L(uint32_t raw) {
 // LDS per wave: 4112 bytes, the group's values for the transpose, then a
 // 32-byte exponent row per lane and the packed escapes (every value may
 // escape).  Every thread of the 256-thread workgroup calls this (barriers).
+// L = 0: the predicted window, read once the item's loads are out (the
+// first pass: its waves do not wait for the statistics before loading).
 template <bool MOMENTS>
 __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint32_t L) {
     __shared__ u32x4 s_area[4][257];  // per wave, 4112 bytes
@@ -210,6 +212,7 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
             for (int k = 0; k < 4; ++k) w[q][k] = u32x4{0, 0, 0, 0};
         }
     }
+    if (!L) L = predicted_L(a.stats[first.seg].L);
     // group moments (wave-uniform); groups past the data are -0.0 (identity)
     double m1[2] = {-0.0, -0.0}, m2[2] = {-0.0, -0.0};
     uint32_t mn[2] = {0, 0}, ec[2] = {0, 0};       // values, escapes
