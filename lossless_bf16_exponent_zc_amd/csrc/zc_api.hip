@@ -7,8 +7,11 @@
 //                      as the prediction (or the caller's fixed window)
 //   zc_window          per segment: variance -> window, statistics, header
 //                      fields known before encoding; where the prediction
-//                      failed, the segment's codes again; chunk table, sizes
-//   zc_place_escapes   group table, escapes to their place
+//                      failed, the segment's codes again; chunk table, sizes;
+//                      with the raw fallback, the raw header where coding
+//                      would not shrink the segment
+//   zc_place_escapes   group table, escapes to their place (a raw segment:
+//                      its values after the header)
 // Decompress: zc_decode.  Decompress-reduce: zc_decode_reduce_wide (one wave
 // per shard, up to 8 shards), else zc_decode_reduce (shards in turn).
 // Every call enqueues on the caller's stream and returns; nothing here reads
