@@ -15,6 +15,8 @@ with the shapes of the evaluated collectives:
                    Zipf(1.2) token counts summing to 65,536 tokens, hidden
                    7168, N(0, 1) times a per-token LogNormal(0, 0.5) scale
 * ``shards``    -- 8 reduce-scatter shards of 33,554,432 values ~ N(0, 1e-3^2)
+* ``gaussian_device`` -- N(0, scale^2) of any size drawn on the GPU (for the
+                   largest segment a plan accepts, 2^32 - 1 values)
 
 Every draw uses ``torch.Generator(device="cpu")`` with a fixed seed, in fp32,
 in the order written below, then rounds to BF16 (nearest even).  The result is
@@ -122,3 +124,15 @@ def shards(n: int = 1 << 25, nshards: int = 8) -> list[np.ndarray]:
     """Shard s uses seed s: randn(n) * 1e-3."""
     return [to_bits(torch.randn(n, generator=_gen(s)) * 1e-3)
             for s in range(nshards)]
+
+
+def gaussian_device(n: int, seed: int = 0, scale: float = 1e-3, device: str = "cuda"):
+    """randn(n) * scale drawn with torch's generator on `device` (seeded),
+    rounded to BF16 there; returns the bits as a device int16 tensor."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    z = torch.randn(n, generator=g, device=device)
+    z.mul_(scale)
+    bits = z.to(torch.bfloat16).view(torch.int16)
+    del z
+    return bits
