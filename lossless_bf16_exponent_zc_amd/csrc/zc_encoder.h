@@ -202,16 +202,10 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
                                  : a.pairs[wg * 4 + wave];
     const bool live = it.seg != 0xFFFFFFFFu;
     const uint64_t g0 = 2ull * it.local;
+    // group 0's words; group 1's are loaded once group 0 is coded, so the
+    // two groups' words are never live together
     u32x4 w[2][4];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        if (live && g0 + q < sd.g) {
-            load_group(a.in + sd.in_off, sd.n, g0 + q, lane, w[q]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) w[q][k] = u32x4{0, 0, 0, 0};
-        }
-    }
+    if (live) load_group(a.in + sd.in_off, sd.n, g0, lane, w[0]);
     if (!L) L = predicted_L(a.stats[first.seg].L);
     // group moments (wave-uniform); groups past the data are -0.0 (identity)
     double m1[2] = {-0.0, -0.0}, m2[2] = {-0.0, -0.0};
@@ -261,6 +255,7 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
             exponent_bytes(w[q], Q);
             rowp[0] = u32x4{Q[0], Q[1], Q[2], Q[3]};
             rowp[1] = u32x4{Q[4], Q[5], Q[6], Q[7]};
+            if (q == 0 && g + 1 < sd.g) load_group(a.in + sd.in_off, sd.n, g + 1, lane, w[1]);
             const uint8_t* rb = reinterpret_cast<const uint8_t*>(rowp);
             for (uint32_t m = M, i = 0; m; m &= m - 1, ++i) ew[excl + i] = rb[__builtin_ctz(m)];
             __builtin_amdgcn_wave_barrier();  // the wave's packed bytes are complete
