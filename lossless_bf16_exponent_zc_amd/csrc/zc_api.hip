@@ -348,6 +348,7 @@ zc_status zc_decompress(const zc_plan* p, const void* d_in, uint64_t in_capacity
     a.ngroups = ngroups(p);
     a.out = static_cast<uint16_t*>(d_out);
     a.status = ws_ptr<uint32_t>(p, d_ws, p->ws.status);
+    a.dummy = ws_ptr<uint8_t>(p, d_ws, p->ws.staging);  // 2048 B per group + 16
     if (a.single) hipLaunchKernelGGL(zc_decode<true>, dim3(group_grid(p)), dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(zc_decode<false>, dim3(group_grid(p)), dim3(256), 0, stream, a);
     return launch_status();
@@ -375,6 +376,7 @@ zc_status zc_decompress_reduce(const zc_plan* p, const void* const* d_streams, u
     a.ngroups = ngroups(p);
     a.out = static_cast<uint16_t*>(d_out);
     a.status = ws_ptr<uint32_t>(p, d_ws, p->ws.status);
+    a.dummy = ws_ptr<uint8_t>(p, d_ws, p->ws.staging);  // 2048 B per group + 16
     if (nstreams <= 8)  // one wave per shard, one workgroup per group
         hipLaunchKernelGGL(zc_decode_reduce_wide, dim3(ngroups(p)), dim3(64 * nstreams), 0, stream, a);
     else

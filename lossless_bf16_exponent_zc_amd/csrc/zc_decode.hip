@@ -45,35 +45,41 @@ __device__ __forceinline__ uint64_t hword64(const HeaderWords& h, int i) {
 }
 
 // 0 for a valid coded header, kRawStream for a valid raw one (flags 1: L 0,
-// E 0, total 64 + 2N, offsets 0), else the rejection bits.
-// E and L receive the header's escape count and window (when cap holds it).
-__device__ __forceinline__ uint32_t check_header(const uint8_t* st, uint64_t cap, const SegDesc& sd,
-                                                 uint32_t C, uint64_t& E, uint32_t& L) {
-    E = 0;
-    L = 0;
-    if (cap < kHeaderBytes) return kBadSize;
-    const HeaderWords h = *reinterpret_cast<const HeaderWords*>(st);
+// E 0, total 64 + 2N, offsets 0), else the rejection bits.  h: the header's
+// words, read whether or not the buffer holds them (hdr_ok: it does).
+// E and L receive the header's escape count and window (0 without a header).
+// FLAT: both verdicts without branches, so every header word is needed at
+// once (the fused reduce); otherwise the raw verdict is a branch (fewer
+// registers: the plain decoder runs at 64).
+template <bool FLAT>
+__device__ __forceinline__ uint32_t check_header(const HeaderWords& h, bool hdr_ok, uint64_t cap,
+                                                 const SegDesc& sd, uint32_t C, uint64_t& E,
+                                                 uint32_t& L) {
     const uint32_t w1 = h.w[1], flags = w1 >> 24;
-    L = (w1 >> 16) & 0xFFu;
-    E = hword64(h, 6);
+    L = hdr_ok ? (w1 >> 16) & 0xFFu : 0u;
+    E = hdr_ok ? hword64(h, 6) : 0u;
+    if (!hdr_ok) return kBadSize;
     const uint64_t N = hword64(h, 2), total = hword64(h, 8);
     const uint64_t o40 = hword64(h, 10), o48 = hword64(h, 12), o56 = hword64(h, 14);
     const bool id_ok = (h.w[0] == kMagic) & ((w1 & 0xFFFFu) == kVersion);
     const bool dims_ok = (N == sd.n) & (h.w[4] == C) & (h.w[5] == sd.k);
-    uint32_t bad = 0;
-    if (flags == kFlagRaw) {
-        const uint64_t raw_total = kHeaderBytes + 2ull * sd.n;
-        bad |= id_ok ? 0u : kBadMagic;
+    const uint64_t raw_total = kHeaderBytes + 2ull * sd.n;
+    if (!FLAT && flags == kFlagRaw) {
+        uint32_t bad = id_ok ? 0u : kBadMagic;
         bad |= L != 0 ? kBadWindow : 0u;
         bad |= (dims_ok & ((o40 | o48 | o56) == 0)) ? 0u : kBadShape;
         bad |= ((E == 0) & (total == raw_total) & (raw_total <= cap)) ? 0u : kBadSize;
         return bad ? bad : kRawStream;
     }
-    bad |= (id_ok & (flags == 0)) ? 0u : kBadMagic;
+    uint32_t raw_bad = id_ok ? 0u : kBadMagic;
+    raw_bad |= L != 0 ? kBadWindow : 0u;
+    raw_bad |= (dims_ok & ((o40 | o48 | o56) == 0)) ? 0u : kBadShape;
+    raw_bad |= ((E == 0) & (total == raw_total) & (raw_total <= cap)) ? 0u : kBadSize;
+    uint32_t bad = (id_ok & (flags == 0)) ? 0u : kBadMagic;
     bad |= ((L >= 1) & (L <= 248)) ? 0u : kBadWindow;
     bad |= (dims_ok & (o40 == sd.code_off) & (o48 == sd.sm_off) & (o56 == sd.esc_off)) ? 0u : kBadShape;
     bad |= ((E <= sd.n) & (total == sd.esc_off + E) & (total <= cap)) ? 0u : kBadSize;
-    return bad;
+    return flags == kFlagRaw ? (raw_bad ? raw_bad : kRawStream) : bad;
 }
 
 // Nibble words of tile k: nibble n of Z[k] = code of the value at plane bit
@@ -182,42 +188,60 @@ struct GroupData {
     uint32_t bad, L, t0, rel, span;
 };
 
-// Issue the loads of group g of stream st (cap readable bytes).  Plane words
-// and sm bytes are only read when the buffer holds the fixed regions.  EARLY:
-// the table words go out with them (one round of loads fewer; the fused
-// reduce, which holds a second stream's loads meanwhile, reads them after the
-// header check instead, to stay within its registers).
-template <bool EARLY>
+// Issue the loads of group g of stream st (cap readable bytes): the header
+// and (EARLY) the table words first, then the plane words and sm bytes, all
+// in one round with no branch between them, so the checks wait only for
+// the header and tables.  Every load is unconditional: where the buffer
+// does not hold a region, the load reads `dummy` (at least 2048 readable
+// bytes) instead and the value is never used (a buffer without its fixed
+// regions fails the size check; a raw stream reads its words elsewhere).
+// EARLY = false (the reduce that walks the shards in turn, which holds a
+// second stream's loads meanwhile): the table words are read after the
+// header check, to stay within its registers.
+template <bool EARLY, bool FLAT>
 __device__ __forceinline__ void fetch(const uint8_t* st, uint64_t cap, const SegDesc& sd,
-                                      uint32_t C, uint32_t g, uint32_t lane, GroupData& d) {
-    const bool fixed_ok = cap >= sd.esc_off;
-    const uint8_t* cw = st + sd.code_off + 768ull * g + 4u * lane;
-    const uint8_t* sw = st + sd.sm_off + 2048ull * g + 8u * lane;
-#pragma unroll
-    for (int b = 0; b < 3; ++b) d.P[b] = fixed_ok ? ld<uint32_t>(cw + 256 * b) : 0u;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) d.sm[k] = fixed_ok ? ld<u32x2>(sw + 512 * k) : u32x2{0, 0};
-
-    // header and table words, loaded with the fixed regions (every offset
-    // here lies before esc_off, inside the buffer when fixed_ok), checked after
+                                      uint32_t C, uint32_t g, uint32_t lane, const uint8_t* dummy,
+                                      GroupData& d) {
+    const bool hdr_ok = cap >= kHeaderBytes;
+    const bool fixed_ok = cap >= sd.esc_off;  // (implies hdr_ok)
+    const HeaderWords h = *reinterpret_cast<const HeaderWords*>(hdr_ok ? st : dummy);
     // C is a power of two >= 2048: chunk k = g >> (log2 C - 11)
     const uint32_t gpc = C / kGroup, k = g >> (__builtin_ctz(C) - 11);
-    const uint32_t* table = reinterpret_cast<const uint32_t*>(st + kHeaderBytes);
-    const uint16_t* gtab = reinterpret_cast<const uint16_t*>(st + sd.gtab_off);
     const bool last_in_chunk = ((g + 1) & (gpc - 1)) == 0 || g + 1 == sd.g;
+    const uint8_t* fb = fixed_ok ? st : dummy;  // the fixed regions, or the stand-in
     uint32_t t0 = 0, t1 = 0, rel = 0, rel1 = 0;
-    if (EARLY && fixed_ok) {
-        t0 = table[k];
-        t1 = table[k + 1];
-        rel = gtab[g];
-        rel1 = gtab[last_in_chunk ? g : g + 1];
+    if (EARLY) {
+        // table entries k, k + 1, and group-table entries g, g + 1 from the
+        // two aligned dwords that hold them (gtab_off is a multiple of 4), so
+        // that all of it can come in scalar loads; everything read here lies
+        // before esc_off (past the last entry: padding or the code region)
+        const uint32_t* tw = reinterpret_cast<const uint32_t*>(fb + (fixed_ok ? kHeaderBytes + 4ull * k : 0));
+        const uint32_t* gw = reinterpret_cast<const uint32_t*>(fb + (fixed_ok ? (sd.gtab_off + 2ull * g) & ~3ull : 0));
+        t0 = tw[0];
+        t1 = tw[1];
+        const uint64_t gq = (uint64_t)gw[0] | ((uint64_t)gw[1] << 32);
+        const uint32_t sh = fixed_ok ? 16u * (g & 1u) : 0u;
+        rel = (uint32_t)(gq >> sh) & 0xFFFFu;
+        rel1 = last_in_chunk ? rel : (uint32_t)(gq >> (sh + 16)) & 0xFFFFu;
     }
+    __builtin_amdgcn_sched_barrier(0);  // the data words' loads after the header's and tables'
+    const uint8_t* cw = fb + (fixed_ok ? sd.code_off + 768ull * g : 0) + 4u * lane;
+    const uint8_t* sw = fb + (fixed_ok ? sd.sm_off + 2048ull * g : 0) + 8u * lane;
+#pragma unroll
+    for (int b = 0; b < 3; ++b) d.P[b] = ld<uint32_t>(cw + 256 * b);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d.sm[q] = ld<u32x2>(sw + 512 * q);
+
     uint64_t E;
     uint32_t L;
-    d.bad = check_header(st, cap, sd, C, E, L);
-    d.L = d.t0 = d.rel = d.span = 0;
-    if (!d.bad) {
+    uint32_t bad = check_header<FLAT>(h, hdr_ok, cap, sd, C, E, L);
+    if (!FLAT) {  // the checks below only for a valid header (a branch)
+        d.bad = bad;
+        d.L = d.t0 = d.rel = d.span = 0;
+        if (bad) return;
         if (!EARLY) {
+            const uint32_t* table = reinterpret_cast<const uint32_t*>(st + kHeaderBytes);
+            const uint16_t* gtab = reinterpret_cast<const uint16_t*>(st + sd.gtab_off);
             t0 = table[k];
             t1 = table[k + 1];
             rel = gtab[g];
@@ -234,7 +258,29 @@ __device__ __forceinline__ void fetch(const uint8_t* st, uint64_t cap, const Seg
             d.bad |= kBadCount;
         else
             d.span = next - rel;
+        return;
     }
+    if (!EARLY && !bad) {
+        const uint32_t* table = reinterpret_cast<const uint32_t*>(st + kHeaderBytes);
+        const uint16_t* gtab = reinterpret_cast<const uint16_t*>(st + sd.gtab_off);
+        t0 = table[k];
+        t1 = table[k + 1];
+        rel = gtab[g];
+        rel1 = gtab[last_in_chunk ? g : g + 1];
+    }
+    // table and count checks, computed whatever the header said (no branch:
+    // the table loads stay with the others), applied to a valid header only
+    const uint32_t next = last_in_chunk ? t1 - t0 : rel1;
+    const bool tbad = (t0 > t1) | (t1 > E) | ((k == 0) & (t0 != 0)) | ((k + 1 == sd.k) & (t1 != E)) |
+                      (((g & (gpc - 1)) == 0) & (rel != 0));
+    const bool cbad = (rel > next) | (next > t1 - t0);
+    if (!bad) bad = tbad ? kBadTable : (cbad ? kBadCount : 0u);
+    d.bad = bad;
+    const bool use = bad == 0;
+    d.L = use ? L : 0u;
+    d.t0 = use ? t0 : 0u;
+    d.rel = use ? rel : 0u;
+    d.span = use ? next - rel : 0u;
 }
 
 // Copy the group's `span` escape bytes (starting at stream byte `at`) into
@@ -302,7 +348,7 @@ __device__ __forceinline__ uint32_t decode_group_all(const DecodeArgs& a, const 
     uint64_t cap;
     const uint8_t* st = stream_of(0, cap);
     GroupData cur;
-    fetch<!REDUCE>(st, cap, sd, a.chunk_elems, g, lane, cur);
+    fetch<!REDUCE, false>(st, cap, sd, a.chunk_elems, g, lane, a.dummy, cur);
     if (!REDUCE && cur.bad == kRawStream) {  // uniform: a raw stream, its words as they are
         u32x4 o[4];
         raw_words<TAIL>(st, sd.n, g, lane, o);
@@ -318,7 +364,7 @@ __device__ __forceinline__ uint32_t decode_group_all(const DecodeArgs& a, const 
         const uint8_t* nst = nullptr;
         if (REDUCE && s + 1 < a.nstreams) {
             nst = stream_of(s + 1, ncap);
-            fetch<!REDUCE>(nst, ncap, sd, a.chunk_elems, g, lane, nxt);
+            fetch<!REDUCE, false>(nst, ncap, sd, a.chunk_elems, g, lane, a.dummy, nxt);
         }
 
         // (raw shards of the sum join the decoded ones before the adds)
@@ -407,10 +453,10 @@ __device__ __forceinline__ void decode_kernel(const DecodeArgs& a) {
 // lane's four words: tile k at word 64k + lane), returns the rejection bits.
 template <bool TAIL>
 __device__ __forceinline__ uint32_t decode_one(const uint8_t* st, uint64_t cap, const SegDesc& sd,
-                                               uint32_t C, uint32_t g, uint32_t lane,
+                                               uint32_t C, uint32_t g, uint32_t lane, const uint8_t* dummy,
                                                uint32_t* esc_lds, u32x4* row, u32x4 (&o)[4]) {
     GroupData d;
-    fetch<true>(st, cap, sd, C, g, lane, d);
+    fetch<true, true>(st, cap, sd, C, g, lane, dummy, d);
     if (d.bad == kRawStream) {  // uniform
         raw_words<TAIL>(st, sd.n, g, lane, o);
         return 0;
@@ -462,7 +508,7 @@ __device__ __forceinline__ void reduce_group_wide(const DecodeArgs& a, const Seg
     const uint32_t lane = lane_id(), wave = wave_id(), S = a.nstreams;
     u32x4* area = s_area[wave];
     u32x4 o[4];
-    const uint32_t bad = decode_one<TAIL>(a.in[wave], a.capacity, sd, a.chunk_elems, g, lane,
+    const uint32_t bad = decode_one<TAIL>(a.in[wave], a.capacity, sd, a.chunk_elems, g, lane, a.dummy,
                                           reinterpret_cast<uint32_t*>(area + 128), area + 2 * lane, o);
     if (!bad) {
 #pragma unroll

@@ -56,6 +56,8 @@ struct DecodeArgs {
     uint32_t ngroups;
     uint16_t* out;
     uint32_t* status;                // per group
+    const uint8_t* dummy;            // >= 2048 readable bytes no decoder writes: the loads'
+                                     // stand-in where a buffer lacks a region
     uint32_t single;                 // one segment: seg0 is it, group i is (0, i)
     SegDesc seg0;
 };

@@ -73,13 +73,15 @@ def streams_to_packed(plan: Plan, streams) -> torch.Tensor:
 
 
 def gpu_reduce(streams, n, chunk=65536, capacity=None):
-    """Decode + sum single-segment host streams on the GPU."""
+    """Decode + sum single-segment host streams on the GPU.  capacity: the
+    readable bytes the kernels are told of (default: the longest stream,
+    rounded up to 256); the buffers are allocated rounded up to 256."""
     plan = Plan([n], chunk)
-    cap = capacity or max(len(s) for s in streams)
-    cap = (cap + 255) // 256 * 256
+    cap = capacity if capacity is not None else (max(len(s) for s in streams) + 255) // 256 * 256
+    alloc = (max([cap] + [len(s) for s in streams]) + 255) // 256 * 256
     dev = []
     for b in streams:
-        t = torch.zeros(cap, dtype=torch.uint8, device="cuda")
+        t = torch.zeros(alloc, dtype=torch.uint8, device="cuda")
         t[:len(b)] = torch.from_numpy(np.frombuffer(b, dtype=np.uint8).copy()).cuda()
         dev.append(t)
     ws = plan.empty_workspace()

@@ -181,6 +181,32 @@ def test_rejection_set_matches_oracle():
             assert np.array_equal(dec[0], oracle.decompress(m, N, 2048))
 
 
+def test_reduce_rejection_set_matches_oracle():
+    # the fused reduce checks headers and tables with its own (branch-free)
+    # code: every mutant, as both shards, at its exact length as the capacity
+    N = 3 * 2048 + 100
+    x = W.small(N, seed=7)
+    s = oracle.compress(x, C=2048)
+    for i, m in enumerate(_mutants(s, N)):
+        obits, _ = oracle.decompress_status(m, N, 2048)
+        gbits, got = gpu_reduce([m, m], N, 2048, capacity=len(m))
+        say(f"  reduce mutant {i}: oracle 0x{obits:02x} gpu 0x{gbits:02x}")
+        assert (obits == 0) == (gbits == 0), i
+        if obits == 0:
+            assert np.array_equal(got, oracle.decompress_reduce([m, m], N, 2048))
+    # a valid stream beside each mutant: the sum is rejected exactly when
+    # the mutant is (the capacity is the valid stream's length: mutants
+    # other than the truncation have the same length)
+    for i, m in enumerate(_mutants(s, N)):
+        if len(m) != len(s):
+            continue
+        obits, _ = oracle.decompress_status(m, N, 2048)
+        gbits, got = gpu_reduce([s, m], N, 2048, capacity=len(s))
+        assert (obits == 0) == (gbits == 0), i
+        if obits == 0:
+            assert np.array_equal(got, oracle.decompress_reduce([s, m], N, 2048))
+
+
 def test_timed_compress_same_streams():
     from lossless_bf16_exponent_zc_amd import Plan
     from gpu_util import pack_inputs

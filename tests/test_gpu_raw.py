@@ -153,6 +153,29 @@ def test_raw_header_rejections_match_the_oracle():
             assert gbits == obits, i
 
 
+def test_reduce_raw_header_rejections_match_the_oracle():
+    # the fused reduce's own header check on raw streams: each mutant as both
+    # shards, at its exact length as the capacity
+    N = 3000
+    x = uniform(N, 5)
+    s = oracle.compress(x, C=2048, raw_fallback=True)
+    muts = [s, s[:-1]]
+    for off, xor in [(0, 1), (4, 2), (6, 5), (7, 3), (8, 1), (16, 1), (20, 1), (24, 1), (32, 1),
+                     (40, 1), (48, 16), (56, 1)]:
+        b = bytearray(s)
+        b[off] ^= xor
+        muts.append(bytes(b))
+    for i, m in enumerate(muts):
+        obits, _ = oracle.decompress_status(m, N, 2048)
+        gbits, got = gpu_reduce([m, m], N, 2048, capacity=len(m))
+        say(f"  reduce mutant {i}: oracle 0x{obits:02x} gpu 0x{gbits:02x}")
+        assert (obits == 0) == (gbits == 0), i
+        if obits == 0:
+            assert np.array_equal(got, oracle.decompress_reduce([m, m], N, 2048))
+        elif i > 1 and obits != oracle.FMT_MAGIC:  # one field changed: the same bit
+            assert gbits == obits, i
+
+
 def test_large_raw_tensor():
     # 2^22 zeros plus a ragged tail: the placement kernel's raw copy over 64 chunks
     n = (1 << 22) + 5
