@@ -306,7 +306,15 @@ __device__ __forceinline__ uint32_t fetch_escapes(const uint8_t* st, uint64_t ca
 
 // Rebuild the group's values into o.  The lane's exponent bytes go to its
 // 32-byte LDS row in plane-bit order; each escape overwrites its byte there
-// with the next escape byte (the lane's escapes are contiguous from `first`).
+// with the next escape byte (the lane's escapes are contiguous from `first`
+// in `esc`, a 4-byte aligned LDS area with at least 20 readable bytes past
+// the group's last escape).  REG, for a group with more than two escapes
+// per lane on average: the first 16 escape bytes come from five dwords read
+// at once and funnel-shifted to the run, so the patch loop does not wait on
+// LDS per byte (a lane with more takes the rest byte by byte).  With fewer
+// escapes the unrolled steps cost more than the waits they save, and the
+// fused reduce, bound by instruction issue, always reads byte by byte.
+template <bool REG>
 __device__ __forceinline__ void rebuild(const GroupData& d, uint32_t M, uint32_t first,
                                         const uint8_t* esc, u32x4* row, u32x4 (&o)[4]) {
     __builtin_amdgcn_wave_barrier();  // the escape bytes are in LDS
@@ -316,7 +324,28 @@ __device__ __forceinline__ void rebuild(const GroupData& d, uint32_t M, uint32_t
     row[0] = u32x4{Q[0], Q[1], Q[2], Q[3]};
     row[1] = u32x4{Q[4], Q[5], Q[6], Q[7]};
     uint8_t* rb = reinterpret_cast<uint8_t*>(row);
-    for (uint32_t m = M, i = first; m; m &= m - 1, ++i) rb[__builtin_ctz(m)] = esc[i];
+    if (REG && d.span > 128) {  // uniform
+      if (M) {
+        const uint32_t* e32 = reinterpret_cast<const uint32_t*>(esc) + (first >> 2);
+        const uint32_t sh = first & 3u;
+        uint32_t e[5], f[4];
+#pragma unroll
+        for (int j = 0; j < 5; ++j) e[j] = e32[j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[j] = __builtin_amdgcn_alignbyte(e[j + 1], e[j], sh);
+        uint32_t m = M;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (m) {
+                rb[__builtin_ctz(m)] = (uint8_t)(f[k >> 2] >> (8 * (k & 3)));
+                m &= m - 1;
+            }
+        }
+        for (uint32_t i = first + 16; m; m &= m - 1, ++i) rb[__builtin_ctz(m)] = esc[i];
+      }
+    } else {
+        for (uint32_t m = M, i = first; m; m &= m - 1, ++i) rb[__builtin_ctz(m)] = esc[i];
+    }
     const u32x4 r0 = row[0], r1 = row[1];
     const uint32_t Qe[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
     assemble(Qe, d.sm, o);
@@ -389,7 +418,7 @@ __device__ __forceinline__ uint32_t decode_group_all(const DecodeArgs& a, const 
             const uint32_t incl = wave_inclusive_scan(cnt);
             if (readlane(incl, 63) != cur.span) bad |= kBadCount;
             if (!bad) {
-                rebuild(cur, M, first + incl - cnt, escb, row, o);
+                rebuild<!REDUCE>(cur, M, first + incl - cnt, escb, row, o);
                 if (REDUCE) have = true;
                 else store_values<TAIL>(a.out + sd.in_off, sd.n, g, lane, o);
             }
@@ -478,7 +507,7 @@ __device__ __forceinline__ uint32_t decode_one(const uint8_t* st, uint64_t cap, 
     const uint32_t cnt = __builtin_popcount(M);
     const uint32_t incl = wave_inclusive_scan(cnt);
     if (readlane(incl, 63) != d.span) bad |= kBadCount;
-    if (!bad) rebuild(d, M, first + incl - cnt, reinterpret_cast<const uint8_t*>(esc_lds), row, o);
+    if (!bad) rebuild<false>(d, M, first + incl - cnt, reinterpret_cast<const uint8_t*>(esc_lds), row, o);
     return bad;
 }
 
