@@ -24,15 +24,21 @@
 
 namespace zc {
 
+// mx: the largest masked exponent field (bits 7-14 of each half) of the
+// lane's 32 values, per half: 0x7F80 in a half only for an Inf or NaN.
 __device__ __forceinline__ void encode_group(const u32x4 (&w)[4], uint32_t L7, uint32_t (&P)[3],
-                                             u32x2 (&sm)[4]) {
+                                             u32x2 (&sm)[4], uint32_t& mx) {
     uint32_t Z[4];
+    mx = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         uint32_t c[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m)  // (e - L) << 7 per half, wrapped values clamp to 7 << 7
-            c[m] = pk_min_u16(pk_sub_u16(w[k][m] & 0x7F807F80u, L7), 0x03800380u);
+        for (int m = 0; m < 4; ++m) {  // (e - L) << 7 per half, wrapped values clamp to 7 << 7
+            const uint32_t e = w[k][m] & 0x7F807F80u;
+            mx = pk_max_u16(mx, e);
+            c[m] = pk_min_u16(pk_sub_u16(e, L7), 0x03800380u);
+        }
         // code of value 2m -> nibble m, of value 2m+1 -> nibble m + 4
         Z[k] = (c[0] >> 7) | (c[1] >> 3) | (c[2] << 1) | (c[3] << 5);
         sm[k].x = bitsel(0x80808080u, perm(w[k][1], w[k][0], 0x07050301u),
@@ -126,20 +132,16 @@ __device__ __forceinline__ uint32_t moments8_careful(const u32x4 w, uint32_t rem
 // 8-value trees of its four runs joined as (r0 + r1) + (r2 + r3), then the
 // lane butterfly.  The runs are taken one after the other, each in two
 // halves (scheduling barriers between them keep only four values' fp64
-// temporaries live).  A full group (all values < n) with only finite values
-// needs no count; otherwise the careful sums leave values past n and
-// non-finite ones out (as +0.0) and count the others.
+// temporaries live).  A full group without Inf or NaN values (careful =
+// false, decided once per group) needs no count; otherwise the careful sums
+// leave values past n and non-finite ones out (as +0.0) and count the
+// others (for finite values within the data both give the same sums).
 __device__ __forceinline__ void run_moments(const u32x4* area, uint32_t lane, uint32_t t,
-                                            uint32_t valid, double& r1, double& r2, uint32_t& cnt) {
+                                            uint32_t valid, bool careful, double& r1, double& r2,
+                                            uint32_t& cnt) {
     const u32x4 w = area[tslot(4 * lane + t)];
-    // an Inf or NaN among the 8 values (exponent field 255: adding 0x80 to a
-    // half's masked exponent bits carries into its top bit only then) or a
-    // partial group takes the careful path; the two paths share nothing
-    uint32_t top = 0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) top |= (w[m] & 0x7F807F80u) + 0x00800080u;
     uint32_t c = 8;
-    if (valid == kGroup && (top & 0x80008000u) == 0) {
+    if (!careful) {  // uniform
         moments8_full(w, r1, r2);
     } else {
         const uint32_t start = 32u * lane + 8u * t;  // the run's first value in the group
@@ -149,16 +151,18 @@ __device__ __forceinline__ void run_moments(const u32x4* area, uint32_t lane, ui
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// valid: the group's values before the data's end (2048 for a full group).
+// valid: the group's values before the data's end (2048 for a full group);
+// special: the group holds an Inf or NaN.
 __device__ __forceinline__ void group_moments(const u32x4* area, uint32_t lane, uint32_t valid,
-                                              double& g1, double& g2, uint32_t& gn) {
+                                              bool special, double& g1, double& g2, uint32_t& gn) {
+    const bool careful = special || valid < kGroup;
     uint32_t cnt = 0;
     double a1, a2, b1, b2;
-    run_moments(area, lane, 0, valid, a1, a2, cnt);
-    run_moments(area, lane, 1, valid, b1, b2, cnt);
+    run_moments(area, lane, 0, valid, careful, a1, a2, cnt);
+    run_moments(area, lane, 1, valid, careful, b1, b2, cnt);
     const double h1 = a1 + b1, h2 = a2 + b2;
-    run_moments(area, lane, 2, valid, a1, a2, cnt);
-    run_moments(area, lane, 3, valid, b1, b2, cnt);
+    run_moments(area, lane, 2, valid, careful, a1, a2, cnt);
+    run_moments(area, lane, 3, valid, careful, b1, b2, cnt);
     g1 = wave_tree(h1 + (a1 + b1));
     g2 = wave_tree(h2 + (a2 + b2));
     gn = wave_sum(cnt);
@@ -207,9 +211,19 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
     u32x4 w[2][4];
     if (live) load_group(a.in + sd.in_off, sd.n, g0, lane, w[0]);
     if (!L) L = predicted_L(a.stats[first.seg].L);
-    // group moments (wave-uniform); groups past the data are -0.0 (identity)
-    double m1[2] = {-0.0, -0.0}, m2[2] = {-0.0, -0.0};
-    uint32_t mn[2] = {0, 0}, ec[2] = {0, 0};       // values, escapes
+    // each group's moments and escape count go to LDS as soon as they are
+    // known (lane 0); groups past the data keep -0.0 (the identity) and 0
+    if (lane == 0) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            s_gc[2 * wave + q] = 0;
+            if (MOMENTS) {
+                s_g1[2 * wave + q] = -0.0;
+                s_g2[2 * wave + q] = -0.0;
+                s_gn[2 * wave + q] = 0;
+            }
+        }
+    }
     if (live) {
         uint8_t* __restrict__ st = a.out + sd.out_off;
         const uint32_t L7 = (L << 7) | (L << 23);
@@ -217,23 +231,13 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
         for (int q = 0; q < 2; ++q) {
             const uint64_t g = g0 + q;
             if (g >= sd.g) break;  // uniform
-            if (MOMENTS) {
-                // the group's words go to LDS and come back after the moments,
-                // so they hold no registers while the fp64 sums run
-#pragma unroll
-                for (int k = 0; k < 4; ++k) s_area[wave][tslot(64 * k + lane)] = w[q][k];
-                __builtin_amdgcn_wave_barrier();
-                const uint64_t left = sd.n - (uint64_t)kGroup * g;
-                group_moments(s_area[wave], lane, left < kGroup ? (uint32_t)left : kGroup,
-                              m1[q], m2[q], mn[q]);
-                asm volatile("" ::: "memory");  // reload below: no forwarding of the stored words
-#pragma unroll
-                for (int k = 0; k < 4; ++k) w[q][k] = s_area[wave][tslot(64 * k + lane)];
-                __builtin_amdgcn_wave_barrier();  // before the area is reused
-            }
-            uint32_t P[3];
+            // coding first, with the words in registers; then (MOMENTS) the
+            // words go to LDS for the moments' transpose
+            uint32_t P[3], mx;
             u32x2 sm[4];
-            encode_group(w[q], L7, P, sm);
+            encode_group(w[q], L7, P, sm, mx);
+            // an Inf or NaN anywhere in the group (a half of mx at 0x7F80)
+            const bool special = MOMENTS && __ballot(((mx + 0x00800080u) & 0x80008000u) != 0) != 0;
             if ((uint64_t)kGroup * (g + 1) > sd.n) {  // last, partial group: padding codes are 0
                 const uint32_t V = valid_bits(lane, (uint32_t)(sd.n - (uint64_t)kGroup * g));
 #pragma unroll
@@ -248,34 +252,43 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
             const uint32_t M = P[0] & P[1] & P[2];
             uint32_t tot;
             const uint32_t excl = wave_prefix_small(__builtin_popcount(M), tot);
-            ec[q] = tot;
             const uint64_t gg = sd.group_base + g;
-            if (lane == 0) a.gcnt[gg] = tot;
+            if (lane == 0) {
+                a.gcnt[gg] = tot;
+                s_gc[2 * wave + q] = tot;
+            }
             uint32_t Q[8];
             exponent_bytes(w[q], Q);
             rowp[0] = u32x4{Q[0], Q[1], Q[2], Q[3]};
             rowp[1] = u32x4{Q[4], Q[5], Q[6], Q[7]};
-            if (q == 0 && g + 1 < sd.g) load_group(a.in + sd.in_off, sd.n, g + 1, lane, w[1]);
+            if (!MOMENTS && q == 0 && g + 1 < sd.g) load_group(a.in + sd.in_off, sd.n, g + 1, lane, w[1]);
             const uint8_t* rb = reinterpret_cast<const uint8_t*>(rowp);
             for (uint32_t m = M, i = 0; m; m &= m - 1, ++i) ew[excl + i] = rb[__builtin_ctz(m)];
             __builtin_amdgcn_wave_barrier();  // the wave's packed bytes are complete
             uint32_t* slot = reinterpret_cast<uint32_t*>(a.staging + gg * kGroup);
             for (uint32_t k = lane; k < (tot + 3) / 4; k += 64) slot[k] = ew32[k];
-            __builtin_amdgcn_wave_barrier();  // before the next group reuses the area
-        }
-    }
-    // the workgroup's blocks (all four waves reach this)
-    if (lane == 0) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            s_gc[2 * wave + q] = ec[q];
+            __builtin_amdgcn_wave_barrier();  // before the area is reused
             if (MOMENTS) {
-                s_g1[2 * wave + q] = m1[q];
-                s_g2[2 * wave + q] = m2[q];
-                s_gn[2 * wave + q] = mn[q];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) s_area[wave][tslot(64 * k + lane)] = w[q][k];
+                __builtin_amdgcn_wave_barrier();
+                const uint64_t left = sd.n - (uint64_t)kGroup * g;
+                double m1, m2;
+                uint32_t mn;
+                group_moments(s_area[wave], lane, left < kGroup ? (uint32_t)left : kGroup, special,
+                              m1, m2, mn);
+                if (lane == 0) {
+                    s_g1[2 * wave + q] = m1;
+                    s_g2[2 * wave + q] = m2;
+                    s_gn[2 * wave + q] = mn;
+                }
+                __builtin_amdgcn_wave_barrier();  // before the next group reuses the area
+                // group q + 1's loads once this group is done (other waves hide them)
+                if (q == 0 && g + 1 < sd.g) load_group(a.in + sd.in_off, sd.n, g + 1, lane, w[1]);
             }
         }
     }
+    // the workgroup's blocks (all four waves reach this)
     lds_barrier();
     const uint32_t per = a.block_elems / kGroup;  // groups per block: 1, 2, 4 or 8
     const uint32_t b = threadIdx.x;
