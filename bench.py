@@ -34,7 +34,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "zc_codec_gradient64M_hbm_traffic.
 KERNEL_SOURCES = {
     "zc_encode": ["zc_encode.hip", "zc_encoder.h", "zc_moments.h", "zc_internal.h", "zc_kernels.h"],
     "zc_decode": ["zc_decode.hip", "zc_internal.h", "zc_kernels.h"],
+    "zc_decode_reduce_wide": ["zc_decode.hip", "zc_internal.h", "zc_kernels.h"],
 }
+# VALU instructions per launch from the committed SQ counter summary (lines
+# "valu <kernel> <wave64 instructions> <sources sha256>"), used while the
+# kernel's sources hash to the recorded value
+ISSUE_FILE = os.path.join(ROOT, "profiles", "zc_codec_instruction_issue.txt")
+# VALU issue peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (a wave64 VALU
+# instruction holds a SIMD for 4 cycles), in 32-bit lane operations per
+# second; the fp32 vector peak of 157.3 TFLOP/s is this x 2 (FMA) x 2 (packed)
+VALU_PEAK = 256 * 4 * 16 * 2.4e9
 
 
 def log(*a):
@@ -82,6 +91,31 @@ def measured_traffic(kernel):
     except (OSError, ValueError):
         pass
     return None
+
+
+def measured_valu(kernel):
+    """Wave64 VALU instructions per launch of `kernel` from the committed SQ
+    counter summary, or None when the kernel's sources have changed since."""
+    try:
+        for line in open(ISSUE_FILE):
+            f = line.split()
+            if len(f) == 4 and f[0] == "valu" and f[1] == kernel:
+                return int(f[2]) if f[3] == sources_hash(kernel) else None
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def issue_roofline(kernel, launch_s):
+    """The kernel's VALU issue against the chip's peak, or None."""
+    n = measured_valu(kernel)
+    if n is None or launch_s <= 0:
+        return None
+    ops = n * 64 / launch_s  # lane operations per second
+    return {"bound": "alu", "kernel": kernel, "achieved": round(ops / 1e12, 2),
+            "peak": round(VALU_PEAK / 1e12, 2), "unit": "T VALU lane-op/s",
+            "frac": round(ops / VALU_PEAK, 4), "valu_instructions": n,
+            "launch_us": round(launch_s * 1e6, 2)}
 
 
 def cpu_baseline(x, chunk):
@@ -327,6 +361,12 @@ def main():
                             "launch_us": round(t_d * 1e6, 2)},
     }
 
+    # the same launches against the VALU issue peak (the encoder pass and the
+    # fused reduce are close to both bounds); instruction counts from the
+    # committed SQ counter summary
+    res["roofline_issue"] = issue_roofline("zc_encode", float(ku[0]) * 1e-6)
+    res["roofline_issue_decode"] = issue_roofline("zc_decode", t_d)
+
     if args.copy_ref:
         src = torch.empty(64 << 20, dtype=torch.int16, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -362,6 +402,7 @@ def main():
         res["reduce_ms"] = round(tr * 1e3, 4)
         res["reduce_hbm_frac"] = round((tot + 2 * n) / tr / HBM_PEAK, 4)
         res["reduce_out_GBps"] = round(2 * n / tr / 1e9, 2)
+        res["roofline_issue_reduce"] = issue_roofline("zc_decode_reduce_wide", tr)
 
     if args.all_configs:
         res["other_configs"] = other_configs(args, stream)
