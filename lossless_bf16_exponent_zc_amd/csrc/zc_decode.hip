@@ -124,11 +124,16 @@ __device__ __forceinline__ void assemble(const uint32_t (&Q)[8], const u32x2 (&s
     }
 }
 
-// BF16 round to nearest even; every NaN becomes the canonical 0x7FC0.
-__device__ __forceinline__ uint32_t to_bf16(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// BF16 round to nearest even, two values at once (low half: lo), by the
+// hardware's packed conversion (denormals kept, as this library is built);
+// every NaN becomes the canonical 0x7FC0: it is made the quiet NaN with no
+// payload first, which converts to 0x7FC0.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t to_bf16x2(float lo, float hi) {
+    const float qnan = __uint_as_float(0x7FC00000u);
+    const f32x2 v = {lo != lo ? qnan : lo, hi != hi ? qnan : hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Bytes of the lane's tile-k sm words that lie past the end (must be zero).
@@ -450,8 +455,7 @@ __device__ __forceinline__ uint32_t decode_group_all(const DecodeArgs& a, const 
         for (int k = 0; k < 4; ++k)
 #pragma unroll
             for (int mm = 0; mm < 4; ++mm)
-                o[k][mm] = to_bf16(acc[REDUCE ? 8 * k + 2 * mm : 0]) |
-                           (to_bf16(acc[REDUCE ? 8 * k + 2 * mm + 1 : 0]) << 16);
+                o[k][mm] = to_bf16x2(acc[REDUCE ? 8 * k + 2 * mm : 0], acc[REDUCE ? 8 * k + 2 * mm + 1 : 0]);
         store_values<TAIL>(a.out + sd.in_off, sd.n, g, lane, o);
     }
     return bad_all;
@@ -565,7 +569,7 @@ __device__ __forceinline__ void reduce_group_wide(const DecodeArgs& a, const Seg
             }
             u32x2 w;
 #pragma unroll
-            for (int m = 0; m < 2; ++m) w[m] = to_bf16(acc[2 * m]) | (to_bf16(acc[2 * m + 1]) << 16);
+            for (int m = 0; m < 2; ++m) w[m] = to_bf16x2(acc[2 * m], acc[2 * m + 1]);
             store_half_word<TAIL>(a.out + sd.in_off, sd.n, g, i, w);
         }
     }

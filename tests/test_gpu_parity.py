@@ -137,6 +137,51 @@ def test_decompress_reduce_scaled():
     assert np.array_equal(gpu_reduce(streams, n)[1], ref)
 
 
+def test_reduce_rounding_boundaries():
+    # fp32 sums of two shards that land on BF16 rounding ties, just above and
+    # just below them (both signs), on overflow (the largest finite value
+    # plus half its ulp is a tie that rounds to Inf), on Inf - Inf and on NaNs
+    # with payloads; and every pattern against a shuffled copy
+    rng = np.random.default_rng(11)
+    allp = np.arange(65536, dtype=np.uint16)
+    a, b = [allp], [rng.permutation(allp)]
+    k = 20000
+    e = rng.integers(10, 255, k).astype(np.uint16)
+    m = rng.integers(0, 128, k).astype(np.uint16)
+    sg = (rng.integers(0, 2, k).astype(np.uint16) << 15).astype(np.uint16)
+    x0 = (sg | (e << 7) | m).astype(np.uint16)
+    for flip in (0, 0x8000):  # half an ulp added, then subtracted
+        for de, dm in ((8, 0), (8, 1), (9, 0x7F)):  # the tie, just above, just below
+            a.append(x0)
+            b.append(((sg ^ flip) | ((e - de) << 7) | dm).astype(np.uint16))
+    sp = [(0x7F7F, 0x7F7F), (0x7F7F, 0x7B00), (0xFF7F, 0xFB00), (0x7F7F, 0x7AFF), (0x7F80, 0xFF80),
+          (0x7F80, 0x3F80), (0x7FC1, 0x3F80), (0xFF81, 0x0001), (0x7F81, 0x7F80), (0x0001, 0x8001),
+          (0x8000, 0x8000), (0x0000, 0x8000), (0x0080, 0x0001), (0x007F, 0x0001)]
+    a.append(np.array([p for p, _ in sp], np.uint16))
+    b.append(np.array([q for _, q in sp], np.uint16))
+    x0, x1 = np.concatenate(a), np.concatenate(b)
+    n = x0.size
+    streams = [oracle.compress(x0), oracle.compress(x1)]
+    ref = oracle.decompress_reduce(streams, n)
+    bits, got = gpu_reduce(streams, n)
+    assert bits == 0
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(hex(x0[i]), hex(x1[i]), hex(got[i]), hex(ref[i])) for i in bad[:8]]
+    # the sums themselves, independently: fp32 adds and the rounding formula
+    f = lambda u: (u.astype(np.uint32) << 16).view(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        acc = (f(x0) + f(x1)).view(np.uint32)
+    nan = (acc & 0x7FFFFFFF) > 0x7F800000
+    rne = ((acc.astype(np.uint64) + 0x7FFF + ((acc >> 16) & 1)) >> 16).astype(np.uint16)
+    assert np.array_equal(got, np.where(nan, np.uint16(0x7FC0), rne))
+    # the same sums through the kernel that walks 9..16 shards in turn
+    # (seven all-zero shards after the two)
+    zero = oracle.compress(np.zeros(n, np.uint16))
+    bits, got9 = gpu_reduce(streams + [zero] * 7, n)
+    assert bits == 0
+    assert np.array_equal(got9, oracle.decompress_reduce(streams + [zero] * 7, n))
+
+
 def _mutants(s, N):
     h = oracle.parse_header(s)
     out = []
