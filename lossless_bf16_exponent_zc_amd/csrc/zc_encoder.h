@@ -12,7 +12,9 @@
 // packed 16-bit ops give (e - L) clamped to 7 for two values at a time;
 // nibble packing and a 4-way bit interleave turn the lane's 32 codes into
 // its three plane words; plane words and sign+mantissa bytes go out at once
-// (static offsets).  Escapes (code 7 = all three plane bits set) are counted
+// (static offsets).  The same masked exponent fields give, by a packed max,
+// whether the group holds an Inf or NaN (the moments then take their careful
+// path).  Escapes (code 7 = all three plane bits set) are counted
 // and ranked across the wave with ballots; each lane puts its 32 exponent
 // bytes in an LDS row (plane-bit order) and copies its escapes' bytes from
 // there, in code order, into the wave's packed LDS area, which goes out in
@@ -182,13 +184,16 @@ __device__ __forceinline__ uint32_t predicted_L(uint32_t raw) {
 // several whole ones when the chunk is smaller.  Codes with window L; each
 // group's escape count and each block's total; with MOMENTS, the blocks'
 // moment partials: the tree needs each lane to hold 32 consecutive values,
-// so a group is transposed through the wave's LDS area first, and groups
-// join pairwise into blocks.
-// LDS per wave: 4112 bytes, the group's values for the transpose, then a
-// 32-byte exponent row per lane and the packed escapes (every value may
-// escape).  Every thread of the 256-thread workgroup calls this (barriers).
-// L = 0: the predicted window, read once the item's loads are out (the
-// first pass: its waves do not wait for the statistics before loading).
+// so once a group is coded its words are transposed through the wave's LDS
+// area, and groups join pairwise into blocks.  A wave loads its second
+// group once the first is done, so the two groups' words are never live
+// together (the encoder runs at 64 VGPRs, 8 waves per SIMD).
+// LDS per wave: 4112 bytes, first a 32-byte exponent row per lane and the
+// packed escapes (every value may escape), then the group's values for the
+// transpose.  Every thread of the 256-thread workgroup calls this
+// (barriers).  L = 0: the predicted window, read once the item's loads are
+// out (the first pass: its waves do not wait for the statistics before
+// loading).
 template <bool MOMENTS>
 __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint32_t L) {
     __shared__ u32x4 s_area[4][257];  // per wave, 4112 bytes
