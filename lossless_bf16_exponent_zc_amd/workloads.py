@@ -17,6 +17,9 @@ with the shapes of the evaluated collectives:
 * ``shards``    -- 8 reduce-scatter shards of 33,554,432 values ~ N(0, 1e-3^2)
 * ``gaussian_device`` -- N(0, scale^2) of any size drawn on the GPU (for the
                    largest segment a plan accepts, 2^32 - 1 values)
+* ``mixed``     -- a seeded mix for randomized tests: Gaussian of a random
+                   binade of scale with zeros, subnormals, Inf and NaN
+                   injected, or uniform bit patterns
 
 Every draw uses ``torch.Generator(device="cpu")`` with a fixed seed, in fp32,
 in the order written below, then rounds to BF16 (nearest even).  The result is
@@ -135,4 +138,25 @@ def gaussian_device(n: int, seed: int = 0, scale: float = 1e-3, device: str = "c
     z.mul_(scale)
     bits = z.to(torch.bfloat16).view(torch.int16)
     del z
+    return bits
+
+
+def mixed(n: int, seed: int) -> np.ndarray:
+    """One of four kinds, drawn from `seed`: plain Gaussian times 2^k
+    (k in -30..29); the same with about 1% of the positions replaced by
+    specials (+-0, subnormals, +-Inf, NaNs with payloads); the same with about
+    30% replaced; or uniform 16-bit patterns."""
+    rng = np.random.default_rng(seed)
+    kind = int(rng.integers(0, 4))
+    if kind == 3:
+        return rng.integers(0, 65536, n, dtype=np.uint16)
+    scale = float(2.0 ** int(rng.integers(-30, 30)))
+    z = torch.from_numpy((rng.standard_normal(n) * scale).astype(np.float32))
+    bits = to_bits(z).copy()
+    if kind > 0 and n:
+        specials = np.array([0x0000, 0x8000, 0x0001, 0x807F, 0x0040, 0x7F80, 0xFF80,
+                             0x7FC0, 0x7F81, 0xFFFF], dtype=np.uint16)
+        frac = 0.01 if kind == 1 else 0.3
+        pos = rng.random(n) < frac
+        bits[pos] = specials[rng.integers(0, specials.size, int(pos.sum()))]
     return bits
