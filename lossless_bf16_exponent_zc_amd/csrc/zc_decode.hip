@@ -214,20 +214,28 @@ __device__ __forceinline__ void fetch(const uint8_t* st, uint64_t cap, const Seg
     const uint32_t gpc = C / kGroup, k = g >> (__builtin_ctz(C) - 11);
     const bool last_in_chunk = ((g + 1) & (gpc - 1)) == 0 || g + 1 == sd.g;
     const uint8_t* fb = fixed_ok ? st : dummy;  // the fixed regions, or the stand-in
-    uint32_t t0 = 0, t1 = 0, rel = 0, rel1 = 0;
+    uint32_t t0 = 0, t1 = 0, rel = 0, rel1 = 0, gw0 = 0, gw1 = 0;
     if (EARLY) {
-        // table entries k, k + 1, and group-table entries g, g + 1 from the
-        // two aligned dwords that hold them (gtab_off is a multiple of 4), so
-        // that all of it can come in scalar loads; everything read here lies
-        // before esc_off (past the last entry: padding or the code region)
+        // table entries k, k + 1 (scalar loads) and group-table entries g,
+        // g + 1; everything read here lies before esc_off (past the last
+        // entry: padding or the code region).  FLAT (the fused reduce, whose
+        // workgroup reads one group of each shard): the two aligned dwords
+        // that hold the entries (gtab_off is a multiple of 4), by scalar
+        // loads.  Otherwise 16-bit vector loads issued before the data
+        // words': with many segments, scalar loads of every segment's group
+        // table crowd the scalar cache.
         const uint32_t* tw = reinterpret_cast<const uint32_t*>(fb + (fixed_ok ? kHeaderBytes + 4ull * k : 0));
-        const uint32_t* gw = reinterpret_cast<const uint32_t*>(fb + (fixed_ok ? (sd.gtab_off + 2ull * g) & ~3ull : 0));
         t0 = tw[0];
         t1 = tw[1];
-        const uint64_t gq = (uint64_t)gw[0] | ((uint64_t)gw[1] << 32);
-        const uint32_t sh = fixed_ok ? 16u * (g & 1u) : 0u;
-        rel = (uint32_t)(gq >> sh) & 0xFFFFu;
-        rel1 = last_in_chunk ? rel : (uint32_t)(gq >> (sh + 16)) & 0xFFFFu;
+        if (FLAT) {
+            const uint32_t* gw = reinterpret_cast<const uint32_t*>(fb + (fixed_ok ? (sd.gtab_off + 2ull * g) & ~3ull : 0));
+            gw0 = gw[0];
+            gw1 = gw[1];
+        } else {
+            const uint16_t* gh = reinterpret_cast<const uint16_t*>(fb + (fixed_ok ? sd.gtab_off + 2ull * g : 0));
+            gw0 = gh[0];
+            gw1 = gh[1];
+        }
     }
     __builtin_amdgcn_sched_barrier(0);  // the data words' loads after the header's and tables'
     const uint8_t* cw = fb + (fixed_ok ? sd.code_off + 768ull * g : 0) + 4u * lane;
@@ -236,35 +244,27 @@ __device__ __forceinline__ void fetch(const uint8_t* st, uint64_t cap, const Seg
     for (int b = 0; b < 3; ++b) d.P[b] = ld<uint32_t>(cw + 256 * b);
 #pragma unroll
     for (int q = 0; q < 4; ++q) d.sm[q] = ld<u32x2>(sw + 512 * q);
+    // every header and table word is needed here, after all the loads are
+    // issued: the compiler may not sink any of them behind a check (the
+    // scalar loads then all go out in the first round)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"s"(h.w[0]), "s"(h.w[1]), "s"(h.w[2]), "s"(h.w[3]), "s"(h.w[4]), "s"(h.w[5]),
+                 "s"(h.w[6]), "s"(h.w[7]), "s"(h.w[8]), "s"(h.w[9]), "s"(h.w[10]), "s"(h.w[11]),
+                 "s"(h.w[12]), "s"(h.w[13]), "s"(h.w[14]), "s"(h.w[15]), "s"(t0), "s"(t1));
+    if (EARLY && FLAT) {
+        asm volatile("" ::"s"(gw0), "s"(gw1));
+        const uint64_t gq = (uint64_t)gw0 | ((uint64_t)gw1 << 32);
+        const uint32_t sh = fixed_ok ? 16u * (g & 1u) : 0u;
+        rel = (uint32_t)(gq >> sh) & 0xFFFFu;
+        rel1 = last_in_chunk ? rel : (uint32_t)(gq >> (sh + 16)) & 0xFFFFu;
+    } else if (EARLY) {
+        rel = gw0;
+        rel1 = last_in_chunk ? rel : gw1;
+    }
 
     uint64_t E;
     uint32_t L;
     uint32_t bad = check_header<FLAT>(h, hdr_ok, cap, sd, C, E, L);
-    if (!FLAT) {  // the checks below only for a valid header (a branch)
-        d.bad = bad;
-        d.L = d.t0 = d.rel = d.span = 0;
-        if (bad) return;
-        if (!EARLY) {
-            const uint32_t* table = reinterpret_cast<const uint32_t*>(st + kHeaderBytes);
-            const uint16_t* gtab = reinterpret_cast<const uint16_t*>(st + sd.gtab_off);
-            t0 = table[k];
-            t1 = table[k + 1];
-            rel = gtab[g];
-            rel1 = gtab[last_in_chunk ? g : g + 1];
-        }
-        d.L = L;
-        d.t0 = t0;
-        d.rel = rel;
-        const uint32_t next = last_in_chunk ? t1 - t0 : rel1;
-        if (t0 > t1 || t1 > E || (k == 0 && t0 != 0) || (k + 1 == sd.k && t1 != E) ||
-            ((g & (gpc - 1)) == 0 && rel != 0))
-            d.bad |= kBadTable;
-        else if (rel > next || next > t1 - t0)
-            d.bad |= kBadCount;
-        else
-            d.span = next - rel;
-        return;
-    }
     if (!EARLY && !bad) {
         const uint32_t* table = reinterpret_cast<const uint32_t*>(st + kHeaderBytes);
         const uint16_t* gtab = reinterpret_cast<const uint16_t*>(st + sd.gtab_off);
