@@ -195,6 +195,9 @@ __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
     cc.run = 0;
     cc.in_table = false;
     if (r == 0 && sd.k) chunk_counts(a, sd, st, cc);
+    // the first pass's window, loaded behind the rounds above and before any
+    // store, so that the check below does not wait for a load of its own
+    const uint32_t pred = a.enc.pred[seg];
     double s1 = 0.0, s2 = 0.0;
     uint64_t n = 0;
     if (moments) {
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
     __syncthreads();
     const uint32_t L = s_L;
     if (sd.k == 0) return;
-    if (L == a.enc.pred[seg]) {  // the prediction held (always, with a fixed window)
+    if (L == pred) {  // the prediction held (always, with a fixed window)
         if (r == 0) place_offsets(a, sd, seg, st, cc);
         return;
     }
