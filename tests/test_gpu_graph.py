@@ -4,7 +4,8 @@ synchronisation), so a caller can capture them once and replay them.  Each
 replay runs on new input written into the captured buffers, with eager work
 and synchronisations between replays, and must give the oracle's streams and
 the eager calls' outputs, also when the window moves between replays (the
-captured encoder then codes again on the device).
+captured encoder then codes again on the device), at several chunk sizes and
+with a window fixed by the caller.
 """
 import numpy as np
 import pytest
@@ -42,8 +43,9 @@ def streams_of(plan, out, sizes):
             for s in range(plan.num_segments)]
 
 
-def test_captured_round_trip_replays():
-    plan = Plan(SIZES)
+@pytest.mark.parametrize("chunk,window", [(65536, None), (2048, None), (16384, 130)])
+def test_captured_round_trip_replays(chunk, window):
+    plan = Plan(SIZES, chunk)
     x = plan.empty_input()
     out, sizes, ws = plan.empty_output(), plan.empty_sizes(), plan.empty_workspace()
     y, ws_d = plan.empty_input(), plan.empty_workspace()
@@ -56,20 +58,20 @@ def test_captured_round_trip_replays():
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):  # warm-up outside the capture
-        plan.compress(x, out, sizes, ws)
+        plan.compress(x, out, sizes, ws, window=window)
         plan.decompress(out, y, ws_d)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        plan.compress(x, out, sizes, ws)
+        plan.compress(x, out, sizes, ws, window=window)
         plan.decompress(out, y, ws_d)
     torch.cuda.synchronize()
 
     for r in range(5):
         segs = inputs(r)
-        say(f"  replay {r}: sizes {SIZES}, window shift {[0, 12, 12, -7, 0][r]}")
+        say(f"  replay {r}: sizes {SIZES}, chunk {chunk}, window {window}, shift {[0, 12, 12, -7, 0][r]}")
         x.copy_(pack_inputs(plan, segs))
         out.fill_(0xA5)
         y.fill_(0x5A5A)
@@ -77,14 +79,14 @@ def test_captured_round_trip_replays():
         g.replay()
         torch.cuda.synchronize()
 
-        plan.compress(x, out_e, sizes_e, ws_e)  # eager, between replays
+        plan.compress(x, out_e, sizes_e, ws_e, window=window)  # eager, between replays
         plan.decompress(out_e, y_e, ws_de)
         torch.cuda.synchronize()
 
         got = streams_of(plan, out, sizes)
         assert got == streams_of(plan, out_e, sizes_e), f"replay {r}: graph and eager streams differ"
         for s, seg in enumerate(segs):
-            assert got[s] == oracle.compress(seg), f"replay {r}, segment {s}: stream differs"
+            assert got[s] == oracle.compress(seg, C=chunk, L=window), f"replay {r}, segment {s}: stream differs"
         assert plan.read_status(ws_d) == 0
         for s, n in enumerate(SIZES):
             o = plan.input_offset(s)
