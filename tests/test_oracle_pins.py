@@ -23,7 +23,7 @@ import oracle
 from oracle import derive_window_constant
 from lossless_bf16_exponent_zc_amd import workloads as W
 
-from conftest import read_golden
+from conftest import check_escape_order_stream, escape_order_input, read_golden
 
 C = 65536
 
@@ -193,6 +193,114 @@ def test_variance_against_exact_rationals():
         depth = max(1, math.ceil(math.log2(n)))
         u = Fraction(2) ** -53
         assert abs(Fraction(var) - exact) <= (3 * depth + 4) * u * ms
+
+
+def rne_f64(q):
+    """The exact rational q rounded to the nearest fp64, ties to even, done
+    by hand: scale |q| by a power of two into [2^52, 2^53), round that
+    integer part, scale back (normal range, which the callers stay in)."""
+    q = Fraction(q)
+    if q == 0:
+        return 0.0
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    m = a * Fraction(2) ** (52 - e)
+    while m >= 2 ** 53:
+        e, m = e + 1, m / 2
+    while m < 2 ** 52:
+        e, m = e - 1, m * 2
+    i = m.numerator // m.denominator
+    r = m - i
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and i % 2 == 1):
+        i += 1
+    v = math.ldexp(i, e - 52)  # exact: i <= 2^53
+    return -v if q < 0 else v
+
+
+def f64_bits(v):
+    return struct.unpack("<Q", struct.pack("<d", v))[0]
+
+
+def test_rne_f64_is_correctly_rounded():
+    # against CPython's correctly rounded int / int division, and on exact
+    # halfway cases built by hand
+    rng = np.random.default_rng(30)
+    for _ in range(2000):
+        a = int(rng.integers(1, 2 ** 62)) * (1 if rng.random() < 0.5 else -1)
+        b = int(rng.integers(1, 2 ** 62))
+        assert rne_f64(Fraction(a, b)) == a / b
+    one = Fraction(1)
+    ulp = Fraction(1, 2 ** 52)
+    assert rne_f64(one + ulp / 2) == 1.0                      # tie to even (down)
+    assert rne_f64(one + ulp + ulp / 2) == 1.0 + 2.0 ** -51   # tie to even (up)
+    assert rne_f64(one + ulp / 2 + Fraction(1, 2 ** 80)) == 1.0 + 2.0 ** -52
+
+
+def _variance_by_steps(S1, S2, n):
+    """(mean, ex2, sq, var): each operation of the oracle's variance rounded
+    to fp64 by hand from the exact rationals of its operands."""
+    d = Fraction(n)
+    mean = rne_f64(Fraction(S1) / d)
+    ex2 = rne_f64(Fraction(S2) / d)
+    sq = rne_f64(Fraction(mean) * Fraction(mean))
+    var = rne_f64(Fraction(ex2) - Fraction(sq))
+    return mean, ex2, sq, (var if var > 0 else 0.0)
+
+
+def test_variance_three_rounded_operations():
+    # pin P5: var = S2/n - mean*mean with mean = S1/n, three separately
+    # rounded operations and no fused multiply-add, on moments of real
+    # tensors (random sizes, scales and offsets: a nonzero mean makes the
+    # subtraction cancel, where a different rounding sequence shows)
+    rng = np.random.default_rng(31)
+    differs_fma = differs_alt = 0
+    for trial in range(200):
+        n = int(rng.integers(2, 3000))
+        scale = 2.0 ** int(rng.integers(-60, 60))
+        offset = float(rng.standard_normal()) * 10.0 ** float(rng.uniform(-1, 2))
+        z = (rng.standard_normal(n) + offset) * scale
+        x = W.to_bits(torch.from_numpy(z.astype(np.float32)))
+        S1, S2, nf, var, _ = oracle.sigma(x)
+        mean, ex2, sq, want = _variance_by_steps(S1, S2, nf)
+        assert f64_bits(var) == f64_bits(want), (trial, var, want)
+        fma = rne_f64(Fraction(ex2) - Fraction(mean) * Fraction(mean))
+        alt = rne_f64(Fraction(rne_f64(Fraction(S2) - Fraction(rne_f64(Fraction(S1) * Fraction(mean)))))
+                      / Fraction(nf))
+        differs_fma += fma != want
+        differs_alt += alt != want
+    # the sample is one where both plausible mistakes would have shown
+    assert differs_fma > 20 and differs_alt > 20, (differs_fma, differs_alt)
+
+
+def test_variance_rounding_fixture():
+    (g,) = read_golden("variance_rounding.txt")
+    x = hexwords(g["input"])
+    S1, S2, n, var, L = oracle.sigma(x)
+    h = lambda k: float.fromhex(g[k])
+    assert (S1, S2, n) == (h("S1"), h("S2"), int(g["n"]))
+    assert S1 == Fraction(430, 128) and S2 == Fraction(61642, 16384)
+    mean, ex2, sq, want = _variance_by_steps(S1, S2, n)
+    assert (mean, ex2, sq, want) == (h("mean"), h("ex2"), h("sq"), h("var"))
+    assert Fraction(want) == Fraction(397045865585, 2 ** 51)
+    fma = rne_f64(Fraction(ex2) - Fraction(mean) * Fraction(mean))
+    alt = rne_f64(Fraction(rne_f64(Fraction(S2) - Fraction(rne_f64(Fraction(S1) * Fraction(mean))))) / 3)
+    assert (fma, alt) == (h("var_fma"), h("var_alt"))
+    assert len({want, fma, alt}) == 3
+    assert f64_bits(var) == f64_bits(want) and L == int(g["L"])
+
+
+def test_escape_order_golden():
+    # three groups over two chunks, escapes in several lane words, tiles and
+    # groups, whose code order differs from their index order
+    (g,) = read_golden("escape_order.txt")
+    x = escape_order_input(g)
+    S1, S2, n, var, L = oracle.sigma(x)
+    assert (S1, S2, n, var, L) == (float(g["S1"]), float(g["S2"]), int(g["n"]),
+                                   float(g["var"]), int(g["L"]))
+    assert var == Fraction(6220, 6144).__float__()
+    s = oracle.compress(x, C=int(g["chunk"]))
+    check_escape_order_stream(s, g)
+    assert np.array_equal(oracle.decompress(s, x.size, int(g["chunk"])), x)
 
 
 def test_sigma_skips_nonfinite_values():
