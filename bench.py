@@ -32,9 +32,10 @@ HBM_PEAK = 8.0e12  # bytes/s, MI355X
 # a kernel's figure is used while its sources hash to the value recorded there
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "zc_codec_gradient64M_hbm_traffic.txt")
 KERNEL_SOURCES = {
-    "zc_encode": ["zc_encode.hip", "zc_encoder.h", "zc_moments.h", "zc_internal.h", "zc_kernels.h"],
-    "zc_decode": ["zc_decode.hip", "zc_internal.h", "zc_kernels.h"],
-    "zc_decode_reduce_wide": ["zc_decode.hip", "zc_internal.h", "zc_kernels.h"],
+    "zc_encode": ["zc_encode.hip", "zc_encoder.h", "zc_moments.h", "zc_internal.h", "zc_kernels.h",
+                  "zc_format.h"],
+    "zc_decode": ["zc_decode.hip", "zc_internal.h", "zc_kernels.h", "zc_format.h"],
+    "zc_decode_reduce_wide": ["zc_decode.hip", "zc_internal.h", "zc_kernels.h", "zc_format.h"],
 }
 # VALU instructions per launch from the committed SQ counter summary (lines
 # "valu <kernel> <wave64 instructions> <sources sha256>"), used while the
@@ -118,11 +119,27 @@ def issue_roofline(kernel, launch_s):
             "launch_us": round(launch_s * 1e6, 2)}
 
 
+def host_threads():
+    """Threads for the oracle's all-core leg: the CPUs this process may run
+    on, at most 16 (a one-GPU machine's share of its host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(x, chunk):
-    """Time the oracle's compress + decompress on a bounded host sample
-    (whole round trips of the workload's first 16M values until 10 s have
-    passed)."""
+    """Time the oracle's compress + decompress on bounded host samples.
+
+    Single thread: whole round trips of the workload's first 16M values until
+    about 10 s have passed.  All cores: the workload's first T x 4M values as
+    T segments (T threads, each segment its own stream, as a multi-segment
+    plan codes them), round trips repeated for about 10 s; every thread's
+    bytes are checked identical to a single-threaded run of the same segment
+    first.  The oracle's C calls release the interpreter lock."""
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
     n = min(x.size, 1 << 24)
     sample = np.ascontiguousarray(x[:n])
     reps, t0 = 0, time.perf_counter()
@@ -133,10 +150,37 @@ def cpu_baseline(x, chunk):
         el = time.perf_counter() - t0
         if el > 10.0 or reps >= 30:  # about 10 s of the oracle's work
             break
-    return {"value": round(2 * n * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"compress+decompress round trip of the first {n} values of the "
-                      f"workload, {reps} rep(s), {el:.1f} s, single-threaded C"}
+    single = 2 * n * reps / el / 1e9
+
+    T = host_threads()
+    seg = min(1 << 22, x.size // T)
+    segs = [np.ascontiguousarray(x[i * seg:(i + 1) * seg]) for i in range(T)]
+    ref = [oracle.compress(v, C=chunk) for v in segs]  # single-threaded, once
+
+    def trip(i):
+        st = oracle.compress(segs[i], C=chunk)
+        oracle.decompress(st, seg, C=chunk)
+        return st
+
+    with ThreadPoolExecutor(max_workers=T) as ex:
+        first = list(ex.map(trip, range(T)))
+        assert first == ref, "threaded oracle streams differ from the single-threaded ones"
+        preps, t0 = 0, time.perf_counter()
+        while True:
+            list(ex.map(trip, range(T)))
+            preps += 1
+            pel = time.perf_counter() - t0
+            if pel > 10.0 or preps >= 50:
+                break
+    allcore = 2 * seg * T * preps / pel / 1e9
+    return {"value": round(allcore, 4), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "host_cpus": os.cpu_count(),
+            "single_thread_value": round(single, 4),
+            "sample": f"all cores: {T} threads, each a compress+decompress round trip of its "
+                      f"own {seg}-value segment of the workload (one stream per segment, "
+                      f"bytes identical to a single-threaded run), {preps} round(s) in "
+                      f"{pel:.1f} s; single thread: the first {n} values as one stream, "
+                      f"{reps} rep(s) in {el:.1f} s; plain C oracle built -O2"}
 
 
 def time_config(name, segs, chunk, args, stream):
@@ -163,8 +207,8 @@ def time_config(name, segs, chunk, args, stream):
     r = {"workload": name, "elements": n, "segments": len(segs), "chunk_elems": chunk,
          "compress_ms": round(tc * 1e3, 4), "decompress_ms": round(td * 1e3, 4),
          "compress_GBps": round(2 * n / tc / 1e9, 2), "decompress_GBps": round(2 * n / td / 1e9, 2),
-         "compress_hbm_frac": round((4 * n + sb) / tc / HBM_PEAK, 4),
-         "compress_hbm_frac_one_read": round((2 * n + sb) / tc / HBM_PEAK, 4),
+         "compress_hbm_frac": round((2 * n + sb) / tc / HBM_PEAK, 4),
+         "compress_hbm_frac_method_bytes": round((4 * n + sb) / tc / HBM_PEAK, 4),
          "decompress_hbm_frac": round((2 * n + sb) / td / HBM_PEAK, 4),
          "ratio": round(2 * n / sb, 4)}
     del plan, xd, out, sizes, ws, y, flush
@@ -178,7 +222,7 @@ def other_configs(args, stream):
     res = [time_config("Llama3-8B MLP layer: 3 BF16 matrices (4096x14336, 14336x4096, "
                        "4096x14336), one segment each", W.llama_mlp(), 65536, args, stream)]
     log("MoE 256 experts")
-    bits, counts = W.moe(device="cuda")
+    bits, counts = W.moe()
     offs = np.concatenate([[0], np.cumsum(counts)])
     segs = [bits[offs[i]:offs[i + 1]] for i in range(len(counts))]
     res.append(time_config("MoE all-to-all: 256 expert segments, 65,536 tokens x 7168", segs,
@@ -260,14 +304,64 @@ def main():
     tcw = timed(comp, args.steps, args.warmup, stream)
     tdw = timed(dec, args.steps, args.warmup, stream)
 
-    # algorithmic bytes as the method is defined (a sigma pass and an encode
-    # pass each read the input, then the stream is written); this library's
-    # compress reads the input once (the moments come from the encoder's
-    # pass), so compress_hbm_frac_one_read gives the same time against
-    # input + stream.  Decompress reads the stream and writes the values.
-    comp_bytes = 2 * N + 2 * N + stream_bytes
-    comp_bytes_one_read = 2 * N + stream_bytes
+    # the bytes this library must move: the input once (the moments come
+    # from the coding pass), the stream out; decompress reads the stream and
+    # writes the values.  The method-bytes count adds a second read of the
+    # input (a separate sigma pass before coding), as the survey counts it.
+    comp_bytes = 2 * N + stream_bytes
+    comp_bytes_method = 2 * N + 2 * N + stream_bytes
     dec_bytes = stream_bytes + 2 * N
+
+    # the window prediction failing on every timed call: two resident tensors
+    # whose windows differ (the workload, and the workload times 16, exact in
+    # BF16: every exponent 4 higher) compressed in turn on one workspace, so
+    # each call codes with the other tensor's window first and the segment is
+    # coded again in the same call
+    log("prediction miss")
+    x16 = (xd.view(torch.bfloat16) * 16).view(torch.int16)
+    out16 = plan.empty_output()
+    pair = [(xd, out), (x16, out16)]
+    turn = [0]
+
+    def comp_alt():
+        a, o = pair[turn[0] % 2]
+        turn[0] += 1
+        plan.compress(a, o, sizes, ws)
+
+    tmiss = timed(comp_alt, args.steps, args.warmup, stream, flush)
+    comp()  # the workload's own window back in the workspace
+    torch.cuda.synchronize()
+    assert int(sizes.cpu()[0]) == stream_bytes
+
+    # the caller's fixed window (the tensor's own, so the stream is the same)
+    L = int(out[6].item())
+    tfixed = timed(lambda: plan.compress(xd, out, sizes, ws, window=L), args.steps, args.warmup,
+                   stream, flush)
+    torch.cuda.synchronize()
+    assert int(sizes.cpu()[0]) == stream_bytes
+
+    # steady state: calls back to back over 4 buffer sets (1.7 GB, more than
+    # the caches hold), so every call reads cold inputs and earlier calls'
+    # dirty outputs are written back during later timed calls
+    log("steady state")
+    sets = [(xd.clone(), plan.empty_output(), plan.empty_input()) for _ in range(4)]
+    for xi, oi, yi in sets:
+        plan.compress(xi, oi, sizes, ws)
+    rot = [0]
+
+    def rot_call(kind):
+        xi, oi, yi = sets[rot[0] % 4]
+        rot[0] += 1
+        if kind == "c":
+            plan.compress(xi, oi, sizes, ws)
+        else:
+            plan.decompress(oi, yi, ws)
+
+    tcs = timed(lambda: rot_call("c"), 4 * args.steps, 4 * args.warmup, stream)
+    tds = timed(lambda: rot_call("d"), 4 * args.steps, 4 * args.warmup, stream)
+    torch.cuda.synchronize()
+    assert all(torch.equal(yi[:N], xd[:N]) for _, _, yi in sets)
+    del sets, x16, out16
 
     # the encoder pass, timed on its own: HIP events on this stream around
     # each kernel of a compress call (cold, like the calls above)
@@ -322,11 +416,22 @@ def main():
         "decompress_GBps": round(2 * N / t_d / 1e9, 2),
         "compress_ms": round(t_c * 1e3, 4),
         "decompress_ms": round(t_d * 1e3, 4),
+        # bytes this library moves (input once + stream) / cold time / 8 TB/s
         "compress_hbm_frac": round(comp_bytes / t_c / HBM_PEAK, 4),
-        "compress_hbm_frac_one_read": round(comp_bytes_one_read / t_c / HBM_PEAK, 4),
+        # the survey's method count (a separate sigma read of the input too)
+        "compress_hbm_frac_method_bytes": round(comp_bytes_method / t_c / HBM_PEAK, 4),
         "decompress_hbm_frac": round(dec_bytes / t_d / HBM_PEAK, 4),
         "timing": "cold: caches filled by a 1 GiB read before every timed call; "
                   "medians of the timed calls",
+        # every timed call a failed window prediction (two tensors, windows 4 apart)
+        "compress_ms_miss": round(float(np.median(tmiss)) * 1e3, 4),
+        # zc_compress_window with the tensor's own window (no moments)
+        "compress_window_ms": round(float(np.median(tfixed)) * 1e3, 4),
+        # back-to-back calls over 4 rotating buffer sets (no flush)
+        "compress_ms_steady": round(float(np.median(tcs)) * 1e3, 4),
+        "decompress_ms_steady": round(float(np.median(tds)) * 1e3, 4),
+        "compress_hbm_frac_steady": round(comp_bytes / float(np.median(tcs)) / HBM_PEAK, 4),
+        "decompress_hbm_frac_steady": round(dec_bytes / float(np.median(tds)) / HBM_PEAK, 4),
         "compress_ms_best": round(min(tc) * 1e3, 4),
         "decompress_ms_best": round(min(td) * 1e3, 4),
         "compress_ms_warm": round(t_cw * 1e3, 4),
@@ -382,7 +487,7 @@ def main():
 
     if not args.no_reduce:
         log("decompress-reduce workload")
-        del xd, y, flush
+        del y, flush
         shards = W.shards()
         n = shards[0].size
         rplan = zc.Plan([n], chunk)
@@ -396,7 +501,7 @@ def main():
             xi[:n] = torch.from_numpy(s.view(np.int16)).cuda()
             cplan.compress(xi, b, csz, cws)
             tot += int(csz.cpu()[0])
-        rws, r = rplan.empty_workspace(), rplan.empty_input()
+        rws, r = rplan.empty_workspace(decode_only=True), rplan.empty_input()
         red = lambda: rplan.decompress_reduce(bufs, r, rws, capacity=cap)
         flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
         tr = float(np.median(timed(red, args.steps, args.warmup, stream, flush)))
@@ -405,6 +510,43 @@ def main():
         res["reduce_hbm_frac"] = round((tot + 2 * n) / tr / HBM_PEAK, 4)
         res["reduce_out_GBps"] = round(2 * n / tr / 1e9, 2)
         res["roofline_issue_reduce"] = issue_roofline("zc_decode_reduce_wide", tr)
+
+        # the native path: the same 8 shards uncompressed, summed by a plain
+        # kernel in the same order with the same rounding (the same bits)
+        log("native reduce")
+        raw = [torch.from_numpy(s_.view(np.int16)).cuda() for s_ in shards]
+        rn = torch.empty(n, dtype=torch.int16, device="cuda")
+        native = lambda: zc.reduce_native(raw, rn)
+        tn = float(np.median(timed(native, args.steps, args.warmup, stream, flush)))
+        assert torch.equal(rn, r[:n])
+        res["reduce_native_ms"] = round(tn * 1e3, 4)
+        res["reduce_native_hbm_frac"] = round((8 * 2 * n + 2 * n) / tn / HBM_PEAK, 4)
+
+        # the reduce-scatter switch for this shape (8 GPUs, one shard per
+        # peer per link): the sender compresses its 7 outgoing shards (one
+        # 7-segment plan), each link carries one shard, and the receiver runs
+        # the fused reduce instead of the native one.  Compressed pays when
+        #   t_compress7 + compressed/B + (t_fused - t_native) < raw/B
+        log("reduce-scatter switch")
+        splan = zc.Plan([n] * 7, chunk)
+        sx = splan.empty_input()
+        for i in range(7):
+            o = splan.input_offset(i)
+            sx[o:o + n] = raw[i + 1]
+        sout, ssz, sws = splan.empty_output(), splan.empty_sizes(), splan.empty_workspace()
+        c7 = lambda: splan.compress(sx, sout, ssz, sws)
+        t7 = float(np.median(timed(c7, args.steps, args.warmup, stream, flush)))
+        per_link = int(ssz.cpu().numpy().mean())
+        extra = max(0.0, (tr - tn) * 1e6)
+        xgmi = 153.0  # GB/s, one xGMI link of an MI355X
+        pref, be = zc.prefer_compressed(2 * n, per_link, t7 * 1e6, extra, xgmi)
+        res["reduce_scatter_switch"] = {
+            "compress_7_shards_ms": round(t7 * 1e3, 4),
+            "fused_minus_native_us": round((tr - tn) * 1e6, 2),
+            "raw_bytes_per_link": 2 * n, "compressed_bytes_per_link": per_link,
+            "break_even_link_GBps": round(be, 1),
+            "xgmi_link_GBps": xgmi, "prefer_compressed_on_xgmi": pref}
+        del splan, sx, sout, ssz, sws, raw, rn
 
     if args.all_configs:
         res["other_configs"] = other_configs(args, stream)

@@ -131,6 +131,12 @@ uint64_t zc_plan_out_bytes(const zc_plan *plan);
  * value (compress stages escape exponents there, 2048 bytes per 2048-value
  * group) plus a few bytes per group and chunk. */
 uint64_t zc_plan_workspace_bytes(const zc_plan *plan);
+/* Workspace bytes zc_decompress, zc_decompress_reduce and zc_read_status
+ * need: 4 bytes per 2048-value group (the rejection bits), rounded up to 256,
+ * plus 2048 bytes (256 for a plan without values).  A receiver that only
+ * decodes can pass a workspace of this size; a workspace of
+ * zc_plan_workspace_bytes, which is never smaller, serves every call. */
+uint64_t zc_plan_decode_workspace_bytes(const zc_plan *plan);
 
 /*
  * Compress every segment of d_in (BF16, zc_plan_input_elems elements) into
@@ -152,8 +158,18 @@ zc_status zc_compress(const zc_plan *plan, const void *d_in, void *d_out,
                       uint64_t out_capacity, uint64_t *d_stream_bytes,
                       void *d_ws, uint64_t ws_bytes, hipStream_t stream);
 
-/* As zc_compress, but every segment uses the window L (1..248) given here
- * instead of one derived from its standard deviation (no moments). */
+/*
+ * As zc_compress, but every segment uses the window L (1..248) given here
+ * instead of one derived from its standard deviation: no moments are taken
+ * and no statistics are written.  The coding itself is the ZipCCL notes'
+ * ("Key idea and contribution", technique 1): exponents in [L, L+6] become
+ * 3-bit codes, the others escape with their full byte, so the stream is
+ * lossless whatever L is; only its size depends on L.  This serves a window
+ * known in advance, e.g. one carried over from an earlier iteration of the
+ * same tensor (the exponent reuse across iterations named by the CIERA
+ * title that the pages list).  Errors as zc_compress, plus
+ * ZC_ERR_INVALID_ARG for L outside 1..248.
+ */
 zc_status zc_compress_window(const zc_plan *plan, const void *d_in, void *d_out,
                              uint64_t out_capacity, uint64_t *d_stream_bytes,
                              uint32_t window_L, void *d_ws, uint64_t ws_bytes,
@@ -189,24 +205,40 @@ zc_status zc_compress_timed(const zc_plan *plan, const void *d_in, void *d_out,
                             float *us);
 
 /*
- * Decode every segment's stream (at d_in + zc_plan_stream_offset(s); the
- * buffer holds in_capacity readable bytes) into d_out (BF16, laid out as
- * d_in of zc_compress).  Streams are validated on the device; a group of
- * 2048 values whose checks fail writes no output and is reported by
- * zc_read_status.  Reads never leave [d_in, d_in + in_capacity).
+ * Decompression, the last step of the ZipCCL notes' compressed-collective
+ * workflow (Fig. 5: compress, exchange sizes, communicate, decompress), as
+ * the inverse of the exponent coding of "Key idea and contribution",
+ * technique 1: e = L + code for codes 0..6, the next escape byte for code 7,
+ * sign and mantissa from the raw byte; a raw stream's words are copied.
+ * Decodes every segment's stream (at d_in + zc_plan_stream_offset(s); the
+ * buffer holds in_capacity readable bytes, 256-B aligned) into d_out (BF16,
+ * laid out as d_in of zc_compress, 16-B aligned).  d_ws: at least
+ * zc_plan_decode_workspace_bytes bytes, 256-B aligned; it receives the
+ * rejection bits.  Streams are validated on the device; a group of 2048
+ * values whose checks fail writes no output and is reported by
+ * zc_read_status, and other groups are decoded as usual.  Reads never leave
+ * [d_in, d_in + in_capacity).  Argument errors: ZC_ERR_INVALID_ARG (null or
+ * misaligned pointer), ZC_ERR_CAPACITY (workspace too small).
  */
 zc_status zc_decompress(const zc_plan *plan, const void *d_in,
                         uint64_t in_capacity, void *d_out, void *d_ws,
                         uint64_t ws_bytes, hipStream_t stream);
 
 /*
- * Receive side of a reduce-scatter: the plan has one segment of N values;
- * d_streams is a HOST array of `nstreams` (1..16) device pointers, each to a
- * stream of N values with stream_capacity readable bytes.  Writes
+ * Receive side of a compressed reduce-scatter (the ZipCCL notes' "Key idea
+ * and contribution", technique 3, names the reduce-scatter path; the UCCL-Zip
+ * page's abstract argues for running decompression inside the collective's
+ * kernel, which removes extra memory traffic and launches): every shard is
+ * decoded (as zc_decompress) and summed in one kernel, so the only global
+ * write is the sum.  The plan has one segment of N values; d_streams is a
+ * HOST array of `nstreams` (1..16) device pointers (256-B aligned), each to
+ * a stream of N values with stream_capacity readable bytes.  Writes
  * d_out[i] = bf16_rne(((x0[i] + x1[i]) + x2[i]) + ...) with the sum in fp32
- * in the given stream order; any NaN sum gives 0x7FC0.  A rejected stream
- * makes the affected 2048-value groups write no output (see
- * zc_read_status).
+ * in the given stream order (no flush of subnormals); any NaN sum gives
+ * 0x7FC0.  A rejected stream makes the affected 2048-value groups write no
+ * output (see zc_read_status).  d_ws as for zc_decompress.  Argument errors:
+ * ZC_ERR_INVALID_ARG (plan with more than one segment, nstreams outside
+ * 1..16, null or misaligned pointer), ZC_ERR_CAPACITY (workspace too small).
  */
 zc_status zc_decompress_reduce(const zc_plan *plan, const void *const *d_streams,
                                uint32_t nstreams, uint64_t stream_capacity,
@@ -214,9 +246,14 @@ zc_status zc_decompress_reduce(const zc_plan *plan, const void *const *d_streams
                                hipStream_t stream);
 
 /*
- * Synchronises `stream`, then ORs the ZC_FMT_* bits of the most recent
- * zc_decompress / zc_decompress_reduce that used this workspace into
- * *host_bits.  Returns ZC_ERR_FORMAT if any bit is set.
+ * Rejection report of the decompress step of the ZipCCL notes' workflow
+ * (Fig. 5).  The pages define no stream validation; this is the library's
+ * own error channel for data-dependent errors, which the enqueue-only calls
+ * cannot return.  Synchronises `stream`, then ORs the ZC_FMT_* bits of the
+ * most recent zc_decompress / zc_decompress_reduce that used this workspace
+ * (any layout: the bits sit at its start) into *host_bits.  Returns
+ * ZC_ERR_FORMAT if any bit is set, ZC_ERR_HIP if the stream or the copy
+ * failed, ZC_ERR_INVALID_ARG for a null argument.
  */
 zc_status zc_read_status(const zc_plan *plan, const void *d_ws,
                          hipStream_t stream, uint32_t *host_bits);
@@ -246,6 +283,20 @@ zc_status zc_read_sigma(const zc_plan *plan, const void *d_ws, uint32_t s,
  */
 int zc_prefer_compressed(uint64_t raw_bytes, uint64_t compressed_bytes, double compress_us,
                          double decompress_us, double link_GBps, double *break_even_GBps);
+
+/*
+ * The native path of a reduce-scatter's receive side, the alternative that
+ * the ZipCCL notes' switch ("Key idea and contribution", technique 3) weighs
+ * the compressed path against: d_out[i] = bf16_rne(((x0[i] + x1[i]) + x2[i])
+ * + ...) over `nshards` (1..16) uncompressed BF16 shards of n values each,
+ * summed in fp32 in the given order with the rounding of
+ * zc_decompress_reduce (so both give the same bits for the same values).
+ * d_shards: HOST array of device pointers, each 16-B aligned; d_out: n BF16
+ * values, 16-B aligned.  One kernel on `stream`, no workspace.  Errors:
+ * ZC_ERR_INVALID_ARG (null or misaligned pointer, nshards outside 1..16).
+ */
+zc_status zc_reduce_native(const void *const *d_shards, uint32_t nshards, uint64_t n,
+                           void *d_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

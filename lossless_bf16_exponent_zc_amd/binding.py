@@ -24,10 +24,11 @@ EXPORTS = (
     "zc_plan_input_offset",
     "zc_plan_input_elems", "zc_plan_stream_offset", "zc_plan_max_stream_bytes",
     "zc_plan_code_offset", "zc_plan_escape_offset",
-    "zc_plan_out_bytes", "zc_plan_workspace_bytes", "zc_compress",
+    "zc_plan_out_bytes", "zc_plan_workspace_bytes", "zc_plan_decode_workspace_bytes",
+    "zc_compress",
     "zc_compress_window", "zc_compress_split", "zc_compress_timed", "zc_decompress",
     "zc_decompress_reduce",
-    "zc_read_status", "zc_read_sigma", "zc_prefer_compressed",
+    "zc_read_status", "zc_read_sigma", "zc_prefer_compressed", "zc_reduce_native",
 )
 
 
@@ -61,7 +62,7 @@ def lib() -> ctypes.CDLL:
     for name, rt in (("zc_plan_num_segments", u32), ("zc_plan_chunk_elems", u32),
                      ("zc_plan_flags", u32),
                      ("zc_plan_input_elems", u64), ("zc_plan_out_bytes", u64),
-                     ("zc_plan_workspace_bytes", u64)):
+                     ("zc_plan_workspace_bytes", u64), ("zc_plan_decode_workspace_bytes", u64)):
         f = getattr(L, name)
         f.argtypes = [vp]
         f.restype = rt
@@ -77,6 +78,7 @@ def lib() -> ctypes.CDLL:
     L.zc_decompress.argtypes = [vp, vp, u64, vp, vp, u64, vp]
     L.zc_decompress_reduce.argtypes = [vp, P(vp), u32, u64, vp, vp, u64, vp]
     L.zc_read_status.argtypes = [vp, vp, vp, P(u32)]
+    L.zc_reduce_native.argtypes = [P(vp), u32, u64, vp, vp]
     L.zc_prefer_compressed.argtypes = [u64, u64, ctypes.c_double, ctypes.c_double,
                                        ctypes.c_double, P(ctypes.c_double)]
     L.zc_prefer_compressed.restype = ctypes.c_int
@@ -86,7 +88,7 @@ def lib() -> ctypes.CDLL:
     for name in ("zc_plan_create", "zc_plan_create_ex", "zc_compress", "zc_compress_window", "zc_compress_timed",
                  "zc_compress_split",
                  "zc_decompress", "zc_decompress_reduce", "zc_read_status",
-                 "zc_read_sigma"):
+                 "zc_read_sigma", "zc_reduce_native"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -122,6 +124,39 @@ def _ptr(t) -> ctypes.c_void_p:
 
 def _nbytes(t) -> int:
     return t.numel() * t.element_size()
+
+
+def check_buffer(t, what: str, elem_size: int | None = None, min_elems: int = 0,
+                 min_bytes: int = 0):
+    """Raise ZcError(ZC_ERR_INVALID_ARG / ZC_ERR_CAPACITY) unless t is a
+    contiguous tensor on a GPU with the given element size and at least
+    min_elems elements and min_bytes bytes.  The C ABI takes bare pointers,
+    so the sizes it cannot see are checked here, before any call."""
+    if not getattr(t, "is_cuda", False):
+        raise ZcError(ZC_ERR_INVALID_ARG, f"{what}: not a GPU tensor")
+    if not t.is_contiguous():
+        raise ZcError(ZC_ERR_INVALID_ARG, f"{what}: not contiguous")
+    if elem_size is not None and t.element_size() != elem_size:
+        raise ZcError(ZC_ERR_INVALID_ARG,
+                      f"{what}: {t.element_size()}-byte elements, {elem_size} expected")
+    if t.numel() < min_elems or _nbytes(t) < min_bytes:
+        raise ZcError(ZC_ERR_CAPACITY, f"{what}: {t.numel()} elements, {_nbytes(t)} bytes "
+                                       f"(needs {min_elems} elements, {min_bytes} bytes)")
+
+
+def reduce_native(shards, out, stream=None):
+    """Enqueue the native (uncompressed) fixed-order fp32 sum of BF16 shards
+    (16-bit tensors of equal length) into out, rounded as decompress_reduce
+    rounds."""
+    if not 1 <= len(shards) <= 16:
+        raise ZcError(ZC_ERR_INVALID_ARG, "reduce_native: 1..16 shards")
+    n = shards[0].numel()
+    for i, t in enumerate(shards):
+        check_buffer(t, f"shard {i}", 2, n)
+    check_buffer(out, "out", 2, n)
+    arr = (ctypes.c_void_p * len(shards))(*[t.data_ptr() for t in shards])
+    _check(lib().zc_reduce_native(arr, len(shards), n, _ptr(out), _stream(stream)),
+           "zc_reduce_native")
 
 
 PLAN_RAW_FALLBACK = 0x1  # ZC_PLAN_RAW_FALLBACK
@@ -172,6 +207,11 @@ class Plan:
     def workspace_bytes(self) -> int:
         return lib().zc_plan_workspace_bytes(self._h)
 
+    @property
+    def decode_workspace_bytes(self) -> int:
+        """Workspace bytes the decoders need (status words and a stand-in)."""
+        return lib().zc_plan_decode_workspace_bytes(self._h)
+
     def input_offset(self, s: int) -> int:
         return lib().zc_plan_input_offset(self._h, s)
 
@@ -198,17 +238,29 @@ class Plan:
         import torch
         return torch.empty(self.out_bytes, dtype=torch.uint8, device=device)
 
-    def empty_workspace(self, device="cuda"):
+    def empty_workspace(self, device="cuda", decode_only: bool = False):
         import torch
-        return torch.empty(self.workspace_bytes, dtype=torch.uint8, device=device)
+        n = self.decode_workspace_bytes if decode_only else self.workspace_bytes
+        return torch.empty(n, dtype=torch.uint8, device=device)
 
     def empty_sizes(self, device="cuda"):
         import torch
         return torch.zeros(self.num_segments, dtype=torch.int64, device=device)
 
     # codec calls ----------------------------------------------------------
+    def _check_compress(self, x, out, stream_bytes, ws):
+        check_buffer(x, "input", 2, self.input_elems)
+        check_buffer(out, "output", 1)
+        check_buffer(stream_bytes, "stream_bytes", 8, self.num_segments)
+        check_buffer(ws, "workspace", 1)
+
+    def _check_decode(self, out, ws):
+        check_buffer(out, "output", 2, self.input_elems)
+        check_buffer(ws, "workspace", 1)
+
     def compress(self, x, out, stream_bytes, ws, window: int | None = None, stream=None):
         """Enqueue compression of x (BF16 bits, 16-bit dtype) into out."""
+        self._check_compress(x, out, stream_bytes, ws)
         if window is None:
             rc = lib().zc_compress(self._h, _ptr(x), _ptr(out), _nbytes(out),
                                    _ptr(stream_bytes), _ptr(ws), _nbytes(ws),
@@ -224,6 +276,7 @@ class Plan:
         """Enqueue compress() and record fixed_ready (a torch.cuda.Event that
         has been recorded once, so it exists) as soon as the headers, chunk
         tables, code planes, sign+mantissa bytes and sizes are final."""
+        self._check_compress(x, out, stream_bytes, ws)
         rc = lib().zc_compress_split(self._h, _ptr(x), _ptr(out), _nbytes(out),
                                      _ptr(stream_bytes), _ptr(ws), _nbytes(ws),
                                      _stream(stream), ctypes.c_void_p(fixed_ready.cuda_event))
@@ -233,6 +286,7 @@ class Plan:
         """Compress as compress() and wait for it; returns the three kernels'
         times in microseconds (encoder pass, window, escape placement), from
         HIP events recorded on the stream between them."""
+        self._check_compress(x, out, stream_bytes, ws)
         us = (ctypes.c_float * 3)()
         rc = lib().zc_compress_timed(self._h, _ptr(x), _ptr(out), _nbytes(out),
                                      _ptr(stream_bytes), _ptr(ws), _nbytes(ws),
@@ -241,14 +295,21 @@ class Plan:
         return [float(v) for v in us]
 
     def decompress(self, comp, out, ws, capacity: int | None = None, stream=None):
-        """Enqueue decoding of the packed streams in comp into out."""
+        """Enqueue decoding of the packed streams in comp into out; capacity
+        (default: all of comp) is the readable bytes the kernels are told of."""
         cap = _nbytes(comp) if capacity is None else int(capacity)
+        check_buffer(comp, "compressed input", 1, 0, cap)
+        self._check_decode(out, ws)
         rc = lib().zc_decompress(self._h, _ptr(comp), cap, _ptr(out), _ptr(ws),
                                  _nbytes(ws), _stream(stream))
         _check(rc, "zc_decompress")
 
     def decompress_reduce(self, streams, out, ws, capacity: int, stream=None):
-        """Enqueue decode + fixed-order fp32 sum of single-segment streams."""
+        """Enqueue decode + fixed-order fp32 sum of single-segment streams
+        (each tensor holds at least `capacity` bytes)."""
+        for i, t in enumerate(streams):
+            check_buffer(t, f"stream {i}", 1, 0, int(capacity))
+        self._check_decode(out, ws)
         arr = (ctypes.c_void_p * len(streams))(*[s.data_ptr() for s in streams])
         rc = lib().zc_decompress_reduce(self._h, arr, len(streams), int(capacity),
                                         _ptr(out), _ptr(ws), _nbytes(ws),

@@ -26,15 +26,11 @@
 
 #include "zc.h"
 #include "zc_kernels.h"
+#include "zc_plan_layout.h"
 
 using namespace zc;
 
-struct zc_plan {
-    uint32_t nseg = 0, chunk = 0, block = 0, flags = 0;
-    std::vector<SegDesc> segs;
-    std::vector<ItemDesc> chunks, groups, pairs, witems;  // pairs: encoder waves; witems: window workgroups
-    uint64_t input_elems = 0, out_bytes = 0;
-    WsLayout ws{};
+struct zc_plan : zc::PlanLayout {  // the host layout plus its device tables
     SegDesc* d_segs = nullptr;
     ItemDesc* d_chunks = nullptr;
     ItemDesc* d_groups = nullptr;
@@ -44,7 +40,6 @@ struct zc_plan {
 
 namespace {
 
-uint64_t a256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
 uint64_t cdiv(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -59,6 +54,13 @@ zc_status launch_status() {
 zc_status check_ws(const zc_plan* p, const void* d_ws, uint64_t ws_bytes) {
     if (!d_ws || !aligned(d_ws, 256)) return ZC_ERR_INVALID_ARG;
     if (ws_bytes < p->ws.total) return ZC_ERR_CAPACITY;
+    return ZC_OK;
+}
+
+// The decoders need the status words and the stand-in only.
+zc_status check_dec_ws(const zc_plan* p, const void* d_ws, uint64_t ws_bytes) {
+    if (!d_ws || !aligned(d_ws, 256)) return ZC_ERR_INVALID_ARG;
+    if (ws_bytes < p->ws.dec_total) return ZC_ERR_CAPACITY;
     return ZC_OK;
 }
 
@@ -163,76 +165,13 @@ zc_status zc_plan_create_ex(uint32_t num_segments, const uint64_t* segment_elems
     if (!out_plan || num_segments == 0 || !segment_elems) return ZC_ERR_INVALID_ARG;
     *out_plan = nullptr;
     if (flags & ~ZC_PLAN_RAW_FALLBACK) return ZC_ERR_INVALID_ARG;
-    const uint32_t C = chunk_elems ? chunk_elems : 65536u;
-    if (C < kGroup || C > 65536u || (C & (C - 1))) return ZC_ERR_UNSUPPORTED;
-
     zc_plan* p = new (std::nothrow) zc_plan;
     if (!p) return ZC_ERR_HIP;
-    p->nseg = num_segments;
-    p->chunk = C;
-    p->flags = flags;
-    p->block = C < kSigmaBlock ? C : kSigmaBlock;
-    uint64_t in_off = 0, out_off = 0, sb = 0;
-    for (uint32_t s = 0; s < num_segments; ++s) {
-        const uint64_t n = segment_elems[s];
-        if (n >= (1ull << 32)) {
-            delete p;
-            return ZC_ERR_UNSUPPORTED;
-        }
-        SegDesc d{};
-        d.n = n;
-        d.k = (uint32_t)cdiv(n, C);
-        d.g = (uint32_t)cdiv(n, kGroup);
-        d.nsb = (uint32_t)cdiv(n, p->block);
-        d.gtab_off = kHeaderBytes + 4ull * (d.k + 1);
-        d.code_off = a256(d.gtab_off + 2ull * d.g);
-        d.sm_off = d.code_off + 768ull * d.g;
-        d.esc_off = d.sm_off + 2048ull * d.g;
-        d.max_bytes = d.esc_off + n;
-        d.in_off = in_off;
-        d.out_off = out_off;
-        d.sb_base = (uint32_t)sb;
-        uint64_t pb = 1;
-        while (pb < d.nsb) pb <<= 1;
-        sb += d.nsb ? pb : 0;  // leaf slots span the power of two
-        d.group_base = (uint32_t)p->groups.size();
-        d.chunk_base = (uint32_t)p->chunks.size();
-        in_off += (n + 7) & ~uint64_t(7);
-        out_off += a256(d.max_bytes);
-        for (uint32_t k = 0; k < d.k; ++k) p->chunks.push_back(ItemDesc{s, k});
-        for (uint32_t g = 0; g < d.g; ++g) p->groups.push_back(ItemDesc{s, g});
-        d.wg_base = (uint32_t)(p->pairs.size() / 4);
-        for (uint32_t q = 0; q < (d.g + 1) / 2; ++q) p->pairs.push_back(ItemDesc{s, q});
-        while (p->pairs.size() % 4) p->pairs.push_back(ItemDesc{0xFFFFFFFFu, 0});  // whole workgroups
-        d.nwg = (uint32_t)(p->pairs.size() / 4) - d.wg_base;
-        // window workgroups: enough to code the segment again at about 16
-        // items each, at most 256 (each joins all of the segment's partials)
-        d.wr = (uint32_t)std::min<uint64_t>(256, std::max<uint64_t>(1, cdiv(d.nwg, 16)));
-        for (uint32_t r = 0; r < d.wr; ++r) p->witems.push_back(ItemDesc{s, r});
-        if (p->groups.size() >= (1ull << 31)) {
-            delete p;
-            return ZC_ERR_UNSUPPORTED;
-        }
-        p->segs.push_back(d);
+    if (const int e = build_layout(num_segments, segment_elems, chunk_elems, flags, *p)) {
+        delete p;
+        return static_cast<zc_status>(e);
     }
-    p->input_elems = in_off;
-    p->out_bytes = out_off;
-    const uint64_t G = p->groups.size(), B = sb, K = p->chunks.size();
-    const uint64_t W = p->pairs.size();
-    uint64_t o = 0;
-    p->ws.status = o;   o += a256(4 * G);
-    p->ws.ps1 = o;      o += a256(8 * B);
-    p->ws.ps2 = o;      o += a256(8 * B);
-    p->ws.pn = o;       o += a256(4 * B);
-    p->ws.pesc = o;     o += a256(4 * B);
-    p->ws.stats = o;    o += a256(sizeof(SegStat) * num_segments);
-    p->ws.gcnt = o;     o += a256(4 * G);
-    p->ws.pred = o;     o += a256(4ull * num_segments);
-    p->ws.done = o;     o += a256(4ull * num_segments);
-    p->ws.zero = o;     o += 256;
-    p->ws.staging = o;  o += a256((uint64_t)kGroup * G + 16);
-    p->ws.total = o;
-
+    const uint64_t G = p->groups.size(), K = p->chunks.size(), W = p->pairs.size();
     if (hipMalloc(&p->d_segs, sizeof(SegDesc) * p->segs.size()) != hipSuccess ||
         hipMalloc(&p->d_chunks, sizeof(ItemDesc) * (K ? K : 1)) != hipSuccess ||
         hipMalloc(&p->d_groups, sizeof(ItemDesc) * (G ? G : 1)) != hipSuccess ||
@@ -286,6 +225,7 @@ uint64_t zc_plan_max_stream_bytes(const zc_plan* p, uint32_t s) {
 }
 uint64_t zc_plan_out_bytes(const zc_plan* p) { return p ? p->out_bytes : 0; }
 uint64_t zc_plan_workspace_bytes(const zc_plan* p) { return p ? p->ws.total : 0; }
+uint64_t zc_plan_decode_workspace_bytes(const zc_plan* p) { return p ? p->ws.dec_total : 0; }
 
 zc_status zc_compress(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
                       uint64_t* d_stream_bytes, void* d_ws, uint64_t ws_bytes, hipStream_t stream) {
@@ -334,7 +274,7 @@ zc_status zc_decompress(const zc_plan* p, const void* d_in, uint64_t in_capacity
                         void* d_ws, uint64_t ws_bytes, hipStream_t stream) {
     if (!p || !d_in || !aligned(d_in, 256)) return ZC_ERR_INVALID_ARG;
     if (p->input_elems && (!d_out || !aligned(d_out, 16))) return ZC_ERR_INVALID_ARG;
-    if (zc_status e = check_ws(p, d_ws, ws_bytes)) return e;
+    if (zc_status e = check_dec_ws(p, d_ws, ws_bytes)) return e;
     if (!ngroups(p)) return ZC_OK;
     DecodeArgs a{};
     a.segs = p->d_segs;
@@ -348,7 +288,7 @@ zc_status zc_decompress(const zc_plan* p, const void* d_in, uint64_t in_capacity
     a.ngroups = ngroups(p);
     a.out = static_cast<uint16_t*>(d_out);
     a.status = ws_ptr<uint32_t>(p, d_ws, p->ws.status);
-    a.dummy = ws_ptr<uint8_t>(p, d_ws, p->ws.staging);  // 2048 B per group + 16
+    a.dummy = ws_ptr<uint8_t>(p, d_ws, p->ws.dummy);  // 2048 readable bytes
     if (a.single) hipLaunchKernelGGL(zc_decode<true>, dim3(group_grid(p)), dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(zc_decode<false>, dim3(group_grid(p)), dim3(256), 0, stream, a);
     return launch_status();
@@ -362,7 +302,7 @@ zc_status zc_decompress_reduce(const zc_plan* p, const void* const* d_streams, u
     for (uint32_t s = 0; s < nstreams; ++s)
         if (!d_streams[s] || !aligned(d_streams[s], 256)) return ZC_ERR_INVALID_ARG;
     if (p->input_elems && (!d_out || !aligned(d_out, 16))) return ZC_ERR_INVALID_ARG;
-    if (zc_status e = check_ws(p, d_ws, ws_bytes)) return e;
+    if (zc_status e = check_dec_ws(p, d_ws, ws_bytes)) return e;
     if (!ngroups(p)) return ZC_OK;
     DecodeArgs a{};
     a.segs = p->d_segs;
@@ -376,7 +316,7 @@ zc_status zc_decompress_reduce(const zc_plan* p, const void* const* d_streams, u
     a.ngroups = ngroups(p);
     a.out = static_cast<uint16_t*>(d_out);
     a.status = ws_ptr<uint32_t>(p, d_ws, p->ws.status);
-    a.dummy = ws_ptr<uint8_t>(p, d_ws, p->ws.staging);  // 2048 B per group + 16
+    a.dummy = ws_ptr<uint8_t>(p, d_ws, p->ws.dummy);  // 2048 readable bytes
     if (nstreams <= 8)  // one wave per shard, one workgroup per group
         hipLaunchKernelGGL(zc_decode_reduce_wide, dim3(ngroups(p)), dim3(64 * nstreams), 0, stream, a);
     else
@@ -414,6 +354,32 @@ zc_status zc_read_sigma(const zc_plan* p, const void* d_ws, uint32_t s, hipStrea
     if (var) *var = st.var;
     if (L) *L = st.L;
     return ZC_OK;
+}
+
+zc_status zc_reduce_native(const void* const* d_shards, uint32_t nshards, uint64_t n, void* d_out,
+                           hipStream_t stream) {
+    if (!d_shards || nshards < 1 || nshards > kMaxStreams) return ZC_ERR_INVALID_ARG;
+    if (n && (!d_out || !aligned(d_out, 16))) return ZC_ERR_INVALID_ARG;
+    NativeReduceArgs a{};
+    for (uint32_t s = 0; s < nshards; ++s) {
+        if (n && (!d_shards[s] || !aligned(d_shards[s], 16))) return ZC_ERR_INVALID_ARG;
+        a.in[s] = static_cast<const uint16_t*>(d_shards[s]);
+    }
+    if (!n) return ZC_OK;
+    a.out = static_cast<uint16_t*>(d_out);
+    a.n = n;
+    // one 8-value word per thread (a grid-stride loop past 2^20 workgroups)
+    const dim3 grid((uint32_t)std::min<uint64_t>(std::max<uint64_t>(1, cdiv(n / 8, 256)), 1u << 20));
+    switch (nshards) {
+#define ZC_NATIVE_CASE(S) \
+        case S: hipLaunchKernelGGL(zc_reduce_native<S>, grid, dim3(256), 0, stream, a); break;
+        ZC_NATIVE_CASE(1) ZC_NATIVE_CASE(2) ZC_NATIVE_CASE(3) ZC_NATIVE_CASE(4)
+        ZC_NATIVE_CASE(5) ZC_NATIVE_CASE(6) ZC_NATIVE_CASE(7) ZC_NATIVE_CASE(8)
+        ZC_NATIVE_CASE(9) ZC_NATIVE_CASE(10) ZC_NATIVE_CASE(11) ZC_NATIVE_CASE(12)
+        ZC_NATIVE_CASE(13) ZC_NATIVE_CASE(14) ZC_NATIVE_CASE(15) ZC_NATIVE_CASE(16)
+#undef ZC_NATIVE_CASE
+    }
+    return launch_status();
 }
 
 int zc_prefer_compressed(uint64_t raw_bytes, uint64_t compressed_bytes, double compress_us,

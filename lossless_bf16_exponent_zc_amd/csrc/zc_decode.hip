@@ -278,7 +278,10 @@ __device__ __forceinline__ void fetch(const uint8_t* st, uint64_t cap, const Seg
     const uint32_t next = last_in_chunk ? t1 - t0 : rel1;
     const bool tbad = (t0 > t1) | (t1 > E) | ((k == 0) & (t0 != 0)) | ((k + 1 == sd.k) & (t1 != E)) |
                       (((g & (gpc - 1)) == 0) & (rel != 0));
-    const bool cbad = (rel > next) | (next > t1 - t0);
+    // a group holds at most kGroup escapes: a larger span (a damaged group
+    // table) is rejected here, before fetch_escapes writes the span into the
+    // wave's fixed LDS area (520 dwords)
+    const bool cbad = (rel > next) | (next > t1 - t0) | (next - rel > kGroup);
     if (!bad) bad = tbad ? kBadTable : (cbad ? kBadCount : 0u);
     d.bad = bad;
     const bool use = bad == 0;
@@ -587,6 +590,62 @@ __global__ __launch_bounds__(512) void zc_decode_reduce_wide(DecodeArgs a) {
     else
         reduce_group_wide<false>(a, sd, g, gg, s_area, s_bad);
 }
+
+// The native (uncompressed) reduce-scatter receive: S BF16 shards summed in
+// fp32 in shard order and rounded as the fused reduce rounds, so the two
+// paths give the same bits.  Each thread takes one 16-byte word (8 values)
+// of every shard per step, all S loads in flight at once; the last n % 8
+// values are summed one by one by the first threads of workgroup 0.
+template <int S>
+__global__ __launch_bounds__(256) void zc_reduce_native(NativeReduceArgs a) {
+    const uint64_t words = a.n / 8;
+    const uint64_t step = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t w = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; w < words; w += step) {
+        u32x4 v[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) v[s] = reinterpret_cast<const u32x4*>(a.in[s])[w];
+        float acc[8];
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float lo = __uint_as_float(v[s][m] << 16), hi = __uint_as_float(v[s][m] & 0xFFFF0000u);
+                acc[2 * m] = s == 0 ? lo : acc[2 * m] + lo;
+                acc[2 * m + 1] = s == 0 ? hi : acc[2 * m + 1] + hi;
+            }
+        u32x4 o;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) o[m] = to_bf16x2(acc[2 * m], acc[2 * m + 1]);
+        reinterpret_cast<u32x4*>(a.out)[w] = o;
+    }
+    const uint64_t i = 8 * words + threadIdx.x;
+    if (blockIdx.x == 0 && threadIdx.x < 8 && i < a.n) {
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const float x = __uint_as_float((uint32_t)a.in[s][i] << 16);
+            acc = s == 0 ? x : acc + x;
+        }
+        a.out[i] = (uint16_t)to_bf16x2(acc, 0.f);
+    }
+}
+
+template __global__ void zc_reduce_native<1>(NativeReduceArgs);
+template __global__ void zc_reduce_native<2>(NativeReduceArgs);
+template __global__ void zc_reduce_native<3>(NativeReduceArgs);
+template __global__ void zc_reduce_native<4>(NativeReduceArgs);
+template __global__ void zc_reduce_native<5>(NativeReduceArgs);
+template __global__ void zc_reduce_native<6>(NativeReduceArgs);
+template __global__ void zc_reduce_native<7>(NativeReduceArgs);
+template __global__ void zc_reduce_native<8>(NativeReduceArgs);
+template __global__ void zc_reduce_native<9>(NativeReduceArgs);
+template __global__ void zc_reduce_native<10>(NativeReduceArgs);
+template __global__ void zc_reduce_native<11>(NativeReduceArgs);
+template __global__ void zc_reduce_native<12>(NativeReduceArgs);
+template __global__ void zc_reduce_native<13>(NativeReduceArgs);
+template __global__ void zc_reduce_native<14>(NativeReduceArgs);
+template __global__ void zc_reduce_native<15>(NativeReduceArgs);
+template __global__ void zc_reduce_native<16>(NativeReduceArgs);
 
 // Eight waves per SIMD for the plain decoder (it fits in 64 VGPRs).
 template <bool SINGLE>

@@ -62,6 +62,12 @@ struct DecodeArgs {
     SegDesc seg0;
 };
 
+struct NativeReduceArgs {
+    const uint16_t* in[kMaxStreams];  // uncompressed shards, 16-byte aligned
+    uint16_t* out;
+    uint64_t n;                       // values per shard
+};
+
 template <bool SINGLE>
 __global__ void zc_window(WindowArgs a);
 template <bool MOMENTS>
@@ -72,5 +78,7 @@ template <bool SINGLE>
 __global__ void zc_decode(DecodeArgs a);
 __global__ void zc_decode_reduce(DecodeArgs a);
 __global__ void zc_decode_reduce_wide(DecodeArgs a);
+template <int S>
+__global__ void zc_reduce_native(NativeReduceArgs a);
 
 }  // namespace zc

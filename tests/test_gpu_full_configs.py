@@ -59,7 +59,8 @@ def test_llama_mlp_layer():
 
 
 def test_moe_all_to_all_segments():
-    bits, sizes = W.moe(device="cuda")
+    # drawn as the workload states it: torch's CPU generator, seed 0
+    bits, sizes = W.moe()
     offs = np.concatenate([[0], np.cumsum(sizes)])
     segs = [bits[offs[i]:offs[i + 1]] for i in range(len(sizes))]
     check_full(segs, "MoE 256 experts")
@@ -75,5 +76,14 @@ def test_reduce_scatter_receive_8_shards():
         assert got[0] == refs[i], i
     bits, out = gpu_reduce(refs, n, CHUNK)
     assert bits == 0, hex(bits)
-    assert np.array_equal(out, oracle.decompress_reduce(refs, n, C=CHUNK))
+    want = oracle.decompress_reduce(refs, n, C=CHUNK)
+    assert np.array_equal(out, want)
     say("  reduce: bit-exact")
+    # the native (uncompressed) reduce of the same shards gives the same bits
+    import torch
+    import lossless_bf16_exponent_zc_amd as zc
+    dev = [torch.from_numpy(s.view(np.int16)).cuda() for s in shards]
+    nat = torch.empty(n, dtype=torch.int16, device="cuda")
+    zc.reduce_native(dev, nat)
+    assert np.array_equal(nat.cpu().numpy().view(np.uint16), want)
+    say("  native reduce: bit-exact")

@@ -57,12 +57,137 @@ def test_chunk_sizes(chunk):
 
 
 def test_every_pattern_every_window():
+    # all 65,536 patterns, sorted and shuffled, under the window rule and
+    # under every forced window L = 1..248: streams byte-identical to the
+    # oracle's, round trips exact (one plan and workspace for the sweep)
+    from lossless_bf16_exponent_zc_amd import Plan
+    from gpu_util import pack_inputs
     allp = np.arange(65536, dtype=np.uint16)
     shuf = np.random.default_rng(6).permutation(allp)
-    for x in (allp, shuf):
+    plan = Plan([allp.size], 8192)
+    out, sizes, ws, y = plan.empty_output(), plan.empty_sizes(), plan.empty_workspace(), plan.empty_input()
+    for name, x in (("sorted", allp), ("shuffled", shuf)):
+        say(f"  {name} patterns, every window")
         check_segments([x], chunk=8192)
-        for L in list(range(1, 249, 7)) + [248]:
-            check_segments([x], chunk=8192, window=L)
+        xd = pack_inputs(plan, [x])
+        for L in range(1, 249):
+            out.fill_(0xA5)
+            plan.compress(xd, out, sizes, ws, window=L)
+            y.fill_(0x5A5A)
+            plan.decompress(out, y, ws)
+            bits = plan.read_status(ws)
+            n = int(sizes.cpu()[0])
+            assert out[:n].cpu().numpy().tobytes() == oracle.compress(x, C=8192, L=L), (name, L)
+            assert bits == 0, (name, L, hex(bits))
+            assert np.array_equal(y[:x.size].cpu().numpy().view(np.uint16), x), (name, L)
+
+
+def test_hand_derived_fixtures():
+    # the golden streams and statistics derived by hand (tests/golden), here
+    # from the GPU: pins the kernels to the readings themselves, not only to
+    # the oracle
+    from conftest import check_escape_order_stream, escape_order_input, read_golden
+    (g,) = read_golden("escape_order.txt")
+    x = escape_order_input(g)
+    streams, plan, _, ws = gpu_compress([x], int(g["chunk"]))
+    check_escape_order_stream(streams[0], g)
+    S1, S2, n, var, L = plan.read_sigma(ws, 0)
+    assert (S1, S2, n, var, L) == (float(g["S1"]), float(g["S2"]), int(g["n"]), float(g["var"]),
+                                   int(g["L"]))
+    (v,) = read_golden("variance_rounding.txt")
+    x = np.array([int(t, 16) for t in v["input"].split()], dtype=np.uint16)
+    _, plan, _, ws = gpu_compress([x])
+    h = lambda k: float(np.float64(float.fromhex(v[k])))
+    want = (h("S1"), h("S2"), int(v["n"]), h("var"), int(v["L"]))
+    assert stat_bits(plan.read_sigma(ws, 0)) == stat_bits(want)
+    for (name, key) in (("fused multiply-add", "var_fma"), ("(S2 - S1 mean) / n", "var_alt")):
+        assert stat_bits(plan.read_sigma(ws, 0))[3] != stat_bits((0, 0, 0, h(key), 0))[3], name
+
+
+def test_damaged_group_table_large_span():
+    # chunks of 65,536 values: a group-table entry raised to its chunk's whole
+    # escape count gives the group before it a span of thousands of escapes.
+    # The decoder must reject those groups before it copies any escape into
+    # LDS; the other groups of the same workgroups (4 waves, 4 groups) decode
+    # exactly, while the oracle rejects the stream.
+    N = 65536 * 2
+    x = W.gradient(N, seed=21)  # about 20% escapes: ~13,000 per chunk
+    s = oracle.compress(x)
+    h = oracle.parse_header(s)
+    K = h["K"]
+    t0 = int.from_bytes(s[64:68], "little")
+    t1 = int.from_bytes(s[68:72], "little")
+    assert t1 - t0 > 4096
+    goff = 64 + 4 * (K + 1)
+    from lossless_bf16_exponent_zc_amd import Plan
+    plan = Plan([N])
+    for g in (5, 17, 31):  # group g - 1 gets the large span; g itself a negative one
+        b = bytearray(s)
+        b[goff + 2 * g:goff + 2 * g + 2] = (t1 - t0).to_bytes(2, "little")
+        obits, _ = oracle.decompress_status(bytes(b), N)
+        assert obits != 0
+        bits, dec = gpu_decompress(plan, streams_to_packed(plan, [bytes(b)]))
+        say(f"  group table entry {g} = {t1 - t0}: oracle 0x{obits:02x} gpu 0x{bits:02x}")
+        assert bits & 0x20  # count
+        bad = np.zeros(N // 2048, dtype=bool)
+        bad[[g - 1, g]] = True
+        got = dec[0].reshape(-1, 2048)
+        want = x.reshape(-1, 2048)
+        assert np.array_equal(got[~bad], want[~bad]), g
+        # the rejected groups wrote nothing (the output keeps its fill)
+        assert (got[bad] == 0x5A5A).all(), g
+        rbits, rgot = gpu_reduce([bytes(b), s], N)
+        assert rbits & 0x20
+        sum_ok = oracle.decompress_reduce([s, s], N).reshape(-1, 2048)
+        assert np.array_equal(rgot.reshape(-1, 2048)[~bad], sum_ok[~bad]), g
+
+
+def test_decode_only_workspace():
+    # decoders and the fused reduce with a workspace of
+    # zc_plan_decode_workspace_bytes (status words + a 2048-byte stand-in)
+    from lossless_bf16_exponent_zc_amd import Plan
+    for n in (1, 2049, 3 * 65536 + 5):
+        x = W.gradient(n, seed=n)
+        s = oracle.compress(x)
+        plan = Plan([n])
+        ws = plan.empty_workspace(decode_only=True)
+        assert ws.numel() == plan.decode_workspace_bytes < plan.workspace_bytes
+        assert plan.decode_workspace_bytes == (4 * -(-n // 2048) + 255) // 256 * 256 + 2048
+        bits, dec = gpu_decompress(plan, streams_to_packed(plan, [s]), ws=ws)
+        assert bits == 0 and np.array_equal(dec[0], x), n
+        sh = [x, W.gradient(n, seed=n + 1)]
+        streams = [oracle.compress(t) for t in sh]
+        cap = (max(len(t) for t in streams) + 255) // 256 * 256
+        dev = [torch.zeros(cap, dtype=torch.uint8, device="cuda") for _ in streams]
+        for d, t in zip(dev, streams):
+            d[:len(t)] = torch.from_numpy(np.frombuffer(t, np.uint8).copy()).cuda()
+        y = plan.empty_input()
+        plan.decompress_reduce(dev, y, ws, capacity=cap)
+        assert plan.read_status(ws) == 0
+        assert np.array_equal(y[:n].cpu().numpy().view(np.uint16), oracle.decompress_reduce(streams, n))
+    # one byte short is refused before anything is enqueued
+    from lossless_bf16_exponent_zc_amd import ZcError
+    short = torch.empty(plan.decode_workspace_bytes - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ZcError):
+        plan.decompress(streams_to_packed(plan, [s]), plan.empty_input(), short)
+
+
+@pytest.mark.parametrize("n,S", [(1, 1), (7, 3), (8, 2), (100003, 8), (65536 * 3 + 9, 16)])
+def test_reduce_native(n, S):
+    # the native path of the reduce-scatter switch: the same sums as the
+    # fused reduce of the shards' coded streams and of their raw streams
+    import lossless_bf16_exponent_zc_amd as zc
+    sh = W.shards(n=n, nshards=S)
+    if n > 20:
+        sh[0][:10] = [0x7F7F, 0x0001, 0x7F80, 0x7FC1, 0x8000, 0, 0x0080, 0xFF80, 0x3F80, 0x7F7F]
+    want = oracle.decompress_reduce([oracle.compress(t) for t in sh], n)
+    raw = oracle.decompress_reduce([oracle.compress(t, raw_fallback=True) for t in sh], n)
+    assert np.array_equal(want, raw)
+    dev = [torch.from_numpy(t.view(np.int16)).cuda() for t in sh]
+    out = torch.full((n,), 0x5A5A, dtype=torch.int16, device="cuda")
+    zc.reduce_native(dev, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), want)
 
 
 def test_special_tensors():
