@@ -159,6 +159,27 @@ zc_status zc_compress(const zc_plan *plan, const void *d_in, void *d_out,
                       void *d_ws, uint64_t ws_bytes, hipStream_t stream);
 
 /*
+ * zc_compress for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * streams and sizes, with the workspace taken from a device array inside the
+ * library (zc_static_workspace_bytes() = 80 MiB per GPU, reserved on each
+ * GPU the library runs on until the process ends) instead of a caller's
+ * buffer.  The call allocates and frees nothing; the caller still passes the
+ * input, the output and d_stream_bytes as for zc_compress.  Plans whose
+ * zc_plan_workspace_bytes exceed the array (about 80 million values) are
+ * refused with ZC_ERR_CAPACITY; ZC_ERR_HIP if the array cannot be found on
+ * the current device.  Every call on one GPU uses that GPU's one array: calls
+ * that overlap on a GPU (other streams, other threads) race and must not be
+ * made.  The array keeps the last call's contents; nothing in it needs to
+ * start at zero (the window it holds from the previous call is only a
+ * prediction, checked on every call).
+ */
+zc_status zc_compress_static(const zc_plan *plan, const void *d_in, void *d_out,
+                             uint64_t out_capacity, uint64_t *d_stream_bytes,
+                             hipStream_t stream);
+uint64_t zc_static_workspace_bytes(void);
+
+/*
  * As zc_compress, but every segment uses the window L (1..248) given here
  * instead of one derived from its standard deviation: no moments are taken
  * and no statistics are written.  The coding itself is the ZipCCL notes'

@@ -29,6 +29,7 @@ EXPORTS = (
     "zc_compress_window", "zc_compress_split", "zc_compress_timed", "zc_decompress",
     "zc_decompress_reduce",
     "zc_read_status", "zc_read_sigma", "zc_prefer_compressed", "zc_reduce_native",
+    "zc_compress_static", "zc_static_workspace_bytes",
 )
 
 
@@ -79,6 +80,9 @@ def lib() -> ctypes.CDLL:
     L.zc_decompress_reduce.argtypes = [vp, P(vp), u32, u64, vp, vp, u64, vp]
     L.zc_read_status.argtypes = [vp, vp, vp, P(u32)]
     L.zc_reduce_native.argtypes = [P(vp), u32, u64, vp, vp]
+    L.zc_compress_static.argtypes = [vp, vp, vp, u64, vp, vp]
+    L.zc_static_workspace_bytes.argtypes = []
+    L.zc_static_workspace_bytes.restype = u64
     L.zc_prefer_compressed.argtypes = [u64, u64, ctypes.c_double, ctypes.c_double,
                                        ctypes.c_double, P(ctypes.c_double)]
     L.zc_prefer_compressed.restype = ctypes.c_int
@@ -88,7 +92,7 @@ def lib() -> ctypes.CDLL:
     for name in ("zc_plan_create", "zc_plan_create_ex", "zc_compress", "zc_compress_window", "zc_compress_timed",
                  "zc_compress_split",
                  "zc_decompress", "zc_decompress_reduce", "zc_read_status",
-                 "zc_read_sigma", "zc_reduce_native"):
+                 "zc_read_sigma", "zc_reduce_native", "zc_compress_static"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -271,6 +275,17 @@ class Plan:
                                           _ptr(stream_bytes), int(window), _ptr(ws),
                                           _nbytes(ws), _stream(stream))
             _check(rc, "zc_compress_window")
+
+    def compress_static(self, x, out, stream_bytes, stream=None):
+        """Enqueue compress() with the library's own device array as the
+        workspace (zc_compress_static: allocates nothing; calls on one GPU
+        must not overlap)."""
+        check_buffer(x, "input", 2, self.input_elems)
+        check_buffer(out, "output", 1)
+        check_buffer(stream_bytes, "stream_bytes", 8, self.num_segments)
+        rc = lib().zc_compress_static(self._h, _ptr(x), _ptr(out), _nbytes(out),
+                                      _ptr(stream_bytes), _stream(stream))
+        _check(rc, "zc_compress_static")
 
     def compress_split(self, x, out, stream_bytes, ws, fixed_ready, stream=None):
         """Enqueue compress() and record fixed_ready (a torch.cuda.Event that

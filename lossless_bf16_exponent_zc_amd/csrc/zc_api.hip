@@ -21,6 +21,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -39,6 +40,34 @@ struct zc_plan : zc::PlanLayout {  // the host layout plus its device tables
 };
 
 namespace {
+
+// The workspace of zc_compress_static: a file-scope device array, one copy
+// per GPU, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: host code uses only the
+// address hipGetSymbolAddress returns for the current device.
+constexpr uint64_t kScratchBytes = 80ull << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (set up once per device, with that
+// device current), or null if the lookup failed.
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();  // leave no error for the caller's next call
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
 
 uint64_t cdiv(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -190,6 +219,9 @@ zc_status zc_plan_create_ex(uint32_t num_segments, const uint64_t* segment_elems
         zc_plan_destroy(p);
         return ZC_ERR_HIP;
     }
+    // set-up of zc_compress_static's array on this device (a failure here is
+    // reported by that call, not by the plan)
+    (void)scratch_for_current_device();
     *out_plan = p;
     return ZC_OK;
 }
@@ -261,6 +293,17 @@ zc_status zc_compress_timed(const zc_plan* p, const void* d_in, void* d_out, uin
         if (e) (void)hipEventDestroy(e);
     return st;
 }
+
+zc_status zc_compress_static(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
+                             uint64_t* d_stream_bytes, hipStream_t stream) {
+    if (!p) return ZC_ERR_INVALID_ARG;
+    if (p->ws.total > kScratchBytes) return ZC_ERR_CAPACITY;  // plan too large for the array
+    void* ws = scratch_for_current_device();
+    if (!ws) return ZC_ERR_HIP;
+    return compress_impl(p, d_in, d_out, out_capacity, d_stream_bytes, 0, ws, kScratchBytes, stream);
+}
+
+uint64_t zc_static_workspace_bytes(void) { return kScratchBytes; }
 
 zc_status zc_compress_window(const zc_plan* p, const void* d_in, void* d_out, uint64_t out_capacity,
                              uint64_t* d_stream_bytes, uint32_t window_L, void* d_ws,

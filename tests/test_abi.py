@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 27
+    assert len(names) == 29
     assert sorted(binding.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
