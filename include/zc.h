@@ -217,8 +217,10 @@ zc_status zc_compress_split(const zc_plan *plan, const void *d_in, void *d_out,
  * For profiling: zc_compress with HIP events recorded on `stream` before,
  * between and after its kernels; waits for the call to finish and writes
  * the kernels' times in microseconds to us[0] (encoder pass: moments, codes,
- * staged escapes), us[1] (window, check of the prediction, chunk table) and
- * us[2] (escape placement).  Same output as zc_compress.
+ * staged escapes), us[1] (window, check of the prediction, chunk table; on
+ * plans where one kernel does this and the escape placement, that kernel)
+ * and us[2] (escape placement when it is a kernel of its own, else 0).
+ * Same output as zc_compress.
  */
 zc_status zc_compress_timed(const zc_plan *plan, const void *d_in, void *d_out,
                             uint64_t out_capacity, uint64_t *d_stream_bytes,

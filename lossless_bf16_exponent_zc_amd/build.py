@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libzc.so")
-SOURCES = ["zc_api.hip", "zc_sigma.hip", "zc_encode.hip", "zc_decode.hip"]
+SOURCES = ["zc_api.hip", "zc_sigma.hip", "zc_encode.hip", "zc_decode.hip", "zc_finish.hip"]
 
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

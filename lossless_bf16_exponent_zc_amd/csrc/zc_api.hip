@@ -5,6 +5,10 @@
 //                      codes, sign+mantissa bytes, staged escape exponents
 //                      and escape counts, with each segment's previous window
 //                      as the prediction (or the caller's fixed window)
+//   zc_finish          the two kernels below in one launch, overlapped (chunks
+//                      of 16,384 values or more, no raw fallback, no split
+//                      event); a failed prediction is coded again chunk by
+//                      chunk there
 //   zc_window          per segment: variance -> window, statistics, header
 //                      fields known before encoding; where the prediction
 //                      failed, the segment's codes again; chunk table, sizes;
@@ -30,6 +34,8 @@
 #include "zc_plan_layout.h"
 
 using namespace zc;
+
+static_assert(kPlanRawFallback == ZC_PLAN_RAW_FALLBACK, "plan flag values agree");
 
 struct zc_plan : zc::PlanLayout {  // the host layout plus its device tables
     SegDesc* d_segs = nullptr;
@@ -126,6 +132,9 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     ea.zero = ws_ptr<uint32_t>(p, d_ws, p->ws.zero);
     ea.staging = ws_ptr<uint8_t>(p, d_ws, p->ws.staging);
     ea.gcnt = ws_ptr<uint32_t>(p, d_ws, p->ws.gcnt);
+    ea.flag = ws_ptr<uint32_t>(p, d_ws, p->ws.flag);
+    ea.agg = ws_ptr<uint64_t>(p, d_ws, p->ws.agg);
+    ea.chunk_elems = p->chunk;
     ea.block_elems = p->block;
     ea.forced_L = forced_L;
     ea.single = p->nseg == 1;
@@ -138,18 +147,35 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return ZC_ERR_HIP;
     WindowArgs wa{ea, p->d_witems, ws_ptr<SegStat>(p, d_ws, p->ws.stats), d_stream_bytes,
                   p->chunk, p->chunk / p->block, (p->flags & ZC_PLAN_RAW_FALLBACK) ? 1u : 0u};
+    uint8_t* out = static_cast<uint8_t*>(d_out);
+    const PlaceArgs pa{p->d_segs, p->d_chunks, out, ea.staging, ea.gcnt, ea.in, p->chunk, nchunks(p),
+                       p->nseg == 1, p->segs[0]};
+    if (p->merged_tail && !fixed) {
+        // the window check and the placement in one launch (zc_finish.hip):
+        // one window workgroup per segment, then one workgroup per chunk
+        const FinishArgs fa{wa, pa, p->nseg};
+        const dim3 grid(p->nseg + nchunks(p));
+        const uint32_t gpw = p->chunk / kGroup / 4;  // groups per wave: 2, 4 or 8
+        if (ea.single) {
+            if (gpw == 2) hipLaunchKernelGGL((zc_finish<true, 2>), grid, dim3(256), 0, stream, fa);
+            else if (gpw == 4) hipLaunchKernelGGL((zc_finish<true, 4>), grid, dim3(256), 0, stream, fa);
+            else hipLaunchKernelGGL((zc_finish<true, 8>), grid, dim3(256), 0, stream, fa);
+        } else {
+            if (gpw == 2) hipLaunchKernelGGL((zc_finish<false, 2>), grid, dim3(256), 0, stream, fa);
+            else if (gpw == 4) hipLaunchKernelGGL((zc_finish<false, 4>), grid, dim3(256), 0, stream, fa);
+            else hipLaunchKernelGGL((zc_finish<false, 8>), grid, dim3(256), 0, stream, fa);
+        }
+        if (ev && (hipEventRecord(ev[2], stream) != hipSuccess || hipEventRecord(ev[3], stream) != hipSuccess))
+            return ZC_ERR_HIP;
+        return launch_status();
+    }
     if (ea.single) hipLaunchKernelGGL(zc_window<true>, dim3((uint32_t)p->witems.size()), dim3(256), 0, stream, wa);
     else hipLaunchKernelGGL(zc_window<false>, dim3((uint32_t)p->witems.size()), dim3(256), 0, stream, wa);
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return ZC_ERR_HIP;
     // after the window kernel: codes and sm bytes (coded again there when
     // the prediction failed), header, chunk table and sizes are final
     if (fixed && hipEventRecord(fixed, stream) != hipSuccess) return ZC_ERR_HIP;
-    uint8_t* out = static_cast<uint8_t*>(d_out);
-    uint8_t* staging = ea.staging;
-    uint32_t* gcnt = ea.gcnt;
     if (nchunks(p)) {
-        PlaceArgs pa{p->d_segs, p->d_chunks, out, staging, gcnt, ea.in, p->chunk, nchunks(p),
-                     p->nseg == 1, p->segs[0]};
         const uint32_t gpc = p->chunk / kGroup;
         // placement: up to 4 waves, each with gpc / waves groups
         const uint32_t pw = gpc < 4 ? gpc : 4;

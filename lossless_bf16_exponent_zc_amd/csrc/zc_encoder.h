@@ -194,11 +194,21 @@ __device__ __forceinline__ uint32_t predicted_L(uint32_t raw) {
 // (barriers).  L = 0: the predicted window, read once the item's loads are
 // out (the first pass: its waves do not wait for the statistics before
 // loading).
+// LDS of one encoder workgroup item (the caller declares it, so kernels with
+// several roles can overlay their roles' areas).
+struct EncodeLds {
+    u32x4 area[4][257];  // per wave, 4112 bytes
+    double g1[8], g2[8];
+    uint32_t gn[8], gc[8];
+};
+
 template <bool MOMENTS>
-__device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint32_t L) {
-    __shared__ u32x4 s_area[4][257];  // per wave, 4112 bytes
-    __shared__ double s_g1[8], s_g2[8];
-    __shared__ uint32_t s_gn[8], s_gc[8];
+__device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint32_t L, EncodeLds& lds) {
+    auto& s_area = lds.area;
+    auto& s_g1 = lds.g1;
+    auto& s_g2 = lds.g2;
+    auto& s_gn = lds.gn;
+    auto& s_gc = lds.gc;
     const uint32_t lane = lane_id(), wave = wave_id();
     uint8_t* area = reinterpret_cast<uint8_t*>(s_area[wave]);
     u32x4* rowp = s_area[wave] + 2 * lane;  // the lane's exponent row

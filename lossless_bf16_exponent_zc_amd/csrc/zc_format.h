@@ -69,6 +69,8 @@ struct WsLayout {
     uint64_t done;      // u32 per segment: window workgroups done re-coding
     uint64_t zero;      // u32: zero (written by the encoder's first pass)
     uint64_t staging;   // 2048 bytes per group (+16): escape exponents before placement
+    uint64_t flag;      // u32 per segment: the finish kernel's window verdict (0 until known)
+    uint64_t agg;       // u64 per chunk: the finish kernel's look-back words
     uint64_t total;
     // the decoders use only the status words and, right after them, 2048
     // readable bytes they never write (the loads' stand-in): a decode-only

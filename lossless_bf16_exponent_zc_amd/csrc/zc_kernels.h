@@ -17,6 +17,9 @@ struct EncodeArgs {
     uint32_t* zero;         // one word the first pass sets to 0 (a target for masked loads)
     uint8_t* staging;       // 2048 bytes per group (+16): the group's escape exponents
     uint32_t* gcnt;         // per group: its escape count
+    uint32_t* flag;         // per segment: the finish kernel's verdict (first pass clears)
+    uint64_t* agg;          // per chunk: look-back words (first pass clears)
+    uint32_t chunk_elems;
     uint32_t block_elems;   // moment block (16,384 values, or the chunk if smaller)
     uint32_t forced_L;      // nonzero: this window for every segment, no moments
     uint32_t single;        // one segment: seg0 is it, items are (0, index)
@@ -62,6 +65,14 @@ struct DecodeArgs {
     SegDesc seg0;
 };
 
+// The merged tail of compress: window workgroups (one per segment) first,
+// then one placement workgroup per chunk.
+struct FinishArgs {
+    WindowArgs win;
+    PlaceArgs place;
+    uint32_t nwin;  // window workgroups (the plan's segments)
+};
+
 struct NativeReduceArgs {
     const uint16_t* in[kMaxStreams];  // uncompressed shards, 16-byte aligned
     uint16_t* out;
@@ -80,5 +91,7 @@ __global__ void zc_decode_reduce(DecodeArgs a);
 __global__ void zc_decode_reduce_wide(DecodeArgs a);
 template <int S>
 __global__ void zc_reduce_native(NativeReduceArgs a);
+template <bool SINGLE, int GPW>
+__global__ void zc_finish(FinishArgs a);
 
 }  // namespace zc

@@ -199,6 +199,64 @@ __device__ __forceinline__ void finish_round(RoundLoads& L, uint32_t B, const Re
     __syncthreads();
 }
 
+// finish_round with the round's loads in two halves of 8 leaves, each half
+// loaded and reduced before the next is requested: half the registers, one
+// more memory round trip.  The same sums: a thread's 16-leaf tree is the add
+// of the trees over its first and its last 8 leaves, and leaves past B (or
+// past m) are -0.0, the identity, as in finish_round.
+__device__ __forceinline__ void halves_round(const double* ps1, const double* ps2, const uint32_t* pn,
+                                             uint32_t B, const ReduceShape& shp, uint32_t r,
+                                             MomentScratch& sh, uint64_t& nn) {
+    const uint32_t tid = threadIdx.x, lane = lane_id(), wave = wave_id(), T = shp.T, m = shp.m;
+    constexpr uint32_t nw = kReduceThreads / 64;
+    double h1[2], h2[2];
+    uint32_t rn = 0;  // at most 16 * 16384 values per thread and round
+#pragma unroll
+    for (uint32_t h = 0; h < 2; ++h) {
+        double v1[8], v2[8];
+        uint32_t n[8];
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u) {  // loads only: nothing here waits for them
+            const uint32_t i = 8 * h + u;
+            const uint32_t slot = (r * T * m) + (i < m ? i : 0u) * T + (tid < T ? tid : 0u);  // < P
+            v1[u] = ps1[slot];
+            v2[u] = ps2[slot];
+            n[u] = pn[slot];
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u) {
+            const uint32_t i = 8 * h + u;
+            const uint32_t leaf = (r * T + tid) * m + i;
+            const bool ok = tid < T && i < m && leaf < B;
+            v1[u] = ok ? v1[u] : -0.0;  // no leaf: the identity
+            v2[u] = ok ? v2[u] : -0.0;
+            rn += ok ? n[u] : 0u;
+        }
+        h1[h] = tree8(v1);
+        h2[h] = tree8(v2);
+        __builtin_amdgcn_sched_barrier(0);  // the second half's loads after the first is reduced
+    }
+    const double r1 = wave_tree(h1[0] + h1[1]), r2 = wave_tree(h2[0] + h2[1]);
+    rn = wave_sum(rn);
+    if (lane == 0) {
+        sh.v1[wave] = r1;
+        sh.v2[wave] = r2;
+        sh.n[wave] = rn;
+    }
+    __syncthreads();
+    if (wave == 0) {  // lanes 0..15 join the waves' sums: a 16-leaf butterfly
+        double t1 = lane < nw ? sh.v1[lane] : -0.0, t2 = lane < nw ? sh.v2[lane] : -0.0;
+        t1 = row_tree(t1);
+        t2 = row_tree(t2);
+        if (lane == 0) {
+            sh.r1[r] = t1;
+            sh.r2[r] = t2;
+            for (uint32_t i = 0; i < nw; ++i) nn += sh.n[i];
+        }
+    }
+    __syncthreads();
+}
+
 // The wave joins the rounds: lane l the 8 rounds 8l .. 8l+7, then the lanes.
 __device__ __forceinline__ void join_rounds(const MomentScratch& sh, uint32_t rounds, uint64_t nn,
                                             double& s1, double& s2, uint64_t& n) {

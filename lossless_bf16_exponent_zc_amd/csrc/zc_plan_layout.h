@@ -20,7 +20,15 @@ struct PlanLayout {
     std::vector<ItemDesc> chunks, groups, pairs, witems;  // pairs: encoder waves; witems: window workgroups
     uint64_t input_elems = 0, out_bytes = 0;
     WsLayout ws{};
+    // compress ends with the merged finish kernel: chunks of whole encoder
+    // items, no segment over kFinishMaxBlocks moment blocks, no raw fallback
+    bool merged_tail = false;
 };
+
+// The merged finish kernel sums a chunk's escape offset from the moment
+// blocks before it: segments up to this many blocks (128M values) use it.
+constexpr uint32_t kFinishMaxBlocks = 8192;
+constexpr uint32_t kPlanRawFallback = 1;  // ZC_PLAN_RAW_FALLBACK
 
 // The ZC_ERR_* values of zc.h that a layout can give.
 enum LayoutStatus : int { kLayoutOk = 0, kLayoutInvalidArg = 1, kLayoutUnsupported = 3, kLayoutNoMemory = 5 };
@@ -88,6 +96,8 @@ inline int build_layout(uint32_t nseg, const uint64_t* sizes, uint32_t chunk_ele
             for (uint32_t r = 0; r < d.wr; ++r) L.witems.push_back(ItemDesc{s, r});
             L.segs.push_back(d);
         }
+        L.merged_tail = C >= kSigmaBlock && !(flags & kPlanRawFallback);
+        for (const SegDesc& d : L.segs) L.merged_tail = L.merged_tail && d.nsb <= kFinishMaxBlocks;
         L.input_elems = in_off;
         L.out_bytes = out_off;
         const uint64_t G = L.groups.size(), B = sb;
@@ -104,6 +114,8 @@ inline int build_layout(uint32_t nseg, const uint64_t* sizes, uint32_t chunk_ele
         w.done = o;     o += layout_a256(4ull * nseg);
         w.zero = o;     o += 256;
         w.staging = o;  o += layout_a256((uint64_t)kGroup * G + 16);
+        w.flag = o;     o += layout_a256(4ull * nseg);
+        w.agg = o;      o += layout_a256(8ull * L.chunks.size());
         w.total = o;
         // decoders: the status words, then a 2048-byte stand-in (inside the
         // full layout too: the staging area alone is larger); a plan without

@@ -17,148 +17,9 @@
 // C0 = 1 / (4 u^2) and u the root of Phi(256u) - Phi(128u) = Phi(2u) - Phi(u)
 // (the sigma-relative position where shifting the window by one binade
 // gains as much mass at the top as it loses at the bottom).
-#include "zc_encoder.h"
+#include "zc_window.h"
 
 namespace zc {
-
-namespace {
-
-// Chunk table, E, total size and stream size of segment sd from the moment
-// blocks' escape counts (BPC blocks per chunk), by the whole workgroup, each
-// thread a run of chunks.  chunk_counts returns the thread's run total and,
-// for runs of up to 8 chunks, the chunks' counts in registers (longer runs
-// leave them in the table entries); place_offsets scans the runs' totals
-// across the workgroup and writes the offsets.  Loads go out in batches of
-// 32, unconditionally (indexes clamped, values masked).
-struct ChunkRun {
-    uint32_t c0, c1;
-};
-
-__device__ __forceinline__ ChunkRun chunk_run(const SegDesc& sd) {
-    const uint32_t K = sd.k, per = (K + blockDim.x - 1) / blockDim.x;
-    const uint32_t c0 = min(K, threadIdx.x * per);
-    return ChunkRun{c0, min(K, c0 + per)};
-}
-
-struct ChunkCounts {
-    uint32_t c[8];
-    uint32_t run;
-    bool in_table;
-};
-
-template <uint32_t BPC>
-__device__ __forceinline__ void chunk_counts_t(const WindowArgs& a, const SegDesc& sd, uint8_t* st,
-                                               ChunkCounts& cc) {
-    constexpr uint32_t U = 32 / BPC;  // chunks per batch
-    const ChunkRun cr = chunk_run(sd);
-    const uint32_t last = sd.nsb - 1;
-    const uint32_t* pe = a.enc.part.esc + sd.sb_base;
-    cc.run = 0;
-    cc.in_table = (sd.k + blockDim.x - 1) / blockDim.x > 8;  // uniform
-    if (!cc.in_table) {
-        // entries outside the run read a word the encoder zeroed, so every
-        // load goes out unconditionally and nothing waits between them
-        uint32_t v[8][BPC];
-#pragma unroll
-        for (uint32_t u = 0; u < 8; ++u)
-#pragma unroll
-            for (uint32_t j = 0; j < BPC; ++j) {
-                const uint32_t b = (cr.c0 + u) * BPC + j;
-                v[u][j] = *(cr.c0 + u < cr.c1 && b <= last ? pe + b : a.enc.zero);
-            }
-#pragma unroll
-        for (uint32_t u = 0; u < 8; ++u) {
-            uint32_t t = 0;
-#pragma unroll
-            for (uint32_t j = 0; j < BPC; ++j) t += v[u][j];
-            cc.c[u] = t;
-            cc.run += t;
-        }
-        return;
-    }
-    uint32_t* table = reinterpret_cast<uint32_t*>(st + kHeaderBytes);
-    for (uint32_t c = cr.c0; c < cr.c1; c += U) {
-        uint32_t v[U][BPC];
-#pragma unroll
-        for (uint32_t u = 0; u < U; ++u)
-#pragma unroll
-            for (uint32_t j = 0; j < BPC; ++j) {
-                const uint32_t b = (c + u) * BPC + j;
-                v[u][j] = *(c + u < cr.c1 && b <= last ? pe + b : a.enc.zero);
-            }
-#pragma unroll
-        for (uint32_t u = 0; u < U; ++u) {
-            uint32_t t = 0;
-#pragma unroll
-            for (uint32_t j = 0; j < BPC; ++j) t += v[u][j];
-            if (c + u < cr.c1) table[c + u] = t;
-            cc.run += t;
-        }
-    }
-}
-
-__device__ __forceinline__ void chunk_counts(const WindowArgs& a, const SegDesc& sd, uint8_t* st,
-                                             ChunkCounts& cc) {
-    switch (a.chunk_blocks) {
-        case 1: chunk_counts_t<1>(a, sd, st, cc); break;
-        case 2: chunk_counts_t<2>(a, sd, st, cc); break;
-        default: chunk_counts_t<4>(a, sd, st, cc); break;
-    }
-}
-
-// Contains __syncthreads.
-__device__ __forceinline__ void place_offsets(const WindowArgs& a, const SegDesc& sd, uint32_t seg,
-                                              uint8_t* st, const ChunkCounts& cc) {
-    __shared__ uint32_t s_w[16], s_base;
-    const uint32_t lane = lane_id(), wave = wave_id(), nw = blockDim.x >> 6;
-    const ChunkRun cr = chunk_run(sd);
-    uint32_t* table = reinterpret_cast<uint32_t*>(st + kHeaderBytes);
-    const uint32_t incl = wave_inclusive_scan(cc.run);
-    if (lane == 63) s_w[wave] = incl;
-    __syncthreads();
-    if (wave == 0) {
-        const uint32_t v = lane < nw ? s_w[lane] : 0u;
-        const uint32_t wi = wave_inclusive_scan(v);
-        if (lane < nw) s_w[lane] = wi - v;
-        if (lane == 63) s_base = wi;  // E
-    }
-    __syncthreads();
-    uint32_t at = s_w[wave] + incl - cc.run;
-    if (!cc.in_table) {
-#pragma unroll
-        for (uint32_t u = 0; u < 8; ++u)
-            if (cr.c0 + u < cr.c1) {
-                table[cr.c0 + u] = at;
-                at += cc.c[u];
-            }
-    } else {
-        for (uint32_t c = cr.c0; c < cr.c1; c += 8) {
-            uint32_t t[8];
-#pragma unroll
-            for (uint32_t u = 0; u < 8; ++u) t[u] = table[min(c + u, cr.c1 - 1)];
-#pragma unroll
-            for (uint32_t u = 0; u < 8; ++u)
-                if (c + u < cr.c1) {
-                    table[c + u] = at;
-                    at += t[u];
-                }
-        }
-    }
-    if (threadIdx.x == 0) {
-        const uint64_t E = s_base;
-        table[sd.k] = (uint32_t)E;
-        if (a.raw_fallback && sd.esc_off + E > kHeaderBytes + 2ull * sd.n) {
-            write_raw_header(st, sd, a.chunk_elems);  // the placement kernel copies the values
-            a.stream_bytes[seg] = kHeaderBytes + 2ull * sd.n;
-            return;
-        }
-        *reinterpret_cast<uint64_t*>(st + 24) = E;
-        *reinterpret_cast<uint64_t*>(st + 32) = sd.esc_off + E;
-        a.stream_bytes[seg] = sd.esc_off + E;
-    }
-}
-
-}  // namespace
 
 // The window of each segment, the check of the first pass's prediction, and
 // the segment's tables.  Workgroups of 256 threads, sd.wr per segment (item
@@ -173,6 +34,8 @@ __device__ __forceinline__ void place_offsets(const WindowArgs& a, const SegDesc
 template <bool SINGLE>
 __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
     __shared__ MomentScratch s_mom;
+    __shared__ EncodeLds s_enc;
+    __shared__ OffsetsLds s_off;
     __shared__ uint32_t s_L, s_last;
     // (SINGLE, one segment: the descriptor from the arguments; a choice made
     // at run time would read it through vector loads before anything else)
@@ -247,10 +110,10 @@ __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
     const uint32_t L = s_L;
     if (sd.k == 0) return;
     if (L == pred) {  // the prediction held (always, with a fixed window)
-        if (r == 0) place_offsets(a, sd, seg, st, cc);
+        if (r == 0) place_offsets(a, sd, seg, st, cc, s_off);
         return;
     }
-    for (uint32_t i = r; i < sd.nwg; i += sd.wr) encode_wg<false>(a.enc, sd.wg_base + i, L);
+    for (uint32_t i = r; i < sd.nwg; i += sd.wr) encode_wg<false>(a.enc, sd.wg_base + i, L, s_enc);
     __threadfence();  // this workgroup's codes, counts and staging, before its report
     __syncthreads();
     if (threadIdx.x == 0) s_last = atomicAdd(a.enc.done + seg, 1u) == sd.wr - 1 ? 1u : 0u;
@@ -259,7 +122,7 @@ __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
         __threadfence();  // the others' reports, before their counts are read
         ChunkCounts c2;
         chunk_counts(a, sd, st, c2);
-        place_offsets(a, sd, seg, st, c2);
+        place_offsets(a, sd, seg, st, c2, s_off);
     }
 }
 

@@ -103,16 +103,21 @@ static void check_layout(const std::vector<uint64_t>& n, uint32_t chunk_arg) {
         wgs += d.wr;
     }
     CHECK(L.chunks.size() == K && L.pairs.size() == 4 * items && L.witems.size() == wgs);
+    // the merged finish kernel: whole encoder items per chunk, segments of at
+    // most kFinishMaxBlocks moment blocks
+    bool merged = C >= 16384;
+    for (const SegDesc& d : L.segs) merged = merged && d.nsb <= kFinishMaxBlocks;
+    CHECK(L.merged_tail == merged);
     CHECK(L.input_elems >= in_end && L.input_elems % 8 == 0 && L.out_bytes >= out_end);
     // workspace regions: aligned, in order, each as large as the kernels index
     const WsLayout& w = L.ws;
     const uint64_t S = n.size();
     const uint64_t start[] = {w.status, w.ps1, w.ps2, w.pn, w.pesc, w.stats, w.gcnt,
-                              w.pred, w.done, w.zero, w.staging, w.total};
+                              w.pred, w.done, w.zero, w.staging, w.flag, w.agg, w.total};
     const uint64_t need[] = {4 * G, 8 * slots, 8 * slots, 4 * slots, 4 * slots,
                              sizeof(SegStat) * S, 4 * G, 4 * S, 4 * S, 4,
-                             (uint64_t)kGroup * G + 16};
-    for (int i = 0; i < 11; ++i) {
+                             (uint64_t)kGroup * G + 16, 4 * S, 8 * K};
+    for (int i = 0; i < 13; ++i) {
         CHECK(start[i] % 256 == 0);
         CHECK(start[i] + need[i] <= start[i + 1]);
     }
