@@ -5,10 +5,10 @@
 //                      codes, sign+mantissa bytes, staged escape exponents
 //                      and escape counts, with each segment's previous window
 //                      as the prediction (or the caller's fixed window)
-//   zc_finish          the two kernels below in one launch, overlapped (chunks
-//                      of 16,384 values or more, no raw fallback, no split
-//                      event); a failed prediction is coded again chunk by
-//                      chunk there
+//   zc_finish          the two kernels below in one launch, overlapped
+//                      (segments up to 8192 moment blocks, no raw fallback,
+//                      no split event); a failed prediction is coded again
+//                      chunk by chunk there
 //   zc_window          per segment: variance -> window, statistics, header
 //                      fields known before encoding; where the prediction
 //                      failed, the segment's codes again; chunk table, sizes;
@@ -43,6 +43,7 @@ struct zc_plan : zc::PlanLayout {  // the host layout plus its device tables
     ItemDesc* d_groups = nullptr;
     ItemDesc* d_pairs = nullptr;
     ItemDesc* d_witems = nullptr;
+    ItemDesc* d_fitems = nullptr;
 };
 
 namespace {
@@ -134,6 +135,7 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     ea.gcnt = ws_ptr<uint32_t>(p, d_ws, p->ws.gcnt);
     ea.flag = ws_ptr<uint32_t>(p, d_ws, p->ws.flag);
     ea.agg = ws_ptr<uint64_t>(p, d_ws, p->ws.agg);
+    ea.fpart = ws_ptr<uint64_t>(p, d_ws, p->ws.fpart);
     ea.chunk_elems = p->chunk;
     ea.block_elems = p->block;
     ea.forced_L = forced_L;
@@ -153,17 +155,25 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     if (p->merged_tail && !fixed) {
         // the window check and the placement in one launch (zc_finish.hip):
         // one window workgroup per segment, then one workgroup per chunk
-        const FinishArgs fa{wa, pa, p->nseg};
-        const dim3 grid(p->nseg + nchunks(p));
-        const uint32_t gpw = p->chunk / kGroup / 4;  // groups per wave: 2, 4 or 8
+        const uint32_t nwin = (uint32_t)p->fitems.size();
+        const FinishArgs fa{wa, pa, p->d_fitems, nwin};
+        const dim3 grid(nwin + nchunks(p));
+        // groups per wave of the 4-wave placement workgroups (a chunk holds
+        // 1 to 32 groups, a power of two): 1, 2, 4 or 8; waves past the
+        // chunk's last group idle
+        const uint32_t gpc = p->chunk / kGroup;
+        const uint32_t gpw = gpc > 4 ? gpc / 4 : 1;
+        auto launch = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, fa); };
         if (ea.single) {
-            if (gpw == 2) hipLaunchKernelGGL((zc_finish<true, 2>), grid, dim3(256), 0, stream, fa);
-            else if (gpw == 4) hipLaunchKernelGGL((zc_finish<true, 4>), grid, dim3(256), 0, stream, fa);
-            else hipLaunchKernelGGL((zc_finish<true, 8>), grid, dim3(256), 0, stream, fa);
+            if (gpw == 1) launch(zc_finish<true, 1>);
+            else if (gpw == 2) launch(zc_finish<true, 2>);
+            else if (gpw == 4) launch(zc_finish<true, 4>);
+            else launch(zc_finish<true, 8>);
         } else {
-            if (gpw == 2) hipLaunchKernelGGL((zc_finish<false, 2>), grid, dim3(256), 0, stream, fa);
-            else if (gpw == 4) hipLaunchKernelGGL((zc_finish<false, 4>), grid, dim3(256), 0, stream, fa);
-            else hipLaunchKernelGGL((zc_finish<false, 8>), grid, dim3(256), 0, stream, fa);
+            if (gpw == 1) launch(zc_finish<false, 1>);
+            else if (gpw == 2) launch(zc_finish<false, 2>);
+            else if (gpw == 4) launch(zc_finish<false, 4>);
+            else launch(zc_finish<false, 8>);
         }
         if (ev && (hipEventRecord(ev[2], stream) != hipSuccess || hipEventRecord(ev[3], stream) != hipSuccess))
             return ZC_ERR_HIP;
@@ -232,6 +242,9 @@ zc_status zc_plan_create_ex(uint32_t num_segments, const uint64_t* segment_elems
         hipMalloc(&p->d_groups, sizeof(ItemDesc) * (G ? G : 1)) != hipSuccess ||
         hipMalloc(&p->d_pairs, sizeof(ItemDesc) * (W ? W : 1)) != hipSuccess ||
         hipMalloc(&p->d_witems, sizeof(ItemDesc) * p->witems.size()) != hipSuccess ||
+        hipMalloc(&p->d_fitems, sizeof(ItemDesc) * p->fitems.size()) != hipSuccess ||
+        hipMemcpy(p->d_fitems, p->fitems.data(), sizeof(ItemDesc) * p->fitems.size(),
+                  hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(p->d_segs, p->segs.data(), sizeof(SegDesc) * p->segs.size(),
                   hipMemcpyHostToDevice) != hipSuccess ||
         (K && hipMemcpy(p->d_chunks, p->chunks.data(), sizeof(ItemDesc) * K,
@@ -259,6 +272,7 @@ void zc_plan_destroy(zc_plan* p) {
     if (p->d_groups) (void)hipFree(p->d_groups);
     if (p->d_pairs) (void)hipFree(p->d_pairs);
     if (p->d_witems) (void)hipFree(p->d_witems);
+    if (p->d_fitems) (void)hipFree(p->d_fitems);
     delete p;
 }
 

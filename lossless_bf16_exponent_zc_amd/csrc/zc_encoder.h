@@ -202,7 +202,10 @@ struct EncodeLds {
     uint32_t gn[8], gc[8];
 };
 
-template <bool MOMENTS>
+// AGAIN: a second coding of the item with another window (a failed
+// prediction): the sign+mantissa bytes do not depend on the window and are
+// already in place, so they are not written again.
+template <bool MOMENTS, bool AGAIN = false>
 __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint32_t L, EncodeLds& lds) {
     auto& s_area = lds.area;
     auto& s_g1 = lds.g1;
@@ -262,8 +265,10 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
 #pragma unroll
             for (int b = 0; b < 3; ++b) *reinterpret_cast<uint32_t*>(cw + 256 * b) = P[b];
             uint8_t* sw = st + sd.sm_off + 2048ull * g + 8u * lane;
+            if (!AGAIN) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x2*>(sw + 512 * k) = sm[k];
+                for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x2*>(sw + 512 * k) = sm[k];
+            }
             const uint32_t M = P[0] & P[1] & P[2];
             uint32_t tot;
             const uint32_t excl = wave_prefix_small(__builtin_popcount(M), tot);
@@ -332,6 +337,67 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
         }
     }
     lds_barrier();  // s_g* are rewritten by the next workgroup item
+}
+
+// One group coded again with window L7 (packed as the encoder packs it):
+// its code planes, escape count and staged escape exponents, as encode_wg
+// writes them (the sign+mantissa bytes are the first pass's: they do not
+// depend on the window).  rowp: the lane's 32-byte LDS row; ew: the wave's
+// packed escape area (2048 + 16 bytes).
+__device__ __forceinline__ void recode_group(const EncodeArgs& a, const SegDesc& sd, uint8_t* st, uint64_t g,
+                                             const u32x4 (&w)[4], uint32_t L7, u32x4* rowp, uint8_t* ew,
+                                             uint32_t lane) {
+    uint32_t P[3], mx;
+    u32x2 sm[4];
+    encode_group(w, L7, P, sm, mx);
+    if ((uint64_t)kGroup * (g + 1) > sd.n) {  // last, partial group: padding codes are 0
+        const uint32_t V = valid_bits(lane, (uint32_t)(sd.n - (uint64_t)kGroup * g));
+#pragma unroll
+        for (int b = 0; b < 3; ++b) P[b] &= V;
+    }
+    uint8_t* cw = st + sd.code_off + 768ull * g + 4u * lane;
+#pragma unroll
+    for (int b = 0; b < 3; ++b) *reinterpret_cast<uint32_t*>(cw + 256 * b) = P[b];
+    const uint32_t M = P[0] & P[1] & P[2];
+    uint32_t tot;
+    const uint32_t excl = wave_prefix_small(__builtin_popcount(M), tot);
+    const uint64_t gg = sd.group_base + g;
+    if (lane == 0) a.gcnt[gg] = tot;
+    uint32_t Q[8];
+    exponent_bytes(w, Q);
+    rowp[0] = u32x4{Q[0], Q[1], Q[2], Q[3]};
+    rowp[1] = u32x4{Q[4], Q[5], Q[6], Q[7]};
+    const uint8_t* rb = reinterpret_cast<const uint8_t*>(rowp);
+    for (uint32_t m = M, i = 0; m; m &= m - 1, ++i) ew[excl + i] = rb[__builtin_ctz(m)];
+    __builtin_amdgcn_wave_barrier();  // the wave's packed bytes are complete
+    const uint32_t* ew32 = reinterpret_cast<const uint32_t*>(ew);
+    uint32_t* slot = reinterpret_cast<uint32_t*>(a.staging + gg * kGroup);
+    for (uint32_t k = lane; k < (tot + 3) / 4; k += 64) slot[k] = ew32[k];
+    __builtin_amdgcn_wave_barrier();  // before the area is reused
+}
+
+// A chunk's ng groups (from segment group gc0) coded again with window L
+// after a failed prediction: code planes, escape counts and staged escape
+// exponents (no moments: the window is known; no per-block counts: nothing
+// reads them after a miss).  Wave w codes groups w, w + 4, ...; the next
+// group's words are requested before the current one is coded.  Every
+// thread of the 256-thread workgroup calls this.
+__device__ __forceinline__ void recode_chunk(const EncodeArgs& a, const SegDesc& sd, uint64_t gc0, uint32_t ng,
+                                             uint32_t L, EncodeLds& lds) {
+    const uint32_t lane = lane_id(), wave = wave_id();
+    u32x4* rowp = lds.area[wave] + 2 * lane;
+    uint8_t* ew = reinterpret_cast<uint8_t*>(lds.area[wave]) + 2048;
+    const uint16_t* in = a.in + sd.in_off;
+    uint8_t* st = a.out + sd.out_off;
+    const uint32_t L7 = (L << 7) | (L << 23);
+    u32x4 wa[4], wb[4];
+    if (wave < ng) load_group(in, sd.n, gc0 + wave, lane, wa);
+    for (uint32_t j = wave; j < ng; j += 8) {  // (uniform)
+        if (j + 4 < ng) load_group(in, sd.n, gc0 + j + 4, lane, wb);
+        recode_group(a, sd, st, gc0 + j, wa, L7, rowp, ew, lane);
+        if (j + 8 < ng) load_group(in, sd.n, gc0 + j + 8, lane, wa);
+        if (j + 4 < ng) recode_group(a, sd, st, gc0 + j + 4, wb, L7, rowp, ew, lane);
+    }
 }
 
 }  // namespace zc

@@ -18,16 +18,14 @@ struct PlanLayout {
     uint32_t nseg = 0, chunk = 0, block = 0, flags = 0;
     std::vector<SegDesc> segs;
     std::vector<ItemDesc> chunks, groups, pairs, witems;  // pairs: encoder waves; witems: window workgroups
+    std::vector<ItemDesc> fitems;  // the finish kernel's window workgroups: (segment, part)
     uint64_t input_elems = 0, out_bytes = 0;
     WsLayout ws{};
-    // compress ends with the merged finish kernel: chunks of whole encoder
-    // items, no segment over kFinishMaxBlocks moment blocks, no raw fallback
+    // compress ends with the merged finish kernel: no segment over
+    // kFinishMaxBlocks moment blocks, no raw fallback
     bool merged_tail = false;
 };
 
-// The merged finish kernel sums a chunk's escape offset from the moment
-// blocks before it: segments up to this many blocks (128M values) use it.
-constexpr uint32_t kFinishMaxBlocks = 8192;
 constexpr uint32_t kPlanRawFallback = 1;  // ZC_PLAN_RAW_FALLBACK
 
 // The ZC_ERR_* values of zc.h that a layout can give.
@@ -94,9 +92,13 @@ inline int build_layout(uint32_t nseg, const uint64_t* sizes, uint32_t chunk_ele
             // items each, at most 256 (each joins all of the segment's partials)
             d.wr = (uint32_t)std::min<uint64_t>(256, std::max<uint64_t>(1, layout_cdiv(d.nwg, 16)));
             for (uint32_t r = 0; r < d.wr; ++r) L.witems.push_back(ItemDesc{s, r});
+            // the finish kernel joins a segment's moment blocks in parts of
+            // kFinishPartBlocks (at least one part)
+            const uint32_t parts = d.nsb > kFinishPartBlocks ? (d.nsb + kFinishPartBlocks - 1) / kFinishPartBlocks : 1u;
+            for (uint32_t q = 0; q < parts && q < kFinishMaxParts; ++q) L.fitems.push_back(ItemDesc{s, q});
             L.segs.push_back(d);
         }
-        L.merged_tail = C >= kSigmaBlock && !(flags & kPlanRawFallback);
+        L.merged_tail = !(flags & kPlanRawFallback);
         for (const SegDesc& d : L.segs) L.merged_tail = L.merged_tail && d.nsb <= kFinishMaxBlocks;
         L.input_elems = in_off;
         L.out_bytes = out_off;
@@ -116,6 +118,7 @@ inline int build_layout(uint32_t nseg, const uint64_t* sizes, uint32_t chunk_ele
         w.staging = o;  o += layout_a256((uint64_t)kGroup * G + 16);
         w.flag = o;     o += layout_a256(4ull * nseg);
         w.agg = o;      o += layout_a256(8ull * L.chunks.size());
+        w.fpart = o;    o += layout_a256(32ull * kFinishMaxParts * nseg);
         w.total = o;
         // decoders: the status words, then a 2048-byte stand-in (inside the
         // full layout too: the staging area alone is larger); a plan without

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void zc_window(WindowArgs a) {
         if (r == 0) place_offsets(a, sd, seg, st, cc, s_off);
         return;
     }
-    for (uint32_t i = r; i < sd.nwg; i += sd.wr) encode_wg<false>(a.enc, sd.wg_base + i, L, s_enc);
+    for (uint32_t i = r; i < sd.nwg; i += sd.wr) encode_wg<false, true>(a.enc, sd.wg_base + i, L, s_enc);
     __threadfence();  // this workgroup's codes, counts and staging, before its report
     __syncthreads();
     if (threadIdx.x == 0) s_last = atomicAdd(a.enc.done + seg, 1u) == sd.wr - 1 ? 1u : 0u;

@@ -1,6 +1,7 @@
 import os
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -13,6 +14,37 @@ def pytest_configure(config):
         "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line(
         "markers", "slow: large CPU-side work (full-size oracle runs)")
+
+
+def first_difference(a, b):
+    """None when two byte strings (or equal-length lists of them) are equal,
+    else a short account of where they first differ.  A failed `==` on long
+    byte strings makes pytest run difflib over their reprs, which at stream
+    sizes takes minutes; the tests compare through this instead."""
+    if isinstance(a, (list, tuple)) and isinstance(b, (list, tuple)):
+        if len(a) != len(b):
+            return f"{len(a)} items vs {len(b)}"
+        for i, (x, y) in enumerate(zip(a, b)):
+            d = first_difference(x, y)
+            if d is not None:
+                return f"item {i}: {d}"
+        return None
+    a, b = bytes(a), bytes(b)
+    if a == b:
+        return None
+    m = min(len(a), len(b))
+    idx = np.flatnonzero(np.frombuffer(a, np.uint8, m) != np.frombuffer(b, np.uint8, m))
+    if idx.size == 0:
+        return f"lengths {len(a)} vs {len(b)}, equal over the first {m} bytes"
+    i = int(idx[0])
+    return (f"lengths {len(a)} vs {len(b)}, {idx.size} differing bytes, first at {i}: "
+            f"{a[i:i + 8].hex()} vs {b[i:i + 8].hex()}")
+
+
+def assert_same_bytes(got, want, what=""):
+    d = first_difference(got, want)
+    if d is not None:
+        raise AssertionError(f"{what}: {d}" if what else d)
 
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -76,4 +108,4 @@ def check_escape_order_stream(s, g):
     x = escape_order_input(g)
     sm = np.where((x >> 15) == 1, 0x80, 0).astype(np.uint8)
     assert np.array_equal(np.frombuffer(s[sm_off:esc_off], dtype=np.uint8), sm)
-    assert s[esc_off:] == bytes(int(t, 16) for t in g["escapes"].split())
+    assert_same_bytes(s[esc_off:], bytes(int(t, 16) for t in g["escapes"].split()), "escapes")

@@ -103,21 +103,32 @@ static void check_layout(const std::vector<uint64_t>& n, uint32_t chunk_arg) {
         wgs += d.wr;
     }
     CHECK(L.chunks.size() == K && L.pairs.size() == 4 * items && L.witems.size() == wgs);
-    // the merged finish kernel: whole encoder items per chunk, segments of at
-    // most kFinishMaxBlocks moment blocks
-    bool merged = C >= 16384;
+    // the merged finish kernel: segments of at most kFinishMaxBlocks moment
+    // blocks (the fuzz plans have no raw fallback)
+    bool merged = true;
     for (const SegDesc& d : L.segs) merged = merged && d.nsb <= kFinishMaxBlocks;
     CHECK(L.merged_tail == merged);
+    // the finish kernel's window parts: each segment's blocks in parts of
+    // kFinishPartBlocks, in segment order
+    size_t fi = 0;
+    for (size_t s = 0; s < n.size(); ++s) {
+        const uint32_t nsb = L.segs[s].nsb;
+        const uint64_t parts = nsb > kFinishPartBlocks ? cdiv(nsb, kFinishPartBlocks) : 1;
+        for (uint64_t q = 0; q < std::min<uint64_t>(parts, kFinishMaxParts); ++q, ++fi)
+            CHECK(fi < L.fitems.size() && L.fitems[fi].seg == s && L.fitems[fi].local == q);
+        if (merged) CHECK(parts <= kFinishMaxParts);
+    }
+    CHECK(fi == L.fitems.size());
     CHECK(L.input_elems >= in_end && L.input_elems % 8 == 0 && L.out_bytes >= out_end);
     // workspace regions: aligned, in order, each as large as the kernels index
     const WsLayout& w = L.ws;
     const uint64_t S = n.size();
     const uint64_t start[] = {w.status, w.ps1, w.ps2, w.pn, w.pesc, w.stats, w.gcnt,
-                              w.pred, w.done, w.zero, w.staging, w.flag, w.agg, w.total};
+                              w.pred, w.done, w.zero, w.staging, w.flag, w.agg, w.fpart, w.total};
     const uint64_t need[] = {4 * G, 8 * slots, 8 * slots, 4 * slots, 4 * slots,
                              sizeof(SegStat) * S, 4 * G, 4 * S, 4 * S, 4,
-                             (uint64_t)kGroup * G + 16, 4 * S, 8 * K};
-    for (int i = 0; i < 13; ++i) {
+                             (uint64_t)kGroup * G + 16, 4 * S, 8 * K, 32ull * kFinishMaxParts * S};
+    for (int i = 0; i < 14; ++i) {
         CHECK(start[i] % 256 == 0);
         CHECK(start[i] + need[i] <= start[i + 1]);
     }

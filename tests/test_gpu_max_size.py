@@ -32,6 +32,7 @@ import oracle
 from lossless_bf16_exponent_zc_amd import Plan
 from lossless_bf16_exponent_zc_amd import workloads as W
 
+from conftest import assert_same_bytes
 from gpu_util import say, stat_bits
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -108,7 +109,7 @@ def test_largest_segment():
         )
         for a, b, n, what in pairs:
             mine = out[a:a + n].cpu().numpy().tobytes()
-            assert mine == sub[b:b + n], f"chunk {k}: {what} differ"
+            assert_same_bytes(mine, sub[b:b + n], f"chunk {k}: {what}")
         assert int(table[k + 1] - table[k]) == sh["E"]
     say("  sampled chunks identical to the oracle's")
     del host

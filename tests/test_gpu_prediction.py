@@ -11,6 +11,7 @@ import oracle
 from lossless_bf16_exponent_zc_amd import Plan
 from lossless_bf16_exponent_zc_amd import workloads as W
 
+from conftest import assert_same_bytes
 from gpu_util import gpu_compress, gpu_decompress, say, stat_bits
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +31,7 @@ def check(segs, plan, ws, chunk=65536, window=None):
     streams, _, out, _ = gpu_compress(segs, chunk, window, plan=plan, ws=ws)
     for s, (seg, st) in enumerate(zip(segs, streams)):
         ref = oracle.compress(seg, C=chunk, L=window)
-        assert st == ref, f"segment {s}: stream differs (len {len(st)} vs {len(ref)})"
+        assert_same_bytes(st, ref, f"segment {s}")
         if window is None:
             assert stat_bits(plan.read_sigma(ws, s)) == stat_bits(oracle.sigma(seg)), s
     bits, dec = gpu_decompress(plan, out)
@@ -130,7 +131,7 @@ def test_split_event_fixed_regions_final():
         for s, seg in enumerate(segs):
             so = plan.stream_offset(s)
             ref = oracle.compress(seg)
-            assert out[so:so + int(sizes[s])].cpu().numpy().tobytes() == ref, (call, s)
+            assert_same_bytes(out[so:so + int(sizes[s])].cpu().numpy().tobytes(), ref, f"call {call}, segment {s}")
             h, f = early[s]
             assert torch.equal(h, out[so:so + h.numel()]), (call, s, "header/table")
             assert torch.equal(f, out[so + plan.code_offset(s):so + plan.escape_offset(s)]), (call, s)

@@ -10,6 +10,7 @@ import torch
 import oracle
 from lossless_bf16_exponent_zc_amd import Plan, ZcError, lib, workloads as W
 
+from conftest import assert_same_bytes
 from gpu_util import pack_inputs, say
 
 pytestmark = pytest.mark.gpu
@@ -31,7 +32,7 @@ def _both(segs, chunk):
     for s, seg in enumerate(segs):
         a = plan.stream_offset(s)
         got = o[a:a + int(sizes[s])].tobytes()
-        assert got == r[a:a + int(sizes[s])].tobytes(), s
+        assert_same_bytes(got, r[a:a + int(sizes[s])].tobytes(), f"segment {s}")
         assert got == oracle.compress(seg, C=chunk), s
     return plan
 
