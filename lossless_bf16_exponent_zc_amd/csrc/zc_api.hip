@@ -400,9 +400,20 @@ zc_status zc_decompress_reduce(const zc_plan* p, const void* const* d_streams, u
     a.out = static_cast<uint16_t*>(d_out);
     a.status = ws_ptr<uint32_t>(p, d_ws, p->ws.status);
     a.dummy = ws_ptr<uint8_t>(p, d_ws, p->ws.dummy);  // 2048 readable bytes
-    if (nstreams <= 8)  // one wave per shard, one workgroup per group
-        hipLaunchKernelGGL(zc_decode_reduce_wide, dim3(ngroups(p)), dim3(64 * nstreams), 0, stream, a);
-    else
+    if (nstreams <= 8) {  // one wave per shard, one workgroup per group
+        void (*k)(DecodeArgs) = nullptr;
+        switch (nstreams) {
+            case 1: k = zc_decode_reduce_wide<1>; break;
+            case 2: k = zc_decode_reduce_wide<2>; break;
+            case 3: k = zc_decode_reduce_wide<3>; break;
+            case 4: k = zc_decode_reduce_wide<4>; break;
+            case 5: k = zc_decode_reduce_wide<5>; break;
+            case 6: k = zc_decode_reduce_wide<6>; break;
+            case 7: k = zc_decode_reduce_wide<7>; break;
+            default: k = zc_decode_reduce_wide<8>; break;
+        }
+        hipLaunchKernelGGL(k, dim3(ngroups(p)), dim3(64 * nstreams), 0, stream, a);
+    } else
         hipLaunchKernelGGL(zc_decode_reduce, dim3(group_grid(p)), dim3(256), 0, stream, a);
     return launch_status();
 }

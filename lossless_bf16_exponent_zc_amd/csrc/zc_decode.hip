@@ -487,14 +487,25 @@ __device__ __forceinline__ void decode_kernel(const DecodeArgs& a) {
 
 // One stream's group for the one-wave-per-shard reduce: decode into o (the
 // lane's four words: tile k at word 64k + lane), returns the rejection bits.
+// Decode one stream's group g into the wave's LDS area `vals` (word
+// 64 k + lane: the lane's tile-k word); the area's first 4128 bytes hold
+// the rows and escape bytes meanwhile (the wave reads them all before it
+// writes a value: LDS operations of a wave run in order).  Returns the
+// rejection bits (nothing written when non-zero).  The values are stored
+// here, not returned, so no register copy of them outlives a branch.
 template <bool TAIL>
 __device__ __forceinline__ uint32_t decode_one(const uint8_t* st, uint64_t cap, const SegDesc& sd,
                                                uint32_t C, uint32_t g, uint32_t lane, const uint8_t* dummy,
-                                               uint32_t* esc_lds, u32x4* row, u32x4 (&o)[4]) {
+                                               u32x4* vals) {
+    uint32_t* esc_lds = reinterpret_cast<uint32_t*>(vals + 128);
+    u32x4* row = vals + 2 * lane;
     GroupData d;
     fetch<true, true>(st, cap, sd, C, g, lane, dummy, d);
     if (d.bad == kRawStream) {  // uniform
+        u32x4 o[4];
         raw_words<TAIL>(st, sd.n, g, lane, o);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vals[64 * k + lane] = o[k];
         return 0;
     }
     uint32_t first = 0;
@@ -514,8 +525,19 @@ __device__ __forceinline__ uint32_t decode_one(const uint8_t* st, uint64_t cap, 
     const uint32_t cnt = __builtin_popcount(M);
     const uint32_t incl = wave_inclusive_scan(cnt);
     if (readlane(incl, 63) != d.span) bad |= kBadCount;
-    if (!bad) rebuild<false>(d, M, first + incl - cnt, reinterpret_cast<const uint8_t*>(esc_lds), row, o);
+    if (!bad) {
+        u32x4 o[4];
+        rebuild<false>(d, M, first + incl - cnt, reinterpret_cast<const uint8_t*>(esc_lds), row, o);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vals[64 * k + lane] = o[k];
+    }
     return bad;
+}
+
+// OR of the 8 bytes of w.
+__device__ __forceinline__ uint32_t or_bytes(uint64_t w) {
+    const uint32_t x = (uint32_t)w | (uint32_t)(w >> 32);
+    return (x | (x >> 8) | (x >> 16) | (x >> 24)) & 0xFFu;
 }
 
 // Output half-word i (values 512 (i / 128) + 8 ((i / 2) % 64) + 4 (i % 2)
@@ -538,30 +560,26 @@ __device__ __forceinline__ void store_half_word(uint16_t* __restrict__ out, uint
 // and escape bytes), then the workgroup sums the shards' values word by
 // word in shard order, in fp32, and rounds to BF16.  Every shard's loads are
 // in flight at once; a group costs two memory round trips.
-template <bool TAIL>
+template <int S, bool TAIL>
 __device__ __forceinline__ void reduce_group_wide(const DecodeArgs& a, const SegDesc& sd, uint32_t g,
-                                                  uint32_t gg, u32x4 (*s_area)[258], uint32_t* s_bad) {
-    const uint32_t lane = lane_id(), wave = wave_id(), S = a.nstreams;
-    u32x4* area = s_area[wave];
-    u32x4 o[4];
+                                                  uint32_t gg, u32x4 (*s_area)[258], uint8_t* s_bad) {
+    const uint32_t lane = lane_id(), wave = wave_id();
     const uint32_t bad = decode_one<TAIL>(a.in[wave], a.capacity, sd, a.chunk_elems, g, lane, a.dummy,
-                                          reinterpret_cast<uint32_t*>(area + 128), area + 2 * lane, o);
-    if (!bad) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) area[64 * k + lane] = o[k];
-    }
-    if (lane == 0) s_bad[wave] = bad;
+                                          s_area[wave]);
+    // one byte per wave (rejection bits fit in 7), read back as one word;
+    // the bytes of waves past S are masked off
+    if (lane == 0) s_bad[wave] = (uint8_t)bad;
     __syncthreads();
-    uint32_t bad_all = 0;
-    for (uint32_t s = 0; s < S; ++s) bad_all |= s_bad[s];
+    const uint64_t bytes = *reinterpret_cast<const uint64_t*>(s_bad);
+    const uint32_t bad_all = or_bytes(S == 8 ? bytes : bytes & ((1ull << (8 * (S & 7))) - 1));
     if (bad_all == 0) {
         // every thread takes 4 values (half an area word), so all S waves
         // share the sum
-        for (uint32_t i = threadIdx.x; i < 512; i += blockDim.x) {
+#pragma unroll
+        for (uint32_t i = threadIdx.x; i < 512; i += 64 * S) {
             float acc[4];
 #pragma unroll
-            for (uint32_t s = 0; s < 8; ++s) {
-                if (s >= S) break;  // uniform
+            for (int s = 0; s < S; ++s) {
                 const u32x2 v = reinterpret_cast<const u32x2*>(s_area[s])[i];
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
@@ -579,17 +597,27 @@ __device__ __forceinline__ void reduce_group_wide(const DecodeArgs& a, const Seg
     if (threadIdx.x == 0) a.status[gg] = bad_all;
 }
 
+template <int S>
 __global__ __launch_bounds__(512) void zc_decode_reduce_wide(DecodeArgs a) {
     __shared__ u32x4 s_area[8][258];  // per wave: rows (2048 B) + escapes (2080 B); then values
-    __shared__ uint32_t s_bad[8];
+    __shared__ __align__(8) uint8_t s_bad[8];
     const uint32_t gg = blockIdx.x;
     const SegDesc& sd = a.seg0;  // a reduce plan has one segment
     const uint32_t g = gg;
     if ((uint64_t)kGroup * (g + 1) > sd.n)
-        reduce_group_wide<true>(a, sd, g, gg, s_area, s_bad);
+        reduce_group_wide<S, true>(a, sd, g, gg, s_area, s_bad);
     else
-        reduce_group_wide<false>(a, sd, g, gg, s_area, s_bad);
+        reduce_group_wide<S, false>(a, sd, g, gg, s_area, s_bad);
 }
+
+template __global__ void zc_decode_reduce_wide<1>(DecodeArgs);
+template __global__ void zc_decode_reduce_wide<2>(DecodeArgs);
+template __global__ void zc_decode_reduce_wide<3>(DecodeArgs);
+template __global__ void zc_decode_reduce_wide<4>(DecodeArgs);
+template __global__ void zc_decode_reduce_wide<5>(DecodeArgs);
+template __global__ void zc_decode_reduce_wide<6>(DecodeArgs);
+template __global__ void zc_decode_reduce_wide<7>(DecodeArgs);
+template __global__ void zc_decode_reduce_wide<8>(DecodeArgs);
 
 // The native (uncompressed) reduce-scatter receive: S BF16 shards summed in
 // fp32 in shard order and rounded as the fused reduce rounds, so the two

@@ -91,6 +91,7 @@ __global__ void zc_place_escapes(PlaceArgs a);
 template <bool SINGLE>
 __global__ void zc_decode(DecodeArgs a);
 __global__ void zc_decode_reduce(DecodeArgs a);
+template <int S>
 __global__ void zc_decode_reduce_wide(DecodeArgs a);
 template <int S>
 __global__ void zc_reduce_native(NativeReduceArgs a);
