@@ -256,7 +256,11 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
             encode_group(w[q], L7, P, sm, mx);
             // an Inf or NaN anywhere in the group (a half of mx at 0x7F80)
             const bool special = MOMENTS && __ballot(((mx + 0x00800080u) & 0x80008000u) != 0) != 0;
-            clear_padding_codes(P, lane, sd.n, g);
+            if ((uint64_t)kGroup * (g + 1) > sd.n) {  // last, partial group: padding codes are 0
+                const uint32_t V = valid_bits(lane, (uint32_t)(sd.n - (uint64_t)kGroup * g));
+#pragma unroll
+                for (int b = 0; b < 3; ++b) P[b] &= V;
+            }
             uint8_t* cw = st + sd.code_off + 768ull * g + 4u * lane;
 #pragma unroll
             for (int b = 0; b < 3; ++b) *reinterpret_cast<uint32_t*>(cw + 256 * b) = P[b];
@@ -346,7 +350,11 @@ __device__ __forceinline__ void recode_group(const EncodeArgs& a, const SegDesc&
     uint32_t P[3], mx;
     u32x2 sm[4];
     encode_group(w, L7, P, sm, mx);
-    clear_padding_codes(P, lane, sd.n, g);
+    if ((uint64_t)kGroup * (g + 1) > sd.n) {  // last, partial group: padding codes are 0
+        const uint32_t V = valid_bits(lane, (uint32_t)(sd.n - (uint64_t)kGroup * g));
+#pragma unroll
+        for (int b = 0; b < 3; ++b) P[b] &= V;
+    }
     uint8_t* cw = st + sd.code_off + 768ull * g + 4u * lane;
 #pragma unroll
     for (int b = 0; b < 3; ++b) *reinterpret_cast<uint32_t*>(cw + 256 * b) = P[b];

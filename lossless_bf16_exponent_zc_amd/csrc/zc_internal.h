@@ -156,21 +156,6 @@ __device__ __forceinline__ uint32_t valid_bits(uint32_t lane, uint32_t valid) {
     return v;
 }
 
-// Clear the codes of the padding values (zeros past the segment's end,
-// which would code as escapes) when g is the segment's last, partial group.
-// The value count passes through an empty volatile asm inside the branch,
-// so the mask cannot be computed ahead of it: if-converted or hoisted,
-// every group would compute the mask.
-__device__ __forceinline__ void clear_padding_codes(uint32_t (&P)[3], uint32_t lane, uint64_t n, uint64_t g) {
-    if ((uint64_t)kGroup * (g + 1) > n) {
-        uint32_t valid = (uint32_t)(n - (uint64_t)kGroup * g);
-        asm volatile("" : "+v"(valid));
-        const uint32_t V = valid_bits(lane, valid);
-#pragma unroll
-        for (int b = 0; b < 3; ++b) P[b] &= V;
-    }
-}
-
 // Load the lane's 8 values of each tile of group g (zero past n).
 __device__ __forceinline__ void load_group(const uint16_t* __restrict__ x, uint64_t n,
                                            uint64_t g, uint32_t lane, u32x4 (&w)[4]) {
