@@ -32,8 +32,10 @@ HBM_PEAK = 8.0e12  # bytes/s, MI355X
 # a kernel's figure is used while its sources hash to the value recorded there
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "zc_codec_gradient64M_hbm_traffic.txt")
 KERNEL_SOURCES = {
-    "zc_encode": ["zc_encode.hip", "zc_encoder.h", "zc_moments.h", "zc_internal.h", "zc_kernels.h",
-                  "zc_format.h"],
+    "zc_encode": ["zc_encode.hip", "zc_place.h", "zc_encoder.h", "zc_moments.h", "zc_internal.h",
+                  "zc_kernels.h", "zc_format.h"],
+    "zc_finish": ["zc_finish.hip", "zc_place.h", "zc_window.h", "zc_encoder.h", "zc_moments.h",
+                  "zc_internal.h", "zc_kernels.h", "zc_format.h"],
     "zc_decode": ["zc_decode.hip", "zc_internal.h", "zc_kernels.h", "zc_format.h"],
     "zc_decode_reduce_wide": ["zc_decode.hip", "zc_internal.h", "zc_kernels.h", "zc_format.h"],
 }
@@ -307,28 +309,38 @@ def main():
     # the bytes this library must move: the input once (the moments come
     # from the coding pass), the stream out; decompress reads the stream and
     # writes the values.  The method-bytes count adds a second read of the
-    # input (a separate sigma pass before coding), as the survey counts it.
+    # input (a separate sigma pass before coding), as the method counts it.
     comp_bytes = 2 * N + stream_bytes
     comp_bytes_method = 2 * N + 2 * N + stream_bytes
     dec_bytes = stream_bytes + 2 * N
 
     # the window prediction failing on every timed call: two resident tensors
-    # whose windows differ (the workload, and the workload times 16, exact in
-    # BF16: every exponent 4 higher) compressed in turn on one workspace, so
-    # each call codes with the other tensor's window first and the segment is
-    # coded again in the same call
+    # whose windows differ compressed in turn on one workspace, so each call
+    # codes with the other tensor's window first and the segment is coded
+    # again in the same call.  The workload and the workload times 2 (exact
+    # in BF16: every exponent one higher, sigma one binade up, the window
+    # one step up) are the miss of a sigma that drifts across a binade
+    # boundary; times 16 (four binades) is a far miss, where most values
+    # escape in the first pass
     log("prediction miss")
-    x16 = (xd.view(torch.bfloat16) * 16).view(torch.int16)
-    out16 = plan.empty_output()
-    pair = [(xd, out), (x16, out16)]
-    turn = [0]
+    out_m = plan.empty_output()
 
-    def comp_alt():
-        a, o = pair[turn[0] % 2]
-        turn[0] += 1
-        plan.compress(a, o, sizes, ws)
+    def miss_times(scale):
+        xs = (xd.view(torch.bfloat16) * scale).view(torch.int16)
+        pair = [(xd, out), (xs, out_m)]
+        turn = [0]
 
-    tmiss = timed(comp_alt, args.steps, args.warmup, stream, flush)
+        def comp_alt():
+            a, o = pair[turn[0] % 2]
+            turn[0] += 1
+            plan.compress(a, o, sizes, ws)
+
+        t = timed(comp_alt, args.steps, args.warmup, stream, flush)
+        del xs
+        return t
+
+    tmiss = miss_times(2)
+    tmiss_far = miss_times(16)
     comp()  # the workload's own window back in the workspace
     torch.cuda.synchronize()
     assert int(sizes.cpu()[0]) == stream_bytes
@@ -361,7 +373,7 @@ def main():
     tds = timed(lambda: rot_call("d"), 4 * args.steps, 4 * args.warmup, stream)
     torch.cuda.synchronize()
     assert all(torch.equal(yi[:N], xd[:N]) for _, _, yi in sets)
-    del sets, x16, out16
+    del sets, out_m
 
     # the encoder pass, timed on its own: HIP events on this stream around
     # each kernel of a compress call (cold, like the calls above)
@@ -418,13 +430,15 @@ def main():
         "decompress_ms": round(t_d * 1e3, 4),
         # bytes this library moves (input once + stream) / cold time / 8 TB/s
         "compress_hbm_frac": round(comp_bytes / t_c / HBM_PEAK, 4),
-        # the survey's method count (a separate sigma read of the input too)
+        # the method's count: a separate sigma pass reads the input a second time
         "compress_hbm_frac_method_bytes": round(comp_bytes_method / t_c / HBM_PEAK, 4),
         "decompress_hbm_frac": round(dec_bytes / t_d / HBM_PEAK, 4),
         "timing": "cold: caches filled by a 1 GiB read before every timed call; "
                   "medians of the timed calls",
-        # every timed call a failed window prediction (two tensors, windows 4 apart)
+        # every timed call a failed window prediction: windows one step apart
+        # (sigma one binade away), and four apart (_far)
         "compress_ms_miss": round(float(np.median(tmiss)) * 1e3, 4),
+        "compress_ms_miss_far": round(float(np.median(tmiss_far)) * 1e3, 4),
         # zc_compress_window with the tensor's own window (no moments)
         "compress_window_ms": round(float(np.median(tfixed)) * 1e3, 4),
         # back-to-back calls over 4 rotating buffer sets (no flush)
@@ -475,6 +489,13 @@ def main():
     # committed SQ counter summary
     res["roofline_issue"] = issue_roofline("zc_encode", float(ku[0]) * 1e-6)
     res["roofline_issue_decode"] = issue_roofline("zc_decode", t_d)
+    # the whole compress call's HBM bytes from the counters (encoder pass +
+    # the merged tail kernel) against the bytes it must move (input once +
+    # stream): the rest is the escape staging round trip and over-reads
+    te, tt = measured_traffic("zc_encode"), measured_traffic("zc_finish")
+    res["compress_traffic"] = None if te is None or tt is None else {
+        "encode": te, "tail": tt, "total": te + tt, "one_read_bytes": comp_bytes,
+        "ratio": round((te + tt) / comp_bytes, 4)}
 
     if args.copy_ref:
         src = torch.empty(64 << 20, dtype=torch.int16, device="cuda").fill_(1)
@@ -511,6 +532,14 @@ def main():
         res["reduce_ms"] = round(tr * 1e3, 4)
         res["reduce_hbm_frac"] = round((tot + 2 * n) / tr / HBM_PEAK, 4)
         res["reduce_out_GBps"] = round(2 * n / tr / 1e9, 2)
+        # one launch per call: the event time is the kernel's launch time
+        res["roofline_reduce"] = {"bound": "hbm", "kernel": "zc_decode_reduce_wide",
+                                  "achieved": round((tot + 2 * n) / tr / 1e9, 1),
+                                  "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                                  "frac": round((tot + 2 * n) / tr / HBM_PEAK, 4),
+                                  "traffic": measured_traffic("zc_decode_reduce_wide"),
+                                  "algorithmic_bytes": tot + 2 * n,
+                                  "launch_us": round(tr * 1e6, 2)}
         res["roofline_issue_reduce"] = issue_roofline("zc_decode_reduce_wide", tr)
 
         # the native path: the same 8 shards uncompressed, summed by a plain
