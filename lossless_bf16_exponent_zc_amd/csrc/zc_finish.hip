@@ -5,11 +5,13 @@
 // comes from the standard deviation) and technique 2 (the kernels pipeline
 // data movement with compression work).
 //
-// Workgroups [0, nwin) are window workgroups, one per segment: the moments'
-// top levels -> variance -> window.  As soon as the window is known the
-// workgroup publishes it, with whether the encoder's pass used it, in the
-// segment's flag word; then it writes the statistics and the header fields
-// known before encoding.
+// Workgroups [0, nwin) are window workgroups: a segment's moment tree is
+// split into parts of 2048 blocks (at most four), one workgroup each; every
+// part but the last publishes its sums as atomic words, and the segment's
+// last part joins them (the tree's top levels) -> variance -> window.  As
+// soon as the window is known that workgroup publishes it, with whether the
+// encoder's pass used it, in the segment's flag word; then it writes the
+// statistics and the header fields known before encoding.
 // Workgroups [nwin, nwin + chunks) place one chunk each.  Before they look
 // at the flag they load what a held prediction makes final: the chunk's
 // group counts, its staged escape bytes, and its escape offset, summed from
@@ -17,15 +19,16 @@
 // latency and the placement's loads overlap, and on a hit the workgroup
 // places its run at once; it also writes its chunk-table entry, and the
 // segment's last chunk writes E, the total and the stream size.  Nothing
-// the window workgroup writes is read in this kernel (the flag word carries
-// the window), so no fence is needed.
+// the window workgroups write is read in this kernel except atomic words
+// (the part sums, and the flag word, which carries the window), so no
+// fence is needed.
 // On a miss the workgroup codes its chunk again with the published window,
 // publishes the chunk's escape count and sums the counts of the chunks
 // before it as they arrive, then places as on a hit.
-// Waiting never goes the other way: window workgroups wait for nothing, and
-// a placement workgroup waits only for its segment's window workgroup and
-// for chunks before its own, all of lower workgroup index, which the
-// hardware dispatches first.  Every wait is bounded; a wait that runs out
+// Waiting never goes the other way: a segment's last window part waits only
+// for its other parts, and a placement workgroup only for its segment's
+// last window part and for chunks before its own, all of lower workgroup
+// index, which the hardware dispatches first.  Every wait is bounded; a wait that runs out
 // leaves the segment's stream size 0 (no stream is shorter than 64 bytes).
 // Plans whose segments hold more than 8192 moment blocks (the direct offset
 // sums would grow), with the raw fallback, or with the static/dynamic split

@@ -46,9 +46,9 @@ static uint64_t pow2_at_least(uint64_t v) {
     return p;
 }
 
-static void check_layout(const std::vector<uint64_t>& n, uint32_t chunk_arg) {
+static void check_layout(const std::vector<uint64_t>& n, uint32_t chunk_arg, uint32_t flags = 0) {
     PlanLayout L;
-    const int rc = build_layout((uint32_t)n.size(), n.data(), chunk_arg, 0u, L);
+    const int rc = build_layout((uint32_t)n.size(), n.data(), chunk_arg, flags, L);
     uint64_t G = 0;
     for (uint64_t v : n) G += cdiv(v, kGroup);
     const uint32_t C = chunk_arg ? chunk_arg : 65536u;
@@ -60,6 +60,7 @@ static void check_layout(const std::vector<uint64_t>& n, uint32_t chunk_arg) {
     CHECK(rc == kLayoutOk);
     if (rc != kLayoutOk) return;
     CHECK(L.nseg == n.size() && L.chunk == C && L.block == (C < kSigmaBlock ? C : kSigmaBlock));
+    CHECK(L.flags == flags);
     CHECK(L.segs.size() == n.size() && L.groups.size() == G);
     uint64_t in_end = 0, out_end = 0, K = 0, slots = 0, items = 0, wgs = 0;
     for (size_t s = 0; s < n.size(); ++s) {
@@ -103,9 +104,9 @@ static void check_layout(const std::vector<uint64_t>& n, uint32_t chunk_arg) {
         wgs += d.wr;
     }
     CHECK(L.chunks.size() == K && L.pairs.size() == 4 * items && L.witems.size() == wgs);
-    // the merged finish kernel: segments of at most kFinishMaxBlocks moment
-    // blocks (the fuzz plans have no raw fallback)
-    bool merged = true;
+    // the merged finish kernel: no raw fallback, and segments of at most
+    // kFinishMaxBlocks moment blocks
+    bool merged = (flags & kPlanRawFallback) == 0;
     for (const SegDesc& d : L.segs) merged = merged && d.nsb <= kFinishMaxBlocks;
     CHECK(L.merged_tail == merged);
     // the finish kernel's window parts: each segment's blocks in parts of
@@ -145,6 +146,8 @@ int main() {
     check_layout({0, 0, 0}, 2048);
     check_layout({(1ull << 32) - 1}, 0);
     check_layout({(1ull << 32) - 1}, 2048);
+    check_layout({(1ull << 32) - 1}, 0, kPlanRawFallback);
+    check_layout({0, 1, 70000}, 4096, kPlanRawFallback);
     check_layout({7, 8, 2047, 2048, 2049, 16383, 16384, 16385, 65535, 65536, 65537}, 0);
     for (uint32_t c : {0u, 1000u, 1024u, 2048u, 3000u, 4096u, 8192u, 16384u, 32768u, 65536u, 131072u})
         check_layout({12345, 0, 99999}, c);
@@ -181,7 +184,7 @@ int main() {
             }
         }
         if (t % 500 == 7) v[0] = (1ull << 32) - 1 - (next_u64() % 5000);
-        check_layout(v, chunks[next_u64() % 7]);
+        check_layout(v, chunks[next_u64() % 7], (next_u64() & 1) ? kPlanRawFallback : 0u);
         ++plans;
     }
     if (failures) return 1;
