@@ -202,7 +202,10 @@ struct GroupData {
 // regions fails the size check; a raw stream reads its words elsewhere).
 // EARLY = false (the reduce that walks the shards in turn, which holds a
 // second stream's loads meanwhile): the table words are read after the
-// header check, to stay within its registers.
+// header check, to stay within its registers.  FLAT (the fused reduce,
+// which reads S streams for every value it writes): the plane and sign+
+// mantissa words are non-temporal loads (8 x 32M shards: 95.7 -> 94.0 us;
+// the plain decoder, one stream in and one out, is faster without).
 template <bool EARLY, bool FLAT>
 __device__ __forceinline__ void fetch(const uint8_t* st, uint64_t cap, const SegDesc& sd,
                                       uint32_t C, uint32_t g, uint32_t lane, const uint8_t* dummy,
@@ -241,9 +244,13 @@ __device__ __forceinline__ void fetch(const uint8_t* st, uint64_t cap, const Seg
     const uint8_t* cw = fb + (fixed_ok ? sd.code_off + 768ull * g : 0) + 4u * lane;
     const uint8_t* sw = fb + (fixed_ok ? sd.sm_off + 2048ull * g : 0) + 8u * lane;
 #pragma unroll
-    for (int b = 0; b < 3; ++b) d.P[b] = ld<uint32_t>(cw + 256 * b);
+    for (int b = 0; b < 3; ++b)
+        d.P[b] = FLAT ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(cw + 256 * b))
+                      : ld<uint32_t>(cw + 256 * b);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) d.sm[q] = ld<u32x2>(sw + 512 * q);
+    for (int q = 0; q < 4; ++q)
+        d.sm[q] = FLAT ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sw + 512 * q))
+                       : ld<u32x2>(sw + 512 * q);
     // every header and table word is needed here, after all the loads are
     // issued: the compiler may not sink any of them behind a check (the
     // scalar loads then all go out in the first round)
@@ -631,7 +638,8 @@ __global__ __launch_bounds__(256) void zc_reduce_native(NativeReduceArgs a) {
     for (uint64_t w = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; w < words; w += step) {
         u32x4 v[S];
 #pragma unroll
-        for (int s = 0; s < S; ++s) v[s] = reinterpret_cast<const u32x4*>(a.in[s])[w];
+        for (int s = 0; s < S; ++s)  // non-temporal: read once (8 x 32M: 117 -> 109 us)
+            v[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.in[s]) + w);
         float acc[8];
 #pragma unroll
         for (int s = 0; s < S; ++s)
