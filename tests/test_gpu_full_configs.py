@@ -55,6 +55,34 @@ def test_gradient_64M():
     check_full([W.gradient()], "gradient 67,108,864")
 
 
+def times2(x):
+    """BF16 bits of 2x (exact: every finite value's exponent one up; the
+    gradient workload has no value near the top of the range)."""
+    f = (x.astype(np.uint32) << 16).view(np.float32) * np.float32(2)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_gradient_64M_window_paths():
+    # the other compress paths at full size (1024 chunks, a moment tree in
+    # two parts): a failed prediction (the workspace last saw the tensor
+    # times 2, whose window is one step up), the caller's fixed window equal
+    # to the natural one, and a fixed window one step up
+    x = W.gradient()
+    ref = oracle.compress(x, C=CHUNK)
+    L = ref[6]
+    _, plan, _, ws = gpu_compress([times2(x)], CHUNK)
+    assert plan.read_sigma(ws, 0)[4] == L + 1
+    miss, _, _, _ = gpu_compress([x], CHUNK, plan=plan, ws=ws)
+    assert_same_bytes(miss[0], ref, "failed prediction")
+    assert plan.read_sigma(ws, 0)[4] == L
+    say("  prediction miss: stream identical to the oracle's")
+    fixed, _, _, _ = gpu_compress([x], CHUNK, window=L, plan=plan, ws=ws)
+    assert_same_bytes(fixed[0], ref, "fixed natural window")
+    up, _, _, _ = gpu_compress([x], CHUNK, window=L + 1, plan=plan, ws=ws)
+    assert_same_bytes(up[0], oracle.compress(x, C=CHUNK, L=L + 1), "fixed window one step up")
+    say("  fixed windows: streams identical to the oracle's")
+
+
 def test_llama_mlp_layer():
     check_full(W.llama_mlp(), "Llama3-8B MLP matrices")
 
