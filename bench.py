@@ -252,6 +252,35 @@ def raw_fallback(zc, N, chunk, args, stream, flush, res):
         "decompress_ms": round(float(np.median(timed(zdec, args.steps, args.warmup, stream, flush))) * 1e3, 4)}
 
 
+def cold_calls(zc, W, plan, comp, dec, chunk, k):
+    """K cold calls of each timed operation, nothing else: a kernel trace of
+    this run gives the kernels' own cold durations, without the HIP events'
+    overhead (an empty event pair reads about 4.4 us on an MI355X)."""
+    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    for fn in (comp, dec):
+        for _ in range(k):
+            flush.sum()
+            fn()
+            torch.cuda.synchronize()
+    shards = W.shards()
+    n = shards[0].size
+    cplan, rplan = zc.Plan([n], chunk), zc.Plan([n], chunk)
+    cap = cplan.out_bytes
+    bufs = [torch.empty(cap, dtype=torch.uint8, device="cuda") for _ in shards]
+    csz, cws = cplan.empty_sizes(), cplan.empty_workspace()
+    for s, b in zip(shards, bufs):
+        xi = cplan.empty_input()
+        xi[:n] = torch.from_numpy(s.view(np.int16)).cuda()
+        cplan.compress(xi, b, csz, cws)
+    rws, r = rplan.empty_workspace(decode_only=True), rplan.empty_input()
+    for _ in range(k):
+        flush.sum()
+        rplan.decompress_reduce(bufs, r, rws, capacity=cap)
+        torch.cuda.synchronize()
+    assert rplan.read_status(rws) == 0
+    log(f"{k} cold calls each of compress, decompress and the 8-shard reduce")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,6 +295,10 @@ def main():
     ap.add_argument("--copy-ref", action="store_true",
                     help="also time a plain 128 MiB device-to-device copy (bandwidth "
                          "reference and counter calibration)")
+    ap.add_argument("--cold-calls", type=int, default=0, metavar="K",
+                    help="only issue K cold compress, K cold decompress and K cold 8-shard "
+                         "reduce calls (caches filled before each) and print no JSON line: "
+                         "for a kernel trace of the kernels' own cold durations")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -296,6 +329,10 @@ def main():
     assert torch.equal(y[:N], xd[:N]), "round trip not exact"
     stream_bytes = int(sizes.cpu()[0])
     E = int(np.frombuffer(out[24:32].cpu().numpy().tobytes(), "<u8")[0])
+
+    if args.cold_calls:
+        cold_calls(zc, W, plan, comp, dec, chunk, args.cold_calls)
+        return
 
     log("timing")
     flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB
