@@ -329,6 +329,10 @@ zc_status zc_compress_timed(const zc_plan* p, const void* d_in, void* d_out, uin
         if (hipEventElapsedTime(&ms, ev[k], ev[k + 1]) != hipSuccess) st = ZC_ERR_HIP;
         us[k] = 1000.f * ms;
     }
+    // a merged plan records its last two events back to back (no kernel
+    // between them): what they read is the events' own overhead, not a
+    // kernel's time
+    if (st == ZC_OK && p->merged_tail) us[2] = 0.f;
     for (auto& e : ev)
         if (e) (void)hipEventDestroy(e);
     return st;

@@ -379,17 +379,21 @@ def test_reduce_rejection_set_matches_oracle():
 
 
 def test_timed_compress_same_streams():
+    # the merged tail (two kernels: us[2] is 0) and the three-kernel tail of
+    # a raw-fallback plan (every time positive), same streams as the oracle's
     from lossless_bf16_exponent_zc_amd import Plan
     from gpu_util import pack_inputs
     x = W.gradient(3 * 65536 + 999, seed=12)
-    plan = Plan([x.size])
-    xd = pack_inputs(plan, [x])
-    out, sizes, ws = plan.empty_output(), plan.empty_sizes(), plan.empty_workspace()
-    for _ in range(2):  # a fresh workspace (prediction may fail), then a settled one
-        us = plan.compress_timed(xd, out, sizes, ws)
-        assert len(us) == 3 and all(t > 0 for t in us), us
-        n = int(sizes.cpu()[0])
-        assert_same_bytes(out[:n].cpu().numpy().tobytes(), oracle.compress(x))
+    for raw in (False, True):
+        plan = Plan([x.size], raw_fallback=raw)
+        xd = pack_inputs(plan, [x])
+        out, sizes, ws = plan.empty_output(), plan.empty_sizes(), plan.empty_workspace()
+        for _ in range(2):  # a fresh workspace (prediction may fail), then a settled one
+            us = plan.compress_timed(xd, out, sizes, ws)
+            assert len(us) == 3 and us[0] > 0 and us[1] > 0, us
+            assert (us[2] > 0) if raw else (us[2] == 0), (raw, us)
+            n = int(sizes.cpu()[0])
+            assert_same_bytes(out[:n].cpu().numpy().tobytes(), oracle.compress(x, raw_fallback=raw))
 
 
 def test_decompress_reduce_more_than_eight_shards():
