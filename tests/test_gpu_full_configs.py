@@ -83,6 +83,28 @@ def test_gradient_64M_window_paths():
     say("  fixed windows: streams identical to the oracle's")
 
 
+def test_merged_tail_part_boundaries():
+    # one plan, two segments at the window parts' edges: 2048 moment blocks
+    # and one value (two parts, the second holding one block) and exactly
+    # 8192 blocks (four full parts, the largest segment the merged tail
+    # takes); fresh, then after a failed prediction (the workspace last saw
+    # the tensors times 2)
+    a = W.small(2048 * 16384 + 1, seed=21)
+    b = W.gradient(8192 * 16384, seed=22)
+    refs = pool_map(lambda x: oracle.compress(x, C=CHUNK), [a, b])
+    streams, plan, _, ws = gpu_compress([a, b], CHUNK)
+    for s, (st, ref) in enumerate(zip(streams, refs)):
+        assert_same_bytes(st, ref, f"fresh, segment {s}")
+    say("  fresh workspace: streams identical to the oracle's")
+    gpu_compress([times2(a), times2(b)], CHUNK, plan=plan, ws=ws)
+    streams, _, _, _ = gpu_compress([a, b], CHUNK, plan=plan, ws=ws)
+    for s, (st, ref) in enumerate(zip(streams, refs)):
+        assert_same_bytes(st, ref, f"after a failed prediction, segment {s}")
+    for s, x in enumerate((a, b)):
+        assert stat_bits(plan.read_sigma(ws, s)) == stat_bits(oracle.sigma(x)), s
+    say("  failed prediction: streams and statistics identical to the oracle's")
+
+
 def test_llama_mlp_layer():
     check_full(W.llama_mlp(), "Llama3-8B MLP matrices")
 
