@@ -186,8 +186,9 @@ __device__ __forceinline__ uint32_t predicted_L(uint32_t raw) {
 // moment partials: the tree needs each lane to hold 32 consecutive values,
 // so once a group is coded its words are transposed through the wave's LDS
 // area, and groups join pairwise into blocks.  A wave loads its second
-// group once the first is done, so the two groups' words are never live
-// together (the encoder runs at 64 VGPRs, 8 waves per SIMD).
+// group once the first group's words are in LDS (with MOMENTS) or coded
+// (without), so the two groups' words are never live together (80 VGPRs
+// and 6 waves per SIMD with MOMENTS, 44 VGPRs without).
 // LDS per wave: 4112 bytes, first a 32-byte exponent row per lane and the
 // packed escapes (every value may escape), then the group's values for the
 // transpose.  Every thread of the 256-thread workgroup calls this
@@ -224,8 +225,8 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
                                  : a.pairs[wg * 4 + wave];
     const bool live = it.seg != 0xFFFFFFFFu;
     const uint64_t g0 = 2ull * it.local;
-    // group 0's words; group 1's are loaded once group 0 is coded, so the
-    // two groups' words are never live together
+    // group 0's words; group 1's are loaded once group 0's are in LDS (or
+    // coded), so the two groups' words are never live together
     u32x4 w[2][4];
     if (live) load_group(a.in + sd.in_off, sd.n, g0, lane, w[0]);
     if (!L) L = predicted_L(a.stats[first.seg].L);
@@ -292,6 +293,12 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
 #pragma unroll
                 for (int k = 0; k < 4; ++k) s_area[wave][tslot(64 * k + lane)] = w[q][k];
                 __builtin_amdgcn_wave_barrier();
+                // group q + 1's loads now: the moments read the LDS copy, so
+                // its words take the registers group q's words leave, and
+                // the loads overlap the moments (80 VGPRs, 6 waves per SIMD:
+                // 46.8 us against 47.6 for the pass at 64 VGPRs and 8 waves
+                // with the loads after the moments)
+                if (q == 0 && g + 1 < sd.g) load_group(a.in + sd.in_off, sd.n, g + 1, lane, w[1]);
                 const uint64_t left = sd.n - (uint64_t)kGroup * g;
                 double m1, m2;
                 uint32_t mn;
@@ -303,8 +310,6 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
                     s_gn[2 * wave + q] = mn;
                 }
                 __builtin_amdgcn_wave_barrier();  // before the next group reuses the area
-                // group q + 1's loads once this group is done (other waves hide them)
-                if (q == 0 && g + 1 < sd.g) load_group(a.in + sd.in_off, sd.n, g + 1, lane, w[1]);
             }
         }
     }
