@@ -125,7 +125,12 @@ __device__ __forceinline__ void place_begin(const PlaceArgs& a, uint32_t ci, Pla
 // last group's slot and are not stored).  MASKED = true: the wave's group
 // counts first, then only the dwords each group's run covers (the reads
 // then track the escapes; one more round, for callers that have other
-// latency to hide it behind).
+// latency to hide it behind), except each group's first dword per lane
+// (256 bytes), loaded at once: a run of typical length gets most of its
+// bytes without waiting for its count, and a short run's few extra bytes
+// cost nothing measurable (67,108,864 values with 20% escapes: a failed
+// prediction's tail 1.0 us shorter, a held one's unchanged; 2.45%: the
+// same).
 template <int GPW, bool MASKED>
 __device__ __forceinline__ void place_load(const PlaceArgs& a, PlaceChunk<GPW>& pc) {
     const uint32_t lane = lane_id(), wave = wave_id(), nw = blockDim.x >> 6;
@@ -135,6 +140,13 @@ __device__ __forceinline__ void place_load(const PlaceArgs& a, PlaceChunk<GPW>& 
     if (MASKED) {
 #pragma unroll
         for (int q = 0; q < GPW; ++q) cnt[q] = gcnt[min(wave + nw * q, pc.ng - 1)];  // wave-uniform
+    }
+    if (MASKED) {
+#pragma unroll
+        for (int q = 0; q < GPW; ++q) {
+            const uint32_t j = min(wave + nw * q, pc.ng - 1);
+            pc.lo[q][0] = pc.slot0[(uint64_t)j * (kGroup / 4) + lane];
+        }
     }
 #pragma unroll
     for (int q = 0; q < GPW; ++q) {
@@ -146,10 +158,10 @@ __device__ __forceinline__ void place_load(const PlaceArgs& a, PlaceChunk<GPW>& 
             pc.past[q] = s32[64 * kPlaceR];  // wave-uniform address
         } else {
             // dwords 0 .. n/4 + 1 carry the run (an output dword needs its
-            // source dword and the next)
+            // source dword and the next); dwords past it are never stored
             const uint32_t need = min(cnt[q], kGroup) / 4 + 2;
 #pragma unroll
-            for (int r = 0; r < kPlaceR; ++r)
+            for (int r = 1; r < kPlaceR; ++r)
                 pc.lo[q][r] = lane + 64 * r < need ? s32[lane + 64 * r] : 0u;
             pc.past[q] = 64 * kPlaceR < need ? s32[64 * kPlaceR] : 0u;
         }
