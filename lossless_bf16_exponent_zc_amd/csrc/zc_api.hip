@@ -143,8 +143,13 @@ zc_status compress_impl(const zc_plan* p, const void* d_in, void* d_out, uint64_
     ea.seg0 = p->segs[0];
     if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return ZC_ERR_HIP;
     if (nwg) {
-        if (forced_L) hipLaunchKernelGGL((zc_encode<false>), dim3(nwg), dim3(256), 0, stream, ea);
-        else hipLaunchKernelGGL((zc_encode<true>), dim3(nwg), dim3(256), 0, stream, ea);
+        // grids of at most 256 items (4M values) take eight waves of one
+        // group each, so a wave's chain is one group long (1M values:
+        // compress 21.5 us against 24; 8M: even; 16M and up: slower, the
+        // second group's loads no longer overlap the first's moments)
+        if (forced_L) hipLaunchKernelGGL((zc_encode<false, 2>), dim3(nwg), dim3(256), 0, stream, ea);
+        else if (nwg <= 256) hipLaunchKernelGGL((zc_encode<true, 1>), dim3(nwg), dim3(512), 0, stream, ea);
+        else hipLaunchKernelGGL((zc_encode<true, 2>), dim3(nwg), dim3(256), 0, stream, ea);
     }
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return ZC_ERR_HIP;
     WindowArgs wa{ea, p->d_witems, ws_ptr<SegStat>(p, d_ws, p->ws.stats), d_stream_bytes,

@@ -4,21 +4,25 @@
 //
 // zc_encode: one workgroup item (zc_encoder.h) per workgroup, with the
 // window predicted from the previous call (or the caller's fixed window);
-// records the window it used per segment.  The window kernel checks the
+// records the window it used per segment.  GW = 2: four waves of two groups
+// (the common shape); GW = 1: eight waves of one group, for grids of at most
+// 256 items, whose time is one wave's chain rather than the chip's bandwidth.  The window kernel checks the
 // prediction and codes the segment again where it failed.
 //
 // zc_place_escapes, one workgroup per chunk, one wave per encoder wave: the
 // group counts give the group table; the chunk's offset in the segment's
 // escape stream comes from the chunk table; each wave's runs, whose source
 // dwords are loaded before that offset is known, go to their place.
+#include <type_traits>
+
 #include "zc_place.h"
 
 namespace zc {
 
-template <bool MOMENTS>
-__global__ __launch_bounds__(256) void zc_encode(EncodeArgs a) {
-    __shared__ EncodeLds lds;
-    encode_wg<MOMENTS>(a, blockIdx.x, a.forced_L, lds);  // 0: the predicted window
+template <bool MOMENTS, int GW>
+__global__ __launch_bounds__(GW == 2 ? 256 : 512) void zc_encode(EncodeArgs a) {
+    __shared__ typename std::conditional<GW == 2, EncodeLds, EncodeLds8>::type lds;
+    encode_wg<MOMENTS, false, GW>(a, blockIdx.x, a.forced_L, lds);  // 0: the predicted window
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.zero = 0u;
     const ItemDesc first = a.single ? ItemDesc{0u, 4 * blockIdx.x} : a.pairs[blockIdx.x * 4];
     if (first.local == 0 && threadIdx.x == 0) {  // the segment's first item
@@ -39,8 +43,9 @@ __global__ __launch_bounds__(256) void zc_encode(EncodeArgs a) {
     }
 }
 
-template __global__ void zc_encode<true>(EncodeArgs);
-template __global__ void zc_encode<false>(EncodeArgs);
+template __global__ void zc_encode<true, 2>(EncodeArgs);
+template __global__ void zc_encode<false, 2>(EncodeArgs);
+template __global__ void zc_encode<true, 1>(EncodeArgs);
 
 template <int GPW>
 __global__ __launch_bounds__(256) void zc_place_escapes(PlaceArgs a) {

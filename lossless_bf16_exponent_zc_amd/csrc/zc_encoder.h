@@ -178,9 +178,10 @@ __device__ __forceinline__ uint32_t predicted_L(uint32_t raw) {
 }
 
 // One workgroup item: four waves, each with two consecutive groups of one
-// segment (item list: one entry per wave; each segment's list is padded to
-// whole workgroups with entries of segment ~0, whose waves do no work), so
-// the item covers 16,384 aligned values of one segment: one moment block, or
+// segment (item list: one entry per wave pair of groups; each segment's list
+// is padded to whole workgroups with entries of segment ~0, whose waves do
+// no work), or eight waves with one group each (GW = 1, below), so the item
+// covers 16,384 aligned values of one segment: one moment block, or
 // several whole ones when the chunk is smaller.  Codes with window L; each
 // group's escape count and each block's total; with MOMENTS, the blocks'
 // moment partials: the tree needs each lane to hold 32 consecutive values,
@@ -191,8 +192,8 @@ __device__ __forceinline__ uint32_t predicted_L(uint32_t raw) {
 // and 6 waves per SIMD with MOMENTS, 44 VGPRs without).
 // LDS per wave: 4112 bytes, first a 32-byte exponent row per lane and the
 // packed escapes (every value may escape), then the group's values for the
-// transpose.  Every thread of the 256-thread workgroup calls this
-// (barriers).  L = 0: the predicted window, read once the item's loads are
+// transpose.  Every thread of the workgroup (256 or 512 threads) calls
+// this (barriers).  L = 0: the predicted window, read once the item's loads are
 // out (the first pass: its waves do not wait for the statistics before
 // loading).
 // LDS of one encoder workgroup item (the caller declares it, so kernels with
@@ -203,11 +204,21 @@ struct EncodeLds {
     uint32_t gn[8], gc[8];
 };
 
+// The same for a workgroup of eight waves with one group each.
+struct EncodeLds8 {
+    u32x4 area[8][257];  // per wave, 4112 bytes
+    double g1[8], g2[8];
+    uint32_t gn[8], gc[8];
+};
+
 // AGAIN: a second coding of the item with another window (a failed
 // prediction): the sign+mantissa bytes do not depend on the window and are
-// already in place, so they are not written again.
-template <bool MOMENTS, bool AGAIN = false>
-__device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint32_t L, EncodeLds& lds) {
+// already in place, so they are not written again.  GW: groups per wave,
+// 2 (four waves, EncodeLds) or 1 (eight waves, EncodeLds8: the same item,
+// each wave's chain one group long, for grids that fill less than one
+// round of the chip).
+template <bool MOMENTS, bool AGAIN = false, int GW = 2, typename Lds = EncodeLds>
+__device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint32_t L, Lds& lds) {
     auto& s_area = lds.area;
     auto& s_g1 = lds.g1;
     auto& s_g2 = lds.g2;
@@ -221,10 +232,12 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
     // the workgroup's first entry is live: its segment is the workgroup's
     const ItemDesc first = a.single ? ItemDesc{0u, 4 * wg} : a.pairs[wg * 4];
     const SegDesc sd = a.single ? a.seg0 : a.segs[first.seg];
-    const ItemDesc it = a.single ? ItemDesc{4 * wg + wave < (sd.g + 1) / 2 ? 0u : 0xFFFFFFFFu, 4 * wg + wave}
-                                 : a.pairs[wg * 4 + wave];
-    const bool live = it.seg != 0xFFFFFFFFu;
-    const uint64_t g0 = 2ull * it.local;
+    const uint32_t pw = GW == 2 ? wave : wave >> 1;  // the wave's entry in the item list
+    const ItemDesc it = a.single ? ItemDesc{4 * wg + pw < (sd.g + 1) / 2 ? 0u : 0xFFFFFFFFu, 4 * wg + pw}
+                                 : a.pairs[wg * 4 + pw];
+    const uint64_t g0 = 2ull * it.local + (GW == 2 ? 0u : (wave & 1u));
+    const bool live = it.seg != 0xFFFFFFFFu && g0 < sd.g;
+    const uint32_t gi0 = GW == 2 ? 2 * wave : wave;  // the wave's first group in the item
     // group 0's words; group 1's are loaded once group 0's are in LDS (or
     // coded), so the two groups' words are never live together
     u32x4 w[2][4];
@@ -234,12 +247,12 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
     // known (lane 0); groups past the data keep -0.0 (the identity) and 0
     if (lane == 0) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            s_gc[2 * wave + q] = 0;
+        for (int q = 0; q < GW; ++q) {
+            s_gc[gi0 + q] = 0;
             if (MOMENTS) {
-                s_g1[2 * wave + q] = -0.0;
-                s_g2[2 * wave + q] = -0.0;
-                s_gn[2 * wave + q] = 0;
+                s_g1[gi0 + q] = -0.0;
+                s_g2[gi0 + q] = -0.0;
+                s_gn[gi0 + q] = 0;
             }
         }
     }
@@ -247,7 +260,7 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
         uint8_t* __restrict__ st = a.out + sd.out_off;
         const uint32_t L7 = (L << 7) | (L << 23);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < GW; ++q) {
             const uint64_t g = g0 + q;
             if (g >= sd.g) break;  // uniform
             // coding first, with the words in registers; then (MOMENTS) the
@@ -276,13 +289,13 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
             const uint64_t gg = sd.group_base + g;
             if (lane == 0) {
                 a.gcnt[gg] = tot;
-                s_gc[2 * wave + q] = tot;
+                s_gc[gi0 + q] = tot;
             }
             uint32_t Q[8];
             exponent_bytes(w[q], Q);
             rowp[0] = u32x4{Q[0], Q[1], Q[2], Q[3]};
             rowp[1] = u32x4{Q[4], Q[5], Q[6], Q[7]};
-            if (!MOMENTS && q == 0 && g + 1 < sd.g) load_group(a.in + sd.in_off, sd.n, g + 1, lane, w[1]);
+            if (!MOMENTS && GW == 2 && q == 0 && g + 1 < sd.g) load_group(a.in + sd.in_off, sd.n, g + 1, lane, w[1]);
             const uint8_t* rb = reinterpret_cast<const uint8_t*>(rowp);
             for (uint32_t m = M, i = 0; m; m &= m - 1, ++i) ew[excl + i] = rb[__builtin_ctz(m)];
             __builtin_amdgcn_wave_barrier();  // the wave's packed bytes are complete
@@ -298,16 +311,16 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
                 // the loads overlap the moments (80 VGPRs, 6 waves per SIMD:
                 // 46.8 us against 47.6 for the pass at 64 VGPRs and 8 waves
                 // with the loads after the moments)
-                if (q == 0 && g + 1 < sd.g) load_group(a.in + sd.in_off, sd.n, g + 1, lane, w[1]);
+                if (GW == 2 && q == 0 && g + 1 < sd.g) load_group(a.in + sd.in_off, sd.n, g + 1, lane, w[1]);
                 const uint64_t left = sd.n - (uint64_t)kGroup * g;
                 double m1, m2;
                 uint32_t mn;
                 group_moments(s_area[wave], lane, left < kGroup ? (uint32_t)left : kGroup, special,
                               m1, m2, mn);
                 if (lane == 0) {
-                    s_g1[2 * wave + q] = m1;
-                    s_g2[2 * wave + q] = m2;
-                    s_gn[2 * wave + q] = mn;
+                    s_g1[gi0 + q] = m1;
+                    s_g2[gi0 + q] = m2;
+                    s_gn[gi0 + q] = mn;
                 }
                 __builtin_amdgcn_wave_barrier();  // before the next group reuses the area
             }

@@ -84,7 +84,7 @@ struct NativeReduceArgs {
 
 template <bool SINGLE>
 __global__ void zc_window(WindowArgs a);
-template <bool MOMENTS>
+template <bool MOMENTS, int GW>  // GW: groups per wave (2: 256 threads, 1: 512)
 __global__ void zc_encode(EncodeArgs a);
 template <int GPW>
 __global__ void zc_place_escapes(PlaceArgs a);
