@@ -331,7 +331,34 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, uint32_t wg, uint
     const uint32_t per = a.block_elems / kGroup;  // groups per block: 1, 2, 4 or 8
     const uint32_t b = threadIdx.x;
     const uint32_t blk = (uint32_t)(2ull * first.local / per) + b;
-    if (b < 8 / per && blk < sd.nsb) {
+    if (per == 8) {
+        // one block per item (chunks of 16,384 values or more), the common
+        // case: every LDS value read at once and the trees unrolled.  With
+        // the loops below (trip count known only at run time) the reads
+        // went one after another, and the workgroup's other waves waited
+        // at the barrier meanwhile: 2 us of a workgroup's 11 us (pass
+        // 47.0 -> 45.0 us for 67,108,864 values)
+        if (b == 0 && blk < sd.nsb) {
+            uint32_t c[8], nn[8];
+            double t1[8], t2[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                c[i] = s_gc[i];
+                if (MOMENTS) {
+                    t1[i] = s_g1[i];
+                    t2[i] = s_g2[i];
+                    nn[i] = s_gn[i];
+                }
+            }
+            a.part.esc[sd.sb_base + blk] = ((c[0] + c[1]) + (c[2] + c[3])) + ((c[4] + c[5]) + (c[6] + c[7]));
+            if (MOMENTS) {
+                const uint32_t slot = sd.sb_base + leaf_slot(blk, leaf_order(sd.nsb));
+                a.part.s1[slot] = tree8(t1);
+                a.part.s2[slot] = tree8(t2);
+                a.part.n[slot] = ((nn[0] + nn[1]) + (nn[2] + nn[3])) + ((nn[4] + nn[5]) + (nn[6] + nn[7]));
+            }
+        }
+    } else if (b < 8 / per && blk < sd.nsb) {
         uint32_t e = 0;
         for (uint32_t i = 0; i < per; ++i) e += s_gc[b * per + i];
         a.part.esc[sd.sb_base + blk] = e;
