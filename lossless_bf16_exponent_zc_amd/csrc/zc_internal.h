@@ -121,20 +121,15 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
     return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
 }
 
-// Exclusive prefix over the wave of per-lane counts below 64, one ballot per
-// bit of the count; `total` is the wave's sum (wave-uniform).
+// Exclusive prefix over the wave of per-lane counts; `total` is the wave's
+// sum (wave-uniform).  The DPP scan, not one ballot per bit of the count:
+// the same time on a held prediction, and a failed one's recode, which
+// ranks every group's escapes with it at a few waves per SIMD, 0.7 us
+// shorter.
 __device__ __forceinline__ uint32_t wave_prefix_small(uint32_t c, uint32_t& total) {
-    uint32_t excl = 0, tot = 0;
-#pragma unroll
-    for (int b = 0; b < 6; ++b) {
-        const uint64_t m = __ballot((c >> b) & 1u);
-        const uint32_t below =
-            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        excl += below << b;
-        tot += (uint32_t)__builtin_popcountll(m) << b;
-    }
-    total = tot;
-    return excl;
+    const uint32_t incl = wave_inclusive_scan(c);
+    total = readlane(incl, 63);
+    return incl - c;
 }
 
 // Value index inside a group of the value at (lane, plane bit p).
