@@ -53,6 +53,52 @@ __device__ __forceinline__ void store_run(uint8_t* dst, const uint32_t* src, uin
     if (lane < tail) dst[head + 4 * nd + lane] = (uint8_t)(last >> (8 * lane));
 }
 
+// One wave writes a run of n bytes (a group's escape exponents) from `src`
+// (its staging slot) into the LDS gather buffer at byte `pos`, with lo / hi
+// as for store_run.  Lanes with nothing to store write their own word of
+// `dummy` instead of being masked off, so only a run past the loaded dwords
+// (over 256 R bytes) branches: masked stores, each with its own change of
+// the execution mask, made the gather cost more scalar instructions than
+// vector ones (67,108,864 values: the tail 13.4 -> 13.0 us, event-timed).
+// The shifts stay: unaligned LDS dword stores of the source dwords as they
+// are give the same bytes but take the tail to 19.6 us.
+template <int R>
+__device__ __forceinline__ void gather_run(uint8_t* buf, uint32_t pos, const uint32_t* src, uint32_t n,
+                                           const uint32_t (&lo)[R], const uint32_t (&hi)[R], uint32_t* dummy) {
+    const uint32_t lane = lane_id();
+    const uint32_t head = min(n, (4u - (pos & 3u)) & 3u);
+    const uint32_t nd = (n - head) >> 2, tail = (n - head) & 3u;
+    uint8_t* d = buf + pos + head;  // 4-byte aligned
+    uint32_t v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t k = lane + 64 * r;
+        v[r] = (uint32_t)((((uint64_t)hi[r] << 32) | lo[r]) >> (8 * head));
+        *(k < nd ? reinterpret_cast<uint32_t*>(d + 4 * k) : dummy + lane) = v[r];
+    }
+    uint32_t last;  // the output dword after the whole ones (its first `tail` bytes)
+    if (nd < 64 * R) {
+        uint32_t sel = v[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) sel = (nd >> 6) == (uint32_t)r ? v[r] : sel;
+        last = readlane(sel, (int)(nd & 63));
+    } else {  // a long run: the dwords past the loaded ones, and its last
+        last = 0;
+        for (uint32_t k = lane + 64 * R; k < nd + 64; k += 64) {
+            const uint32_t w = k <= nd ? (uint32_t)((((uint64_t)src[k + 1] << 32) | src[k]) >> (8 * head)) : 0u;
+            if (k < nd) reinterpret_cast<uint32_t*>(d)[k] = w;
+            if (k - lane == (nd & ~63u)) last = readlane(w, (int)(nd & 63));
+        }
+    }
+    // the head bytes (lanes 0-2, from source dword 0) and the tail bytes
+    // (lanes 4-6) in one byte store
+    const uint32_t first = readlane(lo[0], 0);
+    const bool is_head = lane < head, is_tail = lane >= 4 && lane - 4 < tail;
+    uint8_t* bp = is_head ? buf + pos + lane
+                          : (is_tail ? d + 4 * nd + (lane - 4) : reinterpret_cast<uint8_t*>(dummy + 64) + lane);
+    *bp = (uint8_t)(lane < 4 ? first >> (8 * lane) : last >> (8 * ((lane - 4) & 3)));
+}
+
 // Values [v0, min(n, v0 + C)) of a segment into its raw stream (after the
 // 64-byte header), 16-byte words, four in flight per thread.  Not inlined:
 // its registers stay out of the placement path's allocation.
@@ -86,7 +132,7 @@ constexpr uint32_t place_buf_bytes() {  // LDS gather buffer: 8 workgroups per C
 template <int GPW>
 struct PlaceLds {
     u32x4 buf[place_buf_bytes<GPW>() / 16];
-    uint32_t gb[32], gn[32], prefix, t;  // group offsets in the chunk, counts
+    uint32_t dummy[80];  // where lanes with nothing to store in the gather write
 };
 
 // One chunk's geometry (the few segment fields placement needs, not the
@@ -190,24 +236,15 @@ __device__ __forceinline__ bool place_finish(const PlaceArgs& a, PlaceChunk<GPW>
     const uint64_t gc0 = pc.gc0;
     const uint32_t* slot0 = pc.slot0;
     auto& s_buf = lds.buf;
-    auto& s_gb = lds.gb;
-    auto& s_gn = lds.gn;
-    if (wave == 0) {
-        const uint32_t c = lane < ng ? pc.c_raw : 0u;
-        const uint32_t incl = wave_inclusive_scan(c);
-        if (lane < ng) {
-            s_gb[lane] = incl - c;
-            s_gn[lane] = min(c, kGroup);
-        }
-        if (lane == 0) {
-            const uint32_t t = readlane(incl, 63);
-            // counts that would leave the escape region mean no copy (never
-            // the case when the encoder wrote them)
-            lds.prefix = (uint64_t)prefix + t <= pc.n ? prefix : 0xFFFFFFFFu;
-            lds.t = t;
-        }
-    }
-    lds_barrier();
+    // every wave scans the chunk's group counts itself: each group's offset
+    // in the chunk's run (gb) and its count (gn) are read from registers
+    const uint32_t c = lane < ng ? pc.c_raw : 0u;
+    const uint32_t incl = wave_inclusive_scan(c);
+    const uint32_t gb = incl - c, gn = min(c, kGroup);
+    const uint32_t t = readlane(incl, 63);
+    // counts that would leave the escape region mean no copy (never the case
+    // when the encoder wrote them)
+    const uint32_t pre = (uint64_t)prefix + t <= pc.n ? prefix : 0xFFFFFFFFu;
     uint32_t hi[GPW][R];
 #pragma unroll
     for (int q = 0; q < GPW; ++q)
@@ -223,7 +260,6 @@ __device__ __forceinline__ bool place_finish(const PlaceArgs& a, PlaceChunk<GPW>
         lds_barrier();  // the LDS is rewritten by the next chunk
         return true;
     }
-    const uint32_t pre = lds.prefix, t = lds.t;
     const uint32_t off = pre & 15u;  // esc_off and the stream start are multiples of 256
     const bool fits = pre != 0xFFFFFFFFu && off + t <= kBuf;
     uint8_t* buf = reinterpret_cast<uint8_t*>(s_buf);
@@ -231,7 +267,9 @@ __device__ __forceinline__ bool place_finish(const PlaceArgs& a, PlaceChunk<GPW>
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
             const uint32_t j = wave + nw * q;
-            if (j < ng) store_run<R>(buf + off + s_gb[j], slot0 + (uint64_t)j * (kGroup / 4), s_gn[j], pc.lo[q], hi[q]);
+            if (j < ng)
+                gather_run<R>(buf, off + readlane(gb, (int)j), slot0 + (uint64_t)j * (kGroup / 4), readlane(gn, (int)j),
+                              pc.lo[q], hi[q], lds.dummy);
         }
         lds_barrier();
     }
@@ -239,7 +277,7 @@ __device__ __forceinline__ bool place_finish(const PlaceArgs& a, PlaceChunk<GPW>
         lds_barrier();  // the LDS is rewritten by the next chunk
         return false;
     }
-    if (wave == 0 && lane < ng) reinterpret_cast<uint16_t*>(st + pc.gtab_off)[gc0 + lane] = (uint16_t)s_gb[lane];
+    if (wave == 0 && lane < ng) reinterpret_cast<uint16_t*>(st + pc.gtab_off)[gc0 + lane] = (uint16_t)gb;
     if (pre == 0xFFFFFFFFu) {
         lds_barrier();  // the LDS is rewritten by the next chunk
         return true;
@@ -249,7 +287,8 @@ __device__ __forceinline__ bool place_finish(const PlaceArgs& a, PlaceChunk<GPW>
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
             const uint32_t j = wave + nw * q;
-            if (j < ng) store_run<R>(esc + s_gb[j], slot0 + (uint64_t)j * (kGroup / 4), s_gn[j], pc.lo[q], hi[q]);
+            if (j < ng)
+                store_run<R>(esc + readlane(gb, (int)j), slot0 + (uint64_t)j * (kGroup / 4), readlane(gn, (int)j), pc.lo[q], hi[q]);
         }
         lds_barrier();  // the LDS is rewritten by the next chunk
         return true;
