@@ -73,12 +73,24 @@ def timed(fn, steps, warmup, stream, flush=None):
     return [a.elapsed_time(b) * 1e-3 for a, b in evs]  # seconds
 
 
-def sources_hash(kernel):
+def code_text(src):
+    """C++ source with its comments removed and every run of white space made
+    one space: what the compiler sees, so that editing a comment does not
+    change a kernel's hash.  (No string literal in the kernel sources holds
+    // or /*.)"""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def sources_hash(kernel, root=None):
+    """sha256 prefix of a kernel's sources, comments and spacing aside."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "lossless_bf16_exponent_zc_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(root or ROOT, "lossless_bf16_exponent_zc_amd", "csrc", f)) as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -14,7 +14,8 @@
 namespace zc {
 
 // One wave stores a run of n bytes (a group's escape exponents) from `src`
-// (the group's 2048-byte staging slot) to `dst` (global memory or LDS).  The
+// (the group's 2048-byte staging slot) to `dst` in global memory (a chunk
+// whose run does not fit the LDS gather buffer goes out group by group).  The
 // caller has loaded, for output dwords k = lane + 64 r (r < R), lo[r] =
 // source dword k and hi[r] = source dword k+1: output dword k starts at
 // source byte head + 4k, where head (0..3) brings dst to a 4-byte boundary,

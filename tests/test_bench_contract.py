@@ -45,3 +45,10 @@ def test_stale_summary_gives_none_and_current_one_counts(tmp_path, monkeypatch):
     assert r["valu_instructions"] == 1000000
     assert r["frac"] == pytest.approx(1e6 * 64 / 1e-5 / bench.VALU_PEAK, abs=1e-4)
     assert r["bound"] == "alu" and r["launch_us"] == 10.0
+
+
+def test_source_hash_ignores_comments_but_not_code():
+    src = 'int a = 1;  // one\n/* two\n   lines */ int b = a + 2;\nasm volatile("" ::"s"(a));\n'
+    assert bench.code_text(src) == 'int a = 1; int b = a + 2; asm volatile("" ::"s"(a));'
+    assert bench.code_text(src.replace("// one", "// first value")) == bench.code_text(src)
+    assert bench.code_text(src.replace("a + 2", "a + 3")) != bench.code_text(src)
