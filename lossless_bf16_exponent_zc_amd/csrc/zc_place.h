@@ -77,27 +77,39 @@ __device__ __forceinline__ void gather_run(uint8_t* buf, uint32_t pos, const uin
         v[r] = (uint32_t)((((uint64_t)hi[r] << 32) | lo[r]) >> (8 * head));
         *(k < nd ? reinterpret_cast<uint32_t*>(d + 4 * k) : dummy + lane) = v[r];
     }
-    uint32_t last;  // the output dword after the whole ones (its first `tail` bytes)
-    if (nd < 64 * R) {
-        uint32_t sel = v[0];
+    // the output dword after the whole ones (its first `tail` bytes); a long
+    // run's comes with the rest of it (gather_rest)
+    const bool longrun = nd >= 64 * R;
+    uint32_t sel = v[0];
 #pragma unroll
-        for (int r = 1; r < R; ++r) sel = (nd >> 6) == (uint32_t)r ? v[r] : sel;
-        last = readlane(sel, (int)(nd & 63));
-    } else {  // a long run: the dwords past the loaded ones, and its last
-        last = 0;
-        for (uint32_t k = lane + 64 * R; k < nd + 64; k += 64) {
-            const uint32_t w = k <= nd ? (uint32_t)((((uint64_t)src[k + 1] << 32) | src[k]) >> (8 * head)) : 0u;
-            if (k < nd) reinterpret_cast<uint32_t*>(d)[k] = w;
-            if (k - lane == (nd & ~63u)) last = readlane(w, (int)(nd & 63));
-        }
-    }
+    for (int r = 1; r < R; ++r) sel = (nd >> 6) == (uint32_t)r ? v[r] : sel;
+    const uint32_t last = readlane(sel, (int)(nd & 63));
     // the head bytes (lanes 0-2, from source dword 0) and the tail bytes
     // (lanes 4-6) in one byte store
     const uint32_t first = readlane(lo[0], 0);
-    const bool is_head = lane < head, is_tail = lane >= 4 && lane - 4 < tail;
+    const bool is_head = lane < head, is_tail = !longrun && lane >= 4 && lane - 4 < tail;
     uint8_t* bp = is_head ? buf + pos + lane
                           : (is_tail ? d + 4 * nd + (lane - 4) : reinterpret_cast<uint8_t*>(dummy + 64) + lane);
     *bp = (uint8_t)(lane < 4 ? first >> (8 * lane) : last >> (8 * ((lane - 4) & 3)));
+}
+
+// The rest of a long run (over 256 R bytes) that gather_run started: its
+// dwords past the loaded ones, read from the staging slot here, and its
+// last bytes.
+template <int R>
+__device__ __forceinline__ void gather_rest(uint8_t* buf, uint32_t pos, const uint32_t* src, uint32_t n) {
+    const uint32_t lane = lane_id();
+    const uint32_t head = min(n, (4u - (pos & 3u)) & 3u);
+    const uint32_t nd = (n - head) >> 2, tail = (n - head) & 3u;
+    if (nd < 64 * R) return;  // uniform
+    uint8_t* d = buf + pos + head;
+    uint32_t last = 0;
+    for (uint32_t k = lane + 64 * R; k < nd + 64; k += 64) {
+        const uint32_t w = k <= nd ? (uint32_t)((((uint64_t)src[k + 1] << 32) | src[k]) >> (8 * head)) : 0u;
+        if (k < nd) reinterpret_cast<uint32_t*>(d)[k] = w;
+        if (k - lane == (nd & ~63u)) last = readlane(w, (int)(nd & 63));
+    }
+    if (lane < tail) d[4 * nd + lane] = (uint8_t)(last >> (8 * lane));
 }
 
 // Values [v0, min(n, v0 + C)) of a segment into its raw stream (after the
@@ -277,6 +289,20 @@ __device__ __forceinline__ bool place_finish(const PlaceArgs& a, PlaceChunk<GPW>
     if (!go()) {
         lds_barrier();  // the LDS is rewritten by the next chunk
         return false;
+    }
+    // long runs (over 256 R bytes) are finished only now: after a failed
+    // prediction their staged bytes are never read (a uniform test: every
+    // wave holds every group's count).  A first pass whose window was one
+    // step too high leaves about 40% of the 67,108,864-value tensor's values
+    // escaping, with runs past 512 bytes: a failed prediction's tail
+    // 47.5 -> 46.9 us, a held one's unchanged
+    if (fits && __ballot(gn >= 256u * R) != 0) {
+#pragma unroll
+        for (int q = 0; q < GPW; ++q) {
+            const uint32_t j = wave + nw * q;
+            if (j < ng) gather_rest<R>(buf, off + readlane(gb, (int)j), slot0 + (uint64_t)j * (kGroup / 4), readlane(gn, (int)j));
+        }
+        lds_barrier();
     }
     if (wave == 0 && lane < ng) reinterpret_cast<uint16_t*>(st + pc.gtab_off)[gc0 + lane] = (uint16_t)gb;
     if (pre == 0xFFFFFFFFu) {
