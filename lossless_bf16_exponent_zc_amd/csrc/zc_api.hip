@@ -6,7 +6,7 @@
 //                      and escape counts, with each segment's previous window
 //                      as the prediction (or the caller's fixed window)
 //   zc_finish          the two kernels below in one launch, overlapped
-//                      (segments up to 8192 moment blocks, no raw fallback,
+//                      (segments up to 16,384 moment blocks, no raw fallback,
 //                      no split event); a failed prediction is coded again
 //                      chunk by chunk there
 //   zc_window          per segment: variance -> window, statistics, header

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(GW == 2 ? 256 : 512) void zc_encode(EncodeArgs a) {
         a.pred[first.seg] = a.forced_L ? a.forced_L : predicted_L(a.stats[first.seg].L);
         a.done[first.seg] = 0;
         a.flag[first.seg] = 0;
-        for (uint32_t i = 0; i < 16; ++i) a.fpart[16ull * first.seg + i] = ~0ull;
+        for (uint32_t i = 0; i < 4 * kFinishMaxParts; ++i) a.fpart[4ull * kFinishMaxParts * first.seg + i] = ~0ull;
     }
     // the look-back words of the chunks that start in this item (16,384
     // values from value 4096 * first.local)

@@ -6,7 +6,7 @@
 // data movement with compression work).
 //
 // Workgroups [0, nwin) are window workgroups: a segment's moment tree is
-// split into parts of 2048 blocks (at most four), one workgroup each; every
+// split into parts of 2048 blocks (at most eight), one workgroup each; every
 // part but the last publishes its sums as atomic words, and the segment's
 // last part joins them (the tree's top levels) -> variance -> window.  As
 // soon as the window is known that workgroup publishes it, with whether the
@@ -30,7 +30,7 @@
 // last window part and for chunks before its own, all of lower workgroup
 // index, which the hardware dispatches first.  Every wait is bounded; a wait that runs out
 // leaves the segment's stream size 0 (no stream is shorter than 64 bytes).
-// Plans whose segments hold more than 8192 moment blocks (the direct offset
+// Plans whose segments hold more than 16,384 moment blocks (the direct offset
 // sums would grow), with the raw fallback, or with the static/dynamic split
 // use the window and placement kernels.
 #include "zc_place.h"
@@ -132,7 +132,7 @@ __device__ __forceinline__ void finish_window(const FinishArgs& f, uint32_t wi, 
     const uint32_t parts = sd.nsb > kFinishPartBlocks ? (sd.nsb + kFinishPartBlocks - 1) / kFinishPartBlocks : 1u;
     const bool last = q + 1 == parts;
     if (forced && !last) return;  // no moments with a fixed window
-    uint64_t* fp = a.enc.fpart + 16ull * seg;
+    uint64_t* fp = a.enc.fpart + 4ull * kFinishMaxParts * seg;
     double s1 = 0.0, s2 = 0.0;
     uint64_t n = 0;
     if (!forced && sd.nsb)
@@ -173,10 +173,11 @@ __device__ __forceinline__ void finish_window(const FinishArgs& f, uint32_t wi, 
             }
             p1[parts - 1] = s1;
             p2[parts - 1] = s2;
-            // the tree's top levels: parts joined pairwise (4 leaves, the
+            // the tree's top levels: parts joined pairwise (8 leaves, the
             // missing ones -0.0)
-            s1 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
-            s2 = (p2[0] + p2[1]) + (p2[2] + p2[3]);
+            static_assert(kFinishMaxParts == 8, "the parts' join is an 8-leaf tree");
+            s1 = tree8(p1);
+            s2 = tree8(p2);
             n += pn;
             failed = !ok;  // a part never came: no window
         }
@@ -233,7 +234,7 @@ __device__ __forceinline__ uint32_t wait_verdict(const uint32_t* flag, uint32_t*
 // publishes the chunk's count (an atomic word with a flag bit; the encoder
 // cleared the words), then sums the counts of chunks 0 .. c-1 as they
 // arrive, by the whole workgroup (each thread waits for its own words; a
-// merged plan's segment has at most 8192 chunks, so a direct sum is one
+// merged plan's segment has at most 16,384 chunks, so a direct sum is one
 // round of loads after the last of them arrives: no chain of prefixes).
 // ok = false if a wait ran out.  s_red: 4 words of LDS.
 __device__ __forceinline__ uint32_t chunks_before(uint64_t* agg, uint32_t c, uint32_t count, uint32_t* s_red,

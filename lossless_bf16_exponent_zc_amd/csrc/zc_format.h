@@ -15,10 +15,12 @@ constexpr uint32_t kFlagRaw = 1;  // header flags byte: the values stored as the
 constexpr uint32_t kMaxStreams = 16;
 constexpr uint32_t kSigmaBlock = 16384;  // values per moment partial (or the chunk, if smaller)
 // The merged finish kernel sums a chunk's escape offset from the moment
-// blocks before it: segments up to kFinishMaxBlocks blocks (128M values)
+// blocks before it: segments up to kFinishMaxBlocks blocks (256M values)
 // use it.  Its window workgroups each join kFinishPartBlocks of a segment's
-// blocks.
-constexpr uint32_t kFinishMaxBlocks = 8192;
+// blocks (268,435,456 values: the compress call 236 -> 215.5 us with the
+// merged tail instead of the window and placement kernels, a failed
+// prediction's 510 -> 376 us).
+constexpr uint32_t kFinishMaxBlocks = 16384;
 constexpr uint32_t kFinishPartBlocks = 2048;
 constexpr uint32_t kFinishMaxParts = kFinishMaxBlocks / kFinishPartBlocks;
 
@@ -78,7 +80,7 @@ struct WsLayout {
     uint64_t staging;   // 2048 bytes per group (+16): escape exponents before placement
     uint64_t flag;      // u32 per segment: the finish kernel's window verdict (0 until known)
     uint64_t agg;       // u64 per chunk: the finish kernel's look-back words
-    uint64_t fpart;     // 4 x 4 u64 per segment: the finish kernel's moment parts
+    uint64_t fpart;     // 8 x 4 u64 per segment: the finish kernel's moment parts
     uint64_t total;
     // the decoders use only the status words and, right after them, 2048
     // readable bytes they never write (the loads' stand-in): a decode-only

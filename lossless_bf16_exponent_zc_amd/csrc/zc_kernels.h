@@ -19,7 +19,7 @@ struct EncodeArgs {
     uint32_t* gcnt;         // per group: its escape count
     uint32_t* flag;         // per segment: the finish kernel's verdict (first pass clears)
     uint64_t* agg;          // per chunk: look-back words (first pass clears)
-    uint64_t* fpart;        // per segment, 4 parts x 4 words: the finish kernel's
+    uint64_t* fpart;        // per segment, 8 parts x 4 words: the finish kernel's
                             // moment parts (first pass sets them to ~0, no value)
     uint32_t chunk_elems;
     uint32_t block_elems;   // moment block (16,384 values, or the chunk if smaller)

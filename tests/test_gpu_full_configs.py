@@ -84,24 +84,26 @@ def test_gradient_64M_window_paths():
 
 
 def test_merged_tail_part_boundaries():
-    # one plan, two segments at the window parts' edges: 2048 moment blocks
-    # and one value (two parts, the second holding one block) and exactly
-    # 8192 blocks (four full parts, the largest segment the merged tail
-    # takes); fresh, then after a failed prediction (the workspace last saw
-    # the tensors times 2)
-    a = W.small(2048 * 16384 + 1, seed=21)
-    b = W.gradient(8192 * 16384, seed=22)
-    refs = pool_map(lambda x: oracle.compress(x, C=CHUNK), [a, b])
-    streams, plan, _, ws = gpu_compress([a, b], CHUNK)
+    # one plan, segments at the window parts' edges: 2048 moment blocks and
+    # one value (two parts, the second holding one block), 8194 blocks and
+    # five values (five parts: the 8-leaf join of the parts with three
+    # missing leaves) and exactly 16,384 blocks (eight full parts, the
+    # largest segment the merged tail takes); fresh, then after a failed
+    # prediction (the workspace last saw the tensors times 2)
+    segs = [W.small(2048 * 16384 + 1, seed=21), W.gradient((4 * 2048 + 2) * 16384 + 5, seed=22),
+            W.gradient(16384 * 16384, seed=23)]
+    refs = pool_map(lambda x: oracle.compress(x, C=CHUNK), segs)
+    streams, plan, _, ws = gpu_compress(segs, CHUNK)
     for s, (st, ref) in enumerate(zip(streams, refs)):
         assert_same_bytes(st, ref, f"fresh, segment {s}")
     say("  fresh workspace: streams identical to the oracle's")
-    gpu_compress([times2(a), times2(b)], CHUNK, plan=plan, ws=ws)
-    streams, _, _, _ = gpu_compress([a, b], CHUNK, plan=plan, ws=ws)
+    gpu_compress([times2(x) for x in segs], CHUNK, plan=plan, ws=ws)
+    streams, _, _, _ = gpu_compress(segs, CHUNK, plan=plan, ws=ws)
     for s, (st, ref) in enumerate(zip(streams, refs)):
         assert_same_bytes(st, ref, f"after a failed prediction, segment {s}")
-    for s, x in enumerate((a, b)):
-        assert stat_bits(plan.read_sigma(ws, s)) == stat_bits(oracle.sigma(x)), s
+    sig = pool_map(oracle.sigma, segs)
+    for s in range(len(segs)):
+        assert stat_bits(plan.read_sigma(ws, s)) == stat_bits(sig[s]), s
     say("  failed prediction: streams and statistics identical to the oracle's")
 
 
