@@ -235,9 +235,10 @@ __device__ __forceinline__ void place_load(const PlaceArgs& a, PlaceChunk<GPW>& 
 
 // The chunk's group table entries and its escape run at escape offset
 // `prefix` (or, raw, its values).  go() is called by every thread (it may
-// hold workgroup barriers) once the run is gathered in LDS and before any
-// global store; if it returns false nothing is stored and this returns
-// false.  Contains workgroup barriers.
+// hold workgroup barriers) once the run is gathered in LDS (a group's run
+// past 256 R bytes only up to there: its rest is gathered after go()) and
+// before any global store; if it returns false nothing is stored and this
+// returns false.  Contains workgroup barriers.
 template <int GPW, typename Go>
 __device__ __forceinline__ bool place_finish(const PlaceArgs& a, PlaceChunk<GPW>& pc, uint32_t prefix,
                                              bool raw, PlaceLds<GPW>& lds, Go&& go) {
